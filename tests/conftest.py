@@ -1,0 +1,21 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: large CPU oracle work")
+
+
+def read_golden(name):
+    """Non-comment, non-empty lines of a golden fixture."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.lstrip().startswith("#")]

@@ -141,13 +141,16 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
 
 
 def f32_to_bf16_bits(v) -> np.ndarray:
-    """float32 -> BF16 bit patterns by round-to-nearest-even (overflow gives +-Inf).
+    """float32 -> BF16 bit patterns by round-to-nearest-even (overflow gives +-Inf;
+    +-Inf stays +-Inf, e.g. an FP32 dequantization that overflowed).
 
     Done as a grid rounding with 7 mantissa bits and BF16's normal range
     (smallest normal 2^-126), then the exact FP32 result's top 16 bits.
     """
     v = np.asarray(v, dtype=np.float32)
-    r = round_to_grid(v.astype(np.float64), 7, -126, np.inf)
+    inf = np.isinf(v)
+    r = round_to_grid(np.where(inf, 0.0, v).astype(np.float64), 7, -126, np.inf)
     with np.errstate(over="ignore"):
         r32 = r.astype(np.float32)        # exact, or +-Inf past the BF16 range
+    r32 = np.where(inf, v, r32)           # an FP32 infinity stays infinite
     return (r32.view(np.uint32) >> 16).astype(np.uint16)

@@ -1,0 +1,301 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) microscaling quantize + block-scaled
+ * GEMM library (libmxq.so).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *    allocates, frees or synchronizes; every call validates its arguments on the
+ *    host, enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ *    stream) and returns. Scratch memory, where a call needs it, is a
+ *    caller-provided device `workspace` of at least mxq_workspace_bytes(...).
+ *  - Argument errors are detected before anything is launched and returned as an
+ *    mxq_status; nothing is written then. MXQ_ERR_HIP reports a failed launch.
+ *  - Zero-sized work (rows, cols, M, N or a group of size 0) is a successful no-op.
+ *  - Pointers to element data must be 16-byte aligned; leading dimensions are in
+ *    elements and must keep every row 16-byte aligned.
+ *  - Inputs must be finite; the bytes produced for NaN/Inf inputs are unspecified.
+ *  - Calls on different streams may run concurrently; calls that share an
+ *    output or workspace buffer must be ordered by the caller.
+ *
+ * Formats (all bit-exact against the definitions below)
+ * -----------------------------------------------------
+ *  E4M3 : OCP FP8 "fn" (bias 7, max 448, no Inf, S.1111.111 = NaN, never produced).
+ *  E8M0 : unsigned exponent byte, value 2^(s-127); 0xFF (NaN) is never produced.
+ *  E2M1 : 4-bit float, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, bit 3 = sign;
+ *         two per byte, element 2j in the low nibble of byte j.
+ *  Rounding: round-to-nearest-even onto the target grid, saturating at the largest
+ *  finite magnitude, sign of zero kept. All FP32 arithmetic is IEEE binary32 with
+ *  correctly rounded division and no flush-to-zero (no fast math).
+ *
+ *  Scale layouts are canonical row-major matrices (no swizzle): the scale of the
+ *  block holding element (r, c) sits at s[r * (cols / B) + c / B], B = 32 (MXFP8)
+ *  or 16 (NVFP4). mxq_scale_bytes() returns that size.
+ *
+ * Sources: "Miles Blackwell RL Cambia la Uniformidad BF16 por MXFP8 y NVFP4
+ * Nativos" (remio.ai); "NVIDIA presenta una metodologia de preentrenamiento de 4
+ * bits utilizando NVFP4" (7minutos.es); "Miles Blackwell MXFP8/NVFP4 RL recipes"
+ * (aib.vote). Each declaration names the passage that defines its operation.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  MXQ_ERR_SHAPE = 2,     /* negative size, or a size not a multiple of a block */
+  MXQ_ERR_ALIGN = 3,     /* pointer or leading dimension misaligned            */
+  MXQ_ERR_FORMAT = 4,    /* unsupported format / scope / option combination    */
+  MXQ_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required            */
+  MXQ_ERR_HIP = 6        /* a HIP launch failed                                */
+} mxq_status;
+
+typedef enum { MXQ_MXFP8 = 1, MXQ_NVFP4 = 2, MXQ_BF16 = 3 } mxq_format;
+typedef enum { MXQ_OUT_BF16 = 0, MXQ_OUT_F32 = 1 } mxq_out_dtype;
+
+/* Scope of an NVFP4 FP32 (second-level) scale.
+ *  ROW    : one scale per row (per token for activations), t has `rows` entries;
+ *  TENSOR : one scale for the whole tensor, t has 1 entry;
+ *  GROUP  : one scale per group of `group_rows` consecutive rows (one expert
+ *           matrix of a stacked (G, N, K) weight), t has rows / group_rows entries. */
+typedef enum { MXQ_SCOPE_ROW = 0, MXQ_SCOPE_TENSOR = 1, MXQ_SCOPE_GROUP = 2 } mxq_scope;
+
+/* ---------------------------------------------------------------------------
+ * quantize_mxfp8 -- MXFP8 quantization of a BF16 (rows, cols) row-major tensor
+ * into a rowwise 1x32 copy and/or a columnwise 32x1 copy, both made from the
+ * original BF16 values in one pass over HBM.
+ *   Defined by: every 32 consecutive E4M3 values share one E8M0 scale ("Miles
+ *   Blackwell RL", remio.ai, section "La Compatibilidad de Miles Blackwell Ahora
+ *   Abarca Todo el Ciclo de RL"); rowwise and columnwise copies, because the
+ *   blocks must follow each GEMM's reduction dimension (same page, section "Un
+ *   Cuantizador Compartido Es el Mecanismo Real"; aib.vote, MXFP8 paragraph).
+ *   Scale rule: s = clamp(e + 127, 0, 254) with e the smallest integer such that
+ *   amax <= 448 * 2^e (s = 0 for an all-zero block); q = RNE_sat_E4M3(x * 2^(127-s)).
+ *
+ *   x      : BF16, element (r, c) at x[r * ld_x + c]; ld_x >= cols, ld_x % 8 == 0.
+ *   q_row  : E4M3 (rows, cols) row-major;  s_row : E8M0 (rows, cols/32).
+ *   q_colT : E4M3 (cols, rows): q_colT[c * rows + r] encodes x(r, c) -- the
+ *            columnwise copy stored transposed, so it is K-contiguous for dgrad
+ *            and wgrad;  s_colT : E8M0 (cols, rows/32).
+ *   Either output pair may be NULL to skip that copy (not both).
+ *   Requires cols % 32 == 0, and rows % 32 == 0 when the columnwise copy is
+ *   requested.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          void* q_row, void* s_row, void* q_colT, void* s_colT,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * quantize_nvfp4_per_token -- NVFP4 with one FP32 scale per token (row),
+ * computed online in the same kernel that emits the packed E2M1 values and the
+ * E4M3 block scales.
+ *   Defined by: E2M1 values with an E4M3 scale per 16 values plus an FP32 scale
+ *   ("Miles Blackwell RL", remio.ai, section "La Compatibilidad ..."; 7minutos.es,
+ *   section "Que es realmente NVFP4"); the FP32 scale taken per token so a token's
+ *   bits never depend on the rest of the batch, and one fused operation emitting
+ *   packed FP4, block scales and token scales (remio.ai, section "Un Cuantizador
+ *   Compartido Es el Mecanismo Real"; aib.vote, per-token paragraph).
+ *   Arithmetic (binary32): A = max|x| over the row; s_enc = 2688 / A (1 if A = 0,
+ *   FLT_MAX on overflow); t = 1 / s_enc; per 16-block S = RNE_sat_E4M3((a_b / 6)
+ *   * s_enc); r = min(s_enc / S, FLT_MAX) (0 if S = 0); q = RNE_sat_E2M1(x * r).
+ *
+ *   x       : BF16 (tokens, hidden), row stride ld_x elements (ld_x % 8 == 0).
+ *   q_packed: uint8 (tokens, hidden/2);  s_block: E4M3 (tokens, hidden/16);
+ *   s_token : float (tokens) -- the decode scale t (dequantized x = q * S * t).
+ *   Requires hidden % 16 == 0.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                    void* q_packed, void* s_block, float* s_token,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * quantize_nvfp4 -- general NVFP4 quantizer: any FP32-scale scope, optional
+ * transposed (columnwise) blocking and an optional 16-point random Hadamard
+ * transform along the quantized axis.
+ *   Defined by: the two-level NVFP4 scaling with an FP32 tensor scale (7minutos.es,
+ *   section "Que es realmente NVFP4"); joint gate/up scale for SwiGLU experts, i.e.
+ *   one scale over the fused gate_up matrix of an expert (remio.ai, section "Un
+ *   Cuantizador Compartido ..."); a 16x16 Hadamard matrix times a random +-1 sign
+ *   vector applied to the weight-gradient GEMM inputs before quantization
+ *   (7minutos.es, section "La metodologia de formacion de cuatro partes").
+ *   RHT of a 16-chunk v: w = signs * v; Sylvester-order fast Walsh-Hadamard
+ *   transform in binary32 (stages 1, 2, 4, 8; (a, b) -> (a + b, a - b)); u = w / 4.
+ *   Scope amax is taken over the transformed values.
+ *
+ *   x          : BF16 (rows, cols), row stride ld_x.
+ *   scope      : ROW / TENSOR / GROUP (group_rows consecutive rows share a scale;
+ *                with transpose = 1 a group is group_rows consecutive COLUMNS of x,
+ *                i.e. rows of the transposed output).
+ *   transpose  : 0 -> blocks along each row; outputs (rows, cols/2), (rows, cols/16).
+ *                1 -> blocks along each column, stored transposed; outputs
+ *                (cols, rows/2), (cols, rows/16).
+ *   rht_signs16: HOST pointer to 16 int8 values, each +1 or -1; NULL = no transform.
+ *   q, s, t    : packed E2M1, E4M3 block scales, FP32 decode scales (count per scope).
+ *   workspace  : device scratch of mxq_workspace_bytes(MXQ_OP_QUANTIZE_NVFP4,
+ *                rows, cols, scope-count) bytes (TENSOR and GROUP scopes; NULL
+ *                allowed for ROW).
+ *   Requires the blocked axis % 16 == 0; with transpose = 1 also cols % 8 == 0.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_scope scope, int64_t group_rows, int transpose,
+                          const int8_t* rht_signs16,
+                          void* q, void* s, float* t,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dequantize -- reconstruct BF16 or FP32 values from MXFP8 or NVFP4 data, e.g.
+ * the BF16 operands of the dequantized-backward GEMMs.
+ *   Defined by: the dequantized-backward mode, whose backward GEMMs run in BF16 on
+ *   dequantizations of the exact low-precision forward operands ("Miles Blackwell
+ *   RL", remio.ai, section "La Compatibilidad ..."; aib.vote, backward-modes
+ *   paragraph).
+ *   FP32 output: v = (q * S) * t, one binary32 rounding (q * S is exact; MXFP8 has
+ *   no t). BF16 output: that FP32 value rounded to BF16 (RNE). Overflow gives Inf.
+ *
+ *   fmt   : MXQ_MXFP8 (q (rows, cols) E4M3, s (rows, cols/32) E8M0, t unused) or
+ *           MXQ_NVFP4 (q (rows, cols/2), s (rows, cols/16) E4M3, t per t_scope).
+ *   out   : (rows, cols) row-major, BF16 or FP32.
+ * ------------------------------------------------------------------------- */
+mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float* t,
+                      mxq_scope t_scope, int64_t group_rows, int64_t rows, int64_t cols,
+                      void* out, mxq_out_dtype out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gemm_block_scaled -- C = (A_hat) (B_hat)^T with FP32 output, both operands
+ * K-contiguous ("TN"), scaling blocks along K.
+ *   Defined by: microscaling blocks must follow the reduction dimension of the
+ *   matrix product, with forward and backward using different orientations
+ *   ("Miles Blackwell RL", remio.ai, section "Un Cuantizador Compartido ...");
+ *   fprop, dgrad and wgrad GEMMs of linear layers run in the low-precision format
+ *   (remio.ai, section "La Compatibilidad ..."; 7minutos.es, section "Que esta
+ *   cuantificado y que no").
+ *   MXQ_MXFP8: A (M, K) E4M3 + sA (M, K/32) E8M0; B (N, K) + sB (N, K/32); tA/tB unused.
+ *              Every E4M3 * 2^(s-127) operand value is formed exactly and the
+ *              products are accumulated at FP32 precision (see
+ *              gemm_mxfp8_matrix_core for the native scaled-FP8 MFMA variant).
+ *              Dequantized magnitudes must stay below 2^128.
+ *   MXQ_NVFP4: A (M, K/2) packed E2M1 + sA (M, K/16) E4M3 + tA (ROW: M, TENSOR: 1);
+ *              B likewise with tB (ROW: N, TENSOR: 1);
+ *              C = tA[m] tB[n] * sum_k (qA SA)(qB SB) -- the E4M3-per-16 block
+ *              products are formed exactly, then accumulated in FP32.
+ *   MXQ_BF16 : A (M, K) BF16, B (N, K) BF16; scales unused.
+ *   C[m * ldc + n], ldc >= N, C 4-byte aligned. Accuracy: normwise relative error
+ *   <= 2e-5 against the FP64 product of the exact dequantized operands.
+ *   Requires K % 32 == 0 (MXFP8), K % 32 == 0 (NVFP4), K % 8 == 0 (BF16).
+ * ------------------------------------------------------------------------- */
+mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K,
+                             const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
+                             const void* B, const void* sB, const float* tB, mxq_scope tB_scope,
+                             float* C, int64_t ldc, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gemm_mxfp8_matrix_core -- MXFP8 GEMM C = A_hat B_hat^T on the gfx950 scaled FP8
+ * MFMA, which consumes the E8M0 block scales natively (one byte per row and
+ * 32-K block of each operand).
+ *   Defined by: block scales along the reduction dimension consumed by the
+ *   matrix hardware ("Miles Blackwell RL", remio.ai, section "Un Cuantizador
+ *   Compartido Es el Mecanismo Real").
+ *   Accumulation (measured on MI355X): each group of 8 consecutive K products is
+ *   summed in a fixed-point window ~13 bits below the group's largest product
+ *   (lower bits dropped); group sums accumulate at FP32 precision. Within 2e-5
+ *   normwise on Gaussian-like blocks; outlier-heavy blocks can exceed it -- use
+ *   gemm_block_scaled(MXQ_MXFP8, ...) where the bound must hold for any data.
+ *   Operands, layout and alignment as gemm_block_scaled(MXQ_MXFP8, ...).
+ * ------------------------------------------------------------------------- */
+mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K,
+                                  const void* A, const void* sA, const void* B, const void* sB,
+                                  float* C, int64_t ldc, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * grouped_gemm_block_scaled -- one GEMM per routed expert, scheduled on the device
+ * from the expert offsets (no host synchronisation on the group sizes).
+ *   Defined by: NVFP4 applied to the routed experts' weights and activations of
+ *   the MoE layers ("Miles Blackwell RL", remio.ai, section "La Compatibilidad
+ *   ..."; aib.vote, NVFP4 paragraph), where moving expert weights through memory
+ *   can bind harder than arithmetic (remio.ai, section "NVFP4 por token ...").
+ *
+ *   vary_k = 0 (fprop / dgrad):  for every group g and slot s in
+ *       [offsets[g], offsets[g+1]):  C[s, :] = A_hat[row(s), :] B_hat_g^T
+ *     A      : (a_rows, K) operand; row(s) = a_row_index[s] when a_row_index is
+ *              non-NULL (gather of token rows into expert order), else s. A gather
+ *              index outside [0, a_rows) contributes a zero row (never read).
+ *     B      : stacked (groups, N, K) operand; C : (total_slots, N) FP32.
+ *     tA     : per A row (ROW) or one (TENSOR); tB : per group (GROUP with
+ *              group_rows = N) or per B row (ROW).
+ *   vary_k = 1 (wgrad): for every group g:  C_g = sum over k in [offsets[g],
+ *       offsets[g+1]) of A[:, k] B[:, k]^T
+ *     A : (M, total_k) K-contiguous; B : (N, total_k); C : (groups, M, N).
+ *     Group boundaries must be multiples of 32 (MXFP8) or 8 (BF16); only MXQ_MXFP8
+ *     and MXQ_BF16 are supported with vary_k = 1 in ABI version 1.
+ *   offsets  : DEVICE int64 (groups + 1), non-decreasing, offsets[0] = 0,
+ *              offsets[groups] = total (total_slots or total_k, passed as `total`);
+ *              with vary_k = 1 every offset is a multiple of 32 (MXFP8) or 8 (BF16).
+ *              The device checks this before any tile runs; offsets that break it
+ *              make the call a no-op that leaves C unwritten.
+ *   workspace: device scratch of mxq_workspace_bytes(MXQ_OP_GROUPED_GEMM, groups, 0, 0).
+ * ------------------------------------------------------------------------- */
+mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64_t* offsets,
+                                     int vary_k, int64_t total, int64_t M, int64_t N, int64_t K,
+                                     const int32_t* a_row_index, int64_t a_rows,
+                                     const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
+                                     const void* B, const void* sB, const float* tB, mxq_scope tB_scope,
+                                     float* C, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_swiglu_quantize_nvfp4 -- SwiGLU of the gate_up GEMM output followed by
+ * per-row NVFP4 quantization of the result (input of the down projection).
+ *   Defined by: SwiGLU experts whose gate and up projections enter one fused GEMM
+ *   ("Miles Blackwell RL", remio.ai, section "Un Cuantizador Compartido ..."), and
+ *   per-token NVFP4 on the expert activations (same page, section "La
+ *   Compatibilidad ..."). Each slot row (token, expert) is one scale scope.
+ *   h = silu(g) * u in binary32 (g = row[0:inter], u = row[inter:2*inter]), rounded
+ *   to BF16; then the per-token quantizer above on the BF16 row.
+ *
+ *   gate_up : FP32 (rows, 2*inter); h_bf16 : optional BF16 (rows, inter) copy of h
+ *   (NULL = not written); q (rows, inter/2), s (rows, inter/16), t (rows).
+ *   Requires inter % 16 == 0.
+ * ------------------------------------------------------------------------- */
+mxq_status moe_swiglu_quantize_nvfp4(const float* gate_up, int64_t rows, int64_t inter,
+                                     void* h_bf16, void* q, void* s, float* t, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine -- y[t, :] = sum_j w[t, j] * O[slot_of[t, j], :] in FP32, j ascending.
+ *   The weighted top-k combine that closes a routed-expert layer (remio.ai,
+ *   section "NVFP4 por token ...": experts routed per token).
+ *   o_slots : FP32 (total_slots, hidden); slot_of : DEVICE int64 (tokens, topk), entries
+ *   in [0, total_slots) (others contribute nothing); weights : FP32 (tokens, topk);
+ *   y : FP32 (tokens, hidden). hidden % 4 == 0.
+ * ------------------------------------------------------------------------- */
+mxq_status moe_combine(const float* o_slots, int64_t total_slots, int64_t tokens, int64_t topk,
+                       int64_t hidden, const int64_t* slot_of, const float* weights, float* y,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Queries.
+ * ------------------------------------------------------------------------- */
+/* Bytes of the scale matrix for a (rows, cols) tensor blocked along cols
+ * (MXFP8: rows * cols/32, NVFP4: rows * cols/16); 0 for BF16 or bad shapes. */
+size_t mxq_scale_bytes(mxq_format fmt, int64_t rows, int64_t cols);
+
+enum { MXQ_OP_QUANTIZE_NVFP4 = 1, MXQ_OP_GROUPED_GEMM = 2 };
+/* Workspace bytes for an op:
+ *   MXQ_OP_QUANTIZE_NVFP4 (a = rows, b = cols, c = number of FP32 scales);
+ *   MXQ_OP_GROUPED_GEMM   (a = groups). */
+size_t mxq_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
+
+const char* mxq_status_string(mxq_status s);
+int mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

@@ -1,0 +1,261 @@
+// C ABI of libmxq: host-side validation and kernel dispatch. Every check runs
+// before any launch, so an argument error writes nothing; the calls never
+// allocate, free or synchronize.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mxq.h"
+
+namespace mxq {
+hipError_t launch_quant_mxfp8(const void*, int64_t, int64_t, int64_t, void*, void*, void*, void*, hipStream_t);
+hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
+hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
+                              float*, uint32_t*, int64_t, hipStream_t);
+hipError_t launch_dequant(int, const void*, const void*, const float*, int, int64_t, int64_t, int64_t, void*, int,
+                          hipStream_t);
+hipError_t launch_swiglu_nvfp4(const float*, int64_t, int64_t, void*, void*, void*, float*, hipStream_t);
+hipError_t launch_combine(const float*, int64_t, int64_t, int64_t, int64_t, const int64_t*, const float*, float*,
+                          hipStream_t);
+hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const float* tA,
+                       int tA_mode, const void* B, const void* sB, const float* tB, int tB_mode, float* C,
+                       int64_t ldc, hipStream_t st);
+hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, int vary_k, int64_t total, int64_t M,
+                               int64_t N, int64_t K, const int32_t* a_row_index, int64_t a_rows, const void* A,
+                               const void* sA, const float* tA, int tA_mode, const void* B, const void* sB,
+                               const float* tB, int tB_mode, float* C, void* ws, hipStream_t st);
+size_t grouped_gemm_ws_bytes(int64_t groups);
+hipError_t launch_gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const void* B,
+                                         const void* sB, float* C, int64_t ldc, hipStream_t st);
+}  // namespace mxq
+
+namespace {
+
+constexpr int64_t kMaxRowCols = 16384;       // register-resident NVFP4 row quantizer
+constexpr int64_t kMaxGridBlocks = 0x7FFFFFFF;
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+inline mxq_status hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char* mxq_status_string(mxq_status s) {
+  switch (s) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "required pointer is NULL";
+    case MXQ_ERR_SHAPE: return "invalid shape (negative, not a multiple of the block, or beyond a limit)";
+    case MXQ_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case MXQ_ERR_FORMAT: return "unsupported format, scope or option combination";
+    case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t mxq_scale_bytes(mxq_format fmt, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  if (fmt == MXQ_MXFP8 && cols % 32 == 0) return (size_t)(rows * (cols / 32));
+  if (fmt == MXQ_NVFP4 && cols % 16 == 0) return (size_t)(rows * (cols / 16));
+  return 0;
+}
+
+size_t mxq_workspace_bytes(int op, int64_t a, int64_t b, int64_t c) {
+  (void)b;
+  if (op == MXQ_OP_QUANTIZE_NVFP4) return c > 0 ? (size_t)(((c * 4) + 255) / 256 * 256) : 0;
+  if (op == MXQ_OP_GROUPED_GEMM) return a > 0 ? mxq::grouped_gemm_ws_bytes(a) : 0;
+  return 0;
+}
+
+mxq_status quantize_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q_row, void* s_row,
+                          void* q_colT, void* s_colT, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  const bool do_row = q_row || s_row, do_col = q_colT || s_colT;
+  if (!x || (!do_row && !do_col)) return MXQ_ERR_NULL;
+  if ((do_row && (!q_row || !s_row)) || (do_col && (!q_colT || !s_colT))) return MXQ_ERR_NULL;
+  if (cols % 32) return MXQ_ERR_SHAPE;
+  if (do_col && rows % 32) return MXQ_ERR_SHAPE;
+  if (ld_x < cols) return MXQ_ERR_SHAPE;
+  if (ld_x % 8 || !al16(x) || (do_row && !al16(q_row)) || (do_col && !al16(q_colT))) return MXQ_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if (((rows + 127) / 128) * ((cols + 127) / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_quant_mxfp8(x, rows, cols, ld_x, do_row ? q_row : nullptr, s_row,
+                                            do_col ? q_colT : nullptr, s_colT, S(stream)));
+}
+
+mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x, void* q_packed,
+                                    void* s_block, float* s_token, void* stream) {
+  if (tokens < 0 || hidden < 0) return MXQ_ERR_SHAPE;
+  if (!x || !q_packed || !s_block || !s_token) return MXQ_ERR_NULL;
+  if (hidden % 16 || hidden > kMaxRowCols || ld_x < hidden) return MXQ_ERR_SHAPE;
+  if (ld_x % 8 || !al16(x) || !al4(q_packed) || !al4(s_token)) return MXQ_ERR_ALIGN;
+  if (tokens == 0 || hidden == 0) return MXQ_OK;
+  return hip_status(mxq::launch_quant_nvfp4_token(x, tokens, hidden, ld_x, q_packed, s_block, s_token, S(stream)));
+}
+
+mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,
+                          int64_t group_rows, int transpose, const int8_t* rht_signs16, void* q, void* s, float* t,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  if (!x || !q || !s || !t) return MXQ_ERR_NULL;
+  if (scope != MXQ_SCOPE_ROW && scope != MXQ_SCOPE_TENSOR && scope != MXQ_SCOPE_GROUP) return MXQ_ERR_FORMAT;
+  if (transpose != 0 && transpose != 1) return MXQ_ERR_FORMAT;
+  if (transpose && scope == MXQ_SCOPE_ROW) return MXQ_ERR_FORMAT;
+  uint32_t neg_mask = 0;
+  if (rht_signs16) {
+    for (int i = 0; i < 16; ++i) {
+      if (rht_signs16[i] == -1) neg_mask |= 1u << i;
+      else if (rht_signs16[i] != 1) return MXQ_ERR_FORMAT;
+    }
+  }
+  if (ld_x < cols) return MXQ_ERR_SHAPE;
+  const int64_t out_rows = transpose ? cols : rows;
+  if (transpose) {
+    if (rows % 16 || cols % 8) return MXQ_ERR_SHAPE;
+  } else {
+    if (cols % 16 || cols > kMaxRowCols) return MXQ_ERR_SHAPE;
+  }
+  int64_t n_scopes = 1;
+  if (scope == MXQ_SCOPE_ROW) n_scopes = out_rows;
+  if (scope == MXQ_SCOPE_GROUP) {
+    if (group_rows <= 0 || out_rows % group_rows) return MXQ_ERR_SHAPE;
+    if (transpose && group_rows % 8) return MXQ_ERR_SHAPE;
+    n_scopes = out_rows / group_rows;
+  }
+  if (ld_x % 8 || !al16(x) || !al4(q) || !al4(t)) return MXQ_ERR_ALIGN;
+  if (transpose && !al16(q)) return MXQ_ERR_ALIGN;
+  if (scope != MXQ_SCOPE_ROW) {
+    if (!workspace || workspace_bytes < (size_t)(n_scopes * 4)) return MXQ_ERR_WORKSPACE;
+    if (!al4(workspace)) return MXQ_ERR_ALIGN;
+  }
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  return hip_status(mxq::launch_quant_nvfp4(x, rows, cols, ld_x, (int)scope, group_rows, transpose,
+                                            rht_signs16 != nullptr, neg_mask, q, s, t, (uint32_t*)workspace,
+                                            n_scopes, S(stream)));
+}
+
+mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float* t, mxq_scope t_scope,
+                      int64_t group_rows, int64_t rows, int64_t cols, void* out, mxq_out_dtype out_dtype,
+                      void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4) return MXQ_ERR_FORMAT;
+  if (out_dtype != MXQ_OUT_BF16 && out_dtype != MXQ_OUT_F32) return MXQ_ERR_FORMAT;
+  if (!q || !s || !out || (fmt == MXQ_NVFP4 && !t)) return MXQ_ERR_NULL;
+  if (fmt == MXQ_MXFP8 && cols % 32) return MXQ_ERR_SHAPE;
+  if (fmt == MXQ_NVFP4 && cols % 16) return MXQ_ERR_SHAPE;
+  int tm = 0;
+  if (fmt == MXQ_NVFP4) {
+    if (t_scope == MXQ_SCOPE_ROW) tm = 0;
+    else if (t_scope == MXQ_SCOPE_TENSOR) tm = 1;
+    else if (t_scope == MXQ_SCOPE_GROUP) {
+      tm = 2;
+      if (group_rows <= 0 || rows % group_rows) return MXQ_ERR_SHAPE;
+    } else return MXQ_ERR_FORMAT;
+  }
+  if (!al16(q) || !al16(out)) return MXQ_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  return hip_status(mxq::launch_dequant(fmt == MXQ_NVFP4, q, s, t, tm, group_rows, rows, cols, out,
+                                        out_dtype == MXQ_OUT_F32, S(stream)));
+}
+
+static int scope_mode(mxq_scope sc) {
+  return sc == MXQ_SCOPE_ROW ? 0 : sc == MXQ_SCOPE_TENSOR ? 1 : sc == MXQ_SCOPE_GROUP ? 2 : -1;
+}
+
+mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K, const void* A, const void* sA,
+                             const float* tA, mxq_scope tA_scope, const void* B, const void* sB, const float* tB,
+                             mxq_scope tB_scope, float* C, int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16) return MXQ_ERR_FORMAT;
+  if (!A || !B || !C) return MXQ_ERR_NULL;
+  if (fmt != MXQ_BF16 && (!sA || !sB)) return MXQ_ERR_NULL;
+  int ta = -1, tb = -1;
+  if (fmt == MXQ_NVFP4) {
+    if (!tA || !tB) return MXQ_ERR_NULL;
+    ta = scope_mode(tA_scope);
+    tb = scope_mode(tB_scope);
+    if (ta != 0 && ta != 1) return MXQ_ERR_FORMAT;
+    if (tb != 0 && tb != 1) return MXQ_ERR_FORMAT;
+  }
+  if (fmt == MXQ_MXFP8 && K % 32) return MXQ_ERR_SHAPE;
+  if (fmt == MXQ_NVFP4 && K % 32) return MXQ_ERR_SHAPE;
+  if (fmt == MXQ_BF16 && K % 8) return MXQ_ERR_SHAPE;
+  if (ldc < N) return MXQ_ERR_SHAPE;
+  if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return MXQ_OK;
+  return hip_status(mxq::launch_gemm((int)fmt, M, N, K, A, sA, tA, ta, B, sB, tB, tb, C, ldc, S(stream)));
+}
+
+mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const void* B,
+                                  const void* sB, float* C, int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (!A || !sA || !B || !sB || !C) return MXQ_ERR_NULL;
+  if (K % 32 || ldc < N) return MXQ_ERR_SHAPE;
+  if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return MXQ_OK;
+  return hip_status(mxq::launch_gemm_mxfp8_matrix_core(M, N, K, A, sA, B, sB, C, ldc, S(stream)));
+}
+
+mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64_t* offsets, int vary_k,
+                                     int64_t total, int64_t M, int64_t N, int64_t K, const int32_t* a_row_index,
+                                     int64_t a_rows, const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
+                                     const void* B, const void* sB, const float* tB, mxq_scope tB_scope, float* C,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (groups < 0 || total < 0 || M < 0 || N < 0 || K < 0 || a_rows < 0) return MXQ_ERR_SHAPE;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16) return MXQ_ERR_FORMAT;
+  if (vary_k != 0 && vary_k != 1) return MXQ_ERR_FORMAT;
+  if (vary_k && fmt == MXQ_NVFP4) return MXQ_ERR_FORMAT;
+  if (vary_k && a_row_index) return MXQ_ERR_FORMAT;
+  if (!offsets || !A || !B || !C) return MXQ_ERR_NULL;
+  if (fmt != MXQ_BF16 && (!sA || !sB)) return MXQ_ERR_NULL;
+  int ta = -1, tb = -1;
+  if (fmt == MXQ_NVFP4) {
+    if (!tA || !tB) return MXQ_ERR_NULL;
+    ta = scope_mode(tA_scope);
+    tb = scope_mode(tB_scope);
+    if (ta != 0 && ta != 1) return MXQ_ERR_FORMAT;
+    if (tb != 0 && tb != 2) return MXQ_ERR_FORMAT;    // per B row, or per group (expert)
+  }
+  if (!vary_k) {
+    if (fmt == MXQ_MXFP8 && K % 32) return MXQ_ERR_SHAPE;
+    if (fmt == MXQ_NVFP4 && K % 32) return MXQ_ERR_SHAPE;
+    if (fmt == MXQ_BF16 && K % 8) return MXQ_ERR_SHAPE;
+  } else {
+    if (total % (fmt == MXQ_MXFP8 ? 32 : 8)) return MXQ_ERR_SHAPE;
+  }
+  if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
+  if (groups == 0 || N == 0 || (vary_k ? M == 0 : total == 0)) return MXQ_OK;
+  if (!workspace || workspace_bytes < mxq::grouped_gemm_ws_bytes(groups)) return MXQ_ERR_WORKSPACE;
+  if (!al16(workspace)) return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_grouped_gemm((int)fmt, groups, offsets, vary_k, total, M, N, K, a_row_index,
+                                             a_row_index ? a_rows : total, A, sA,
+                                             tA, ta, B, sB, tB, tb, C, workspace, S(stream)));
+}
+
+mxq_status moe_swiglu_quantize_nvfp4(const float* gate_up, int64_t rows, int64_t inter, void* h_bf16, void* q,
+                                     void* s, float* t, void* stream) {
+  if (rows < 0 || inter < 0) return MXQ_ERR_SHAPE;
+  if (!gate_up || !q || !s || !t) return MXQ_ERR_NULL;
+  if (inter % 16 || inter > kMaxRowCols) return MXQ_ERR_SHAPE;
+  if (!al16(gate_up) || !al4(q) || (h_bf16 && !al16(h_bf16)) || !al4(t)) return MXQ_ERR_ALIGN;
+  if (rows == 0 || inter == 0) return MXQ_OK;
+  return hip_status(mxq::launch_swiglu_nvfp4(gate_up, rows, inter, h_bf16, q, s, t, S(stream)));
+}
+
+mxq_status moe_combine(const float* o_slots, int64_t total_slots, int64_t tokens, int64_t topk, int64_t hidden,
+                       const int64_t* slot_of, const float* weights, float* y, void* stream) {
+  if (tokens < 0 || topk < 0 || hidden < 0 || total_slots < 0) return MXQ_ERR_SHAPE;
+  if (!o_slots || !slot_of || !weights || !y) return MXQ_ERR_NULL;
+  if (hidden % 4) return MXQ_ERR_SHAPE;
+  if (!al16(o_slots) || !al16(y)) return MXQ_ERR_ALIGN;
+  if (tokens == 0 || hidden == 0) return MXQ_OK;
+  if (tokens > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_combine(o_slots, total_slots, tokens, topk, hidden, slot_of, weights, y, S(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Dequantization and the MoE expert-layer glue (SwiGLU + per-row NVFP4 requant,
+// weighted top-k combine).
+//
+// Dequantization serves the dequantized-backward mode: backward GEMMs run in
+// BF16 on dequantizations of the exact low-precision forward operands
+// ("Miles Blackwell RL", remio.ai, section "La Compatibilidad de Miles
+// Blackwell Ahora Abarca Todo el Ciclo de RL"; aib.vote, backward paragraph).
+//   v = fl(fl(q * S) * t)  (q * S exact; MXFP8 has no t), BF16 = RNE(v).
+// SwiGLU experts with gate and up in one fused GEMM, and per-token NVFP4 on the
+// expert activations: remio.ai, sections "Un Cuantizador Compartido Es el
+// Mecanismo Real" and "La Compatibilidad ...".
+#include "common.h"
+
+namespace mxq {
+
+// ---------------------------------------------------------------------------
+// Dequantize: one thread per 16 consecutive elements of a row.
+// ---------------------------------------------------------------------------
+template <bool NV, bool OUT_F32>
+__global__ void __launch_bounds__(256)
+dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, const float* __restrict__ t,
+               int t_mode, int64_t group_rows, int64_t rows, int64_t cols, void* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = cols / 16;
+  if (idx >= rows * per_row) return;
+  const int64_t r = idx / per_row, c0 = (idx % per_row) * 16;
+  float v[16];
+  if (!NV) {
+    const uint4 b = *reinterpret_cast<const uint4*>(q + r * cols + c0);
+    const float sc = e8m0_to_float(s[r * (cols / 32) + c0 / 32]);
+    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFF) * sc;
+  } else {
+    const uint2 b = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c0 / 2);
+    const float S = e4m3_to_f32(s[r * (cols / 16) + c0 / 16]);
+    const float tt = t_mode == 0 ? t[r] : t_mode == 1 ? t[0] : t[r / group_rows];
+    const uint32_t w[2] = {b.x, b.y};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float qs = e2m1_to_f32((w[i / 8] >> (4 * (i % 8))) & 0xF) * S;   // exact
+      v[i] = qs * tt;
+    }
+  }
+  if (OUT_F32) {
+    float4* o = reinterpret_cast<float4*>((float*)out + r * cols + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+    uint32_t p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = f32_to_bf16_rne(v[2 * i]) | (f32_to_bf16_rne(v[2 * i + 1]) << 16);
+    uint4* o = reinterpret_cast<uint4*>((uint16_t*)out + r * cols + c0);
+    o[0] = make_uint4(p[0], p[1], p[2], p[3]);
+    o[1] = make_uint4(p[4], p[5], p[6], p[7]);
+  }
+}
+
+hipError_t launch_dequant(int nv, const void* q, const void* s, const float* t, int t_mode, int64_t group_rows,
+                          int64_t rows, int64_t cols, void* out, int out_f32, hipStream_t st) {
+  const int64_t n = rows * (cols / 16);
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  const uint8_t *qp = (const uint8_t*)q, *sp = (const uint8_t*)s;
+  if (nv && out_f32) hipLaunchKernelGGL((dequant_kernel<true, true>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+  else if (nv) hipLaunchKernelGGL((dequant_kernel<true, false>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+  else if (out_f32) hipLaunchKernelGGL((dequant_kernel<false, true>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+  else hipLaunchKernelGGL((dequant_kernel<false, false>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU + per-row NVFP4: one wave per slot row; the row stays in registers.
+// h = silu(g) * u = g / (1 + exp(-g)) * u in binary32, rounded to BF16, then the
+// per-token quantizer's arithmetic on the BF16 row.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float swiglu1(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+template <int CH>
+__global__ void __launch_bounds__(256)
+swiglu_nvfp4_kernel(const float* __restrict__ gu, int64_t rows, int64_t inter, uint16_t* __restrict__ h_out,
+                    uint8_t* __restrict__ q, uint8_t* __restrict__ s, float* __restrict__ t_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* g = gu + row * 2 * inter;
+  const float* u = g + inter;
+  uint4 hb[CH];            // BF16 h, 8 per lane per chunk
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t e = (int64_t)i * 512 + 8 * lane;
+    uint32_t p[4] = {0, 0, 0, 0};
+    if (e < inter) {
+      const float4 g0 = *reinterpret_cast<const float4*>(g + e), g1 = *reinterpret_cast<const float4*>(g + e + 4);
+      const float4 u0 = *reinterpret_cast<const float4*>(u + e), u1 = *reinterpret_cast<const float4*>(u + e + 4);
+      p[0] = f32_to_bf16_rne(swiglu1(g0.x, u0.x)) | (f32_to_bf16_rne(swiglu1(g0.y, u0.y)) << 16);
+      p[1] = f32_to_bf16_rne(swiglu1(g0.z, u0.z)) | (f32_to_bf16_rne(swiglu1(g0.w, u0.w)) << 16);
+      p[2] = f32_to_bf16_rne(swiglu1(g1.x, u1.x)) | (f32_to_bf16_rne(swiglu1(g1.y, u1.y)) << 16);
+      p[3] = f32_to_bf16_rne(swiglu1(g1.z, u1.z)) | (f32_to_bf16_rne(swiglu1(g1.w, u1.w)) << 16);
+      if (h_out) *reinterpret_cast<uint4*>(h_out + row * inter + e) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+    hb[i] = make_uint4(p[0], p[1], p[2], p[3]);
+    amax_bits = pk_max_u16(amax_bits, pk_max_u16(pk_max_u16(p[0] & 0x7FFF7FFFu, p[1] & 0x7FFF7FFFu),
+                                                 pk_max_u16(p[2] & 0x7FFF7FFFu, p[3] & 0x7FFF7FFFu)));
+  }
+  uint32_t u32 = max_halves(amax_bits) << 16;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = shfl_xor_u32(u32, off);
+    u32 = u32 > o ? u32 : o;
+  }
+  const float A = __uint_as_float(u32);
+  float s_enc = 2688.0f / A;
+  if (A == 0.0f) s_enc = 1.0f;
+  if (__builtin_isinf(s_enc)) s_enc = kFltMax;
+  if (lane == 0) t_out[row] = 1.0f / s_enc;
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t e = (int64_t)i * 512 + 8 * lane;
+    const uint32_t w[4] = {hb[i].x, hb[i].y, hb[i].z, hb[i].w};
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { f[2 * k] = bf16_lo(w[k]); f[2 * k + 1] = bf16_hi(w[k]); }
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = fmaxf(a, __uint_as_float(dpp_xor1(__float_as_uint(a))));
+    float d = fminf((a / 6.0f) * s_enc, kE4M3Max);
+    const uint32_t code = cvt_fp8x2_f32(0u, d, 0.0f, 1.0f, false) & 0xFFu;
+    const float S = e4m3_to_f32(code);
+    const float r = (S == 0.0f) ? 0.0f : fminf(s_enc / S, kFltMax);
+    uint32_t o = 0;
+    o = cvt_fp4x2_f32<0>(o, f[0] * r, f[1] * r);
+    o = cvt_fp4x2_f32<1>(o, f[2] * r, f[3] * r);
+    o = cvt_fp4x2_f32<2>(o, f[4] * r, f[5] * r);
+    o = cvt_fp4x2_f32<3>(o, f[6] * r, f[7] * r);
+    if (e < inter) {
+      *reinterpret_cast<uint32_t*>(q + row * (inter / 2) + e / 2) = o;
+      if (!odd) s[row * (inter / 16) + e / 16] = (uint8_t)code;
+    }
+  }
+}
+
+hipError_t launch_swiglu_nvfp4(const float* gu, int64_t rows, int64_t inter, void* h, void* q, void* s, float* t,
+                               hipStream_t st) {
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int64_t ch = (inter + 511) / 512;
+  uint16_t* hp = (uint16_t*)h;
+  if (ch <= 2) hipLaunchKernelGGL(swiglu_nvfp4_kernel<2>, grid, block, 0, st, gu, rows, inter, hp, (uint8_t*)q, (uint8_t*)s, t);
+  else if (ch <= 4) hipLaunchKernelGGL(swiglu_nvfp4_kernel<4>, grid, block, 0, st, gu, rows, inter, hp, (uint8_t*)q, (uint8_t*)s, t);
+  else if (ch <= 8) hipLaunchKernelGGL(swiglu_nvfp4_kernel<8>, grid, block, 0, st, gu, rows, inter, hp, (uint8_t*)q, (uint8_t*)s, t);
+  else if (ch <= 16) hipLaunchKernelGGL(swiglu_nvfp4_kernel<16>, grid, block, 0, st, gu, rows, inter, hp, (uint8_t*)q, (uint8_t*)s, t);
+  else hipLaunchKernelGGL(swiglu_nvfp4_kernel<32>, grid, block, 0, st, gu, rows, inter, hp, (uint8_t*)q, (uint8_t*)s, t);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one workgroup per token, float4 per thread, j ascending.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ o, int64_t total_slots, int64_t topk, int64_t hidden,
+               const int64_t* __restrict__ slot_of, const float* __restrict__ w, float* __restrict__ y) {
+  const int64_t tok = blockIdx.x;
+  for (int64_t c = 4 * (int64_t)threadIdx.x; c < hidden; c += 4 * (int64_t)blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t j = 0; j < topk; ++j) {
+      const float wj = w[tok * topk + j];
+      const int64_t slot = slot_of[tok * topk + j];
+      if (slot < 0 || slot >= total_slots) continue;
+      const float4 v = *reinterpret_cast<const float4*>(o + slot * hidden + c);
+      acc.x += wj * v.x; acc.y += wj * v.y; acc.z += wj * v.z; acc.w += wj * v.w;
+    }
+    *reinterpret_cast<float4*>(y + tok * hidden + c) = acc;
+  }
+}
+
+hipError_t launch_combine(const float* o, int64_t total_slots, int64_t tokens, int64_t topk, int64_t hidden,
+                          const int64_t* slot_of, const float* w, float* y, hipStream_t st) {
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)tokens), dim3(256), 0, st, o, total_slots, topk, hidden, slot_of,
+                     w, y);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,357 @@
+// NVFP4 quantizers: E2M1 elements, one E4M3 scale per 16 values, one FP32
+// decode scale per scope (token row, tensor, or group of rows).
+//
+// Operation (restated from the pages): two-level NVFP4 scaling, where the FP32
+// scale keeps the E4M3 block scales in range and the block amax lands next to
+// the FP4 maximum (7minutos.es NVFP4 page, section "Que es realmente NVFP4");
+// the FP32 scale computed online per token inside the one kernel that emits the
+// packed values, block scales and token scales (remio.ai "Miles Blackwell RL",
+// section "Un Cuantizador Compartido Es el Mecanismo Real"); no approximate
+// math in the FP4 path (same section); optional 16-point random Hadamard
+// transform of the quantized axis (7minutos.es, section "La metodologia de
+// formacion de cuatro partes").
+//
+// Binary32 steps, in this order (every division correctly rounded):
+//   s_enc = 2688 / A  (A = scope amax; 1 if A == 0; FLT_MAX if it overflows)
+//   t     = 1 / s_enc                                (stored decode scale)
+//   S_b   = E4M3_RNE_sat((a_b / 6) * s_enc)           (a_b = block amax)
+//   r_b   = min(s_enc / S_b, FLT_MAX), 0 when S_b == 0
+//   q_i   = E2M1_RNE_sat(x_i * r_b)
+#include "common.h"
+
+namespace mxq {
+
+__device__ __forceinline__ void scope_scales(float A, float& s_enc, float& t) {
+  float s = 2688.0f / A;
+  if (A == 0.0f) s = 1.0f;
+  if (__builtin_isinf(s)) s = kFltMax;
+  s_enc = s;
+  t = 1.0f / s;
+}
+
+// Block scale code and element multiplier for a 16-block with amax a_b.
+__device__ __forceinline__ uint32_t block_scale(float a_b, float s_enc, float& r_b) {
+  float d = (a_b / 6.0f) * s_enc;
+  d = fminf(d, kE4M3Max);                                   // saturate (d >= 0)
+  const uint32_t code = cvt_fp8x2_f32(0u, d, 0.0f, 1.0f, false) & 0xFFu;
+  const float S = e4m3_to_f32(code);
+  float r = s_enc / S;
+  r = fminf(r, kFltMax);
+  r_b = (S == 0.0f) ? 0.0f : r;
+  return code;
+}
+
+// Eight consecutive values (a 16-block is two lanes) -> 4 packed bytes.
+__device__ __forceinline__ uint32_t pack8_e2m1(const float* v, float r) {
+  uint32_t o = 0;
+  o = cvt_fp4x2_f32<0>(o, v[0] * r, v[1] * r);
+  o = cvt_fp4x2_f32<1>(o, v[2] * r, v[3] * r);
+  o = cvt_fp4x2_f32<2>(o, v[4] * r, v[5] * r);
+  o = cvt_fp4x2_f32<3>(o, v[6] * r, v[7] * r);
+  return o;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// 16-point RHT of a block split over a lane pair (8 values each, even lane
+// holds elements 0..7): w = s * v; FWHT stages 1, 2, 4 inside the lane, stage 8
+// across the pair; u = w * 0.25.
+__device__ __forceinline__ void rht16_pair(float* f, const float* sg, bool odd) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] *= sg[i];
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = f[i], b = f[i + h];
+      f[i] = a + b;
+      f[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float other = __uint_as_float(dpp_xor1(__float_as_uint(f[i])));
+    f[i] = odd ? (other - f[i]) : (f[i] + other);
+    f[i] *= 0.25f;
+  }
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  uint32_t u = __float_as_uint(v);  // v >= 0: bits order like values
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = shfl_xor_u32(u, off);
+    u = u > o ? u : o;
+  }
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------------------
+// Row-blocked quantizer: one wave per row, the row kept in registers.
+//   MODE 0: per-row scope, amax computed here (per-token NVFP4).
+//   MODE 1: scope amax read from `scope_amax[row / group_rows]` (tensor/group).
+//   MODE 2: pass 1 of MODE 1 -- only the scope amax, by atomic max.
+// CH = register chunks of 512 values (the row holds at most CH * 512 values).
+// ---------------------------------------------------------------------------
+template <int MODE, int CH, bool RHT>
+__global__ void __launch_bounds__(256)
+nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+                  int64_t group_rows, uint32_t neg_mask,
+                  uint32_t* __restrict__ scope_amax,
+                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, float* __restrict__ t_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;   // wave-uniform; with MODE 2 a partial group never syncs
+  const uint16_t* xr = x + row * ld_x;
+  const bool odd = lane & 1;
+  float sg[8];
+  if (RHT) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sg[i] = ((neg_mask >> ((odd ? 8 : 0) + i)) & 1u) ? -1.0f : 1.0f;
+  }
+
+  uint4 v[CH];
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t e = (int64_t)i * 512 + 8 * lane;
+    v[i] = (e < cols) ? *reinterpret_cast<const uint4*>(xr + e) : make_uint4(0, 0, 0, 0);
+    if (!RHT)
+      amax_bits = pk_max_u16(amax_bits, pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                                                   pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu)));
+  }
+  float A;
+  if (MODE == 1) {
+    A = __uint_as_float(scope_amax[row / group_rows]);
+  } else if (!RHT) {
+    A = __uint_as_float(max_halves(amax_bits) << 16);
+    A = wave_max_f32(A);
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      float f[8];
+      unpack8(v[i], f);
+      rht16_pair(f, sg, odd);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
+    }
+    A = wave_max_f32(m);
+  }
+  if (MODE == 2) {
+    // One atomic per workgroup when its 4 rows share a scope, else one per row.
+    const int64_t row0 = (int64_t)blockIdx.x * 4;
+    const bool shared = (row0 + 3 < rows) && (row0 / group_rows == (row0 + 3) / group_rows);
+    if (!shared) {
+      if (lane == 0 && A > 0.0f) atomicMax(scope_amax + row / group_rows, __float_as_uint(A));
+      return;
+    }
+    __shared__ uint32_t red[4];
+    if (lane == 0) red[threadIdx.x >> 6] = __float_as_uint(A);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+      if (m) atomicMax(scope_amax + row0 / group_rows, m);
+    }
+    return;
+  }
+  float s_enc, t;
+  scope_scales(A, s_enc, t);
+  if (MODE == 0 && lane == 0) t_out[row] = t;
+
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t e = (int64_t)i * 512 + 8 * lane;
+    float f[8];
+    unpack8(v[i], f);
+    if (RHT) rht16_pair(f, sg, odd);
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = fmaxf(a, __uint_as_float(dpp_xor1(__float_as_uint(a))));
+    float r;
+    const uint32_t code = block_scale(a, s_enc, r);
+    const uint32_t packed = pack8_e2m1(f, r);
+    if (e < cols) {
+      *reinterpret_cast<uint32_t*>(q + row * (cols / 2) + e / 2) = packed;
+      if (!odd) s[row * (cols / 16) + e / 16] = (uint8_t)code;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column-blocked (transposed) quantizer: blocks of 16 consecutive ROWS of x,
+// output row c of (cols, rows/2) holds column c of x. One wave = 16 rows x 512
+// columns; lane holds 8 columns x 16 rows.
+//   MODE 1: scope amax from scope_amax[c / group_rows]; MODE 2: pass 1 (amax only).
+// ---------------------------------------------------------------------------
+template <int MODE, bool RHT>
+__global__ void __launch_bounds__(256)
+nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+                  int64_t group_rows, uint32_t neg_mask,
+                  uint32_t* __restrict__ scope_amax,
+                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t col_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int64_t band = (int64_t)blockIdx.x / col_tiles * 4 + (threadIdx.x >> 6);   // 16-row band
+  const int64_t c = ((int64_t)blockIdx.x % col_tiles) * 512 + 8 * lane;
+  if (band * 16 >= rows) return;
+  const bool ok = c < cols;
+  const int64_t r0 = band * 16;
+  uint4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    v[j] = ok ? *reinterpret_cast<const uint4*>(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
+
+  float sg[16];
+  if (RHT) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sg[i] = ((neg_mask >> i) & 1u) ? -1.0f : 1.0f;
+  }
+  // two columns (one dword position p) at a time
+  float mloc[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // per-group max (MODE 2)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float f[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t w = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
+        f[j] = half ? bf16_hi(w) : bf16_lo(w);
+      }
+      if (RHT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] *= sg[i];
+#pragma unroll
+        for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (i & h) continue;
+            const float a = f[i], b = f[i + h];
+            f[i] = a + b;
+            f[i + h] = a - b;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] *= 0.25f;
+      }
+      float a = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(f[k]));
+      const int64_t col = c + 2 * p + half;
+      if (MODE == 2) {
+        mloc[0] = fmaxf(mloc[0], a);
+        continue;
+      }
+      if (!ok) continue;
+      float s_enc, t;
+      scope_scales(__uint_as_float(scope_amax[col / group_rows]), s_enc, t);
+      float r;
+      const uint32_t code = block_scale(a, s_enc, r);
+      const uint32_t lo = pack8_e2m1(f, r), hi = pack8_e2m1(f + 8, r);
+      *reinterpret_cast<uint2*>(q + col * (rows / 2) + r0 / 2) = make_uint2(lo, hi);
+      s[col * (rows / 16) + band] = (uint8_t)code;
+    }
+  }
+  if (MODE == 2) {
+    // The lane's 8 columns share a scope (group_rows % 8 == 0). Reduce over the
+    // workgroup when its whole column tile lies in one scope.
+    const int64_t tile_c0 = ((int64_t)blockIdx.x % col_tiles) * 512;
+    const int64_t tile_c1 = min(tile_c0 + 512, cols) - 1;
+    const bool shared = tile_c0 / group_rows == tile_c1 / group_rows;
+    if (!shared) {
+      if (ok && mloc[0] > 0.0f) atomicMax(scope_amax + c / group_rows, __float_as_uint(mloc[0]));
+      return;
+    }
+    float m = wave_max_f32(mloc[0]);
+    // waves whose band is past the end returned early; only use an atomic per wave
+    if (lane == 0 && m > 0.0f) atomicMax(scope_amax + tile_c0 / group_rows, __float_as_uint(m));
+  }
+}
+
+// t[g] = decode scale of scope g, from the amax in the workspace.
+__global__ void nvfp4_scope_t_kernel(const uint32_t* __restrict__ scope_amax, float* __restrict__ t, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s_enc, tt;
+  scope_scales(__uint_as_float(scope_amax[i]), s_enc, tt);
+  t[i] = tt;
+}
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <int MODE, bool RHT>
+static void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
+                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, float* t, hipStream_t st) {
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int64_t ch = (cols + 511) / 512;
+  if (ch <= 4)
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 4, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+  else if (ch <= 8)
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 8, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+  else if (ch <= 16)
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 16, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+  else
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 32, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+}
+
+template <int MODE, bool RHT>
+static void launch_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
+                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, hipStream_t st) {
+  const int64_t col_tiles = (cols + 511) / 512;
+  const int64_t bands = rows / 16;
+  dim3 grid((unsigned)((bands + 3) / 4 * col_tiles)), block(256);
+  hipLaunchKernelGGL((nvfp4_cols_kernel<MODE, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, col_tiles);
+}
+
+
+hipError_t launch_quant_nvfp4_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                    void* q, void* s, float* t, hipStream_t st) {
+  launch_rows<0, false>((const uint16_t*)x, tokens, hidden, ld_x, 1, 0u, nullptr, (uint8_t*)q, (uint8_t*)s, t, st);
+  return hipGetLastError();
+}
+
+// General entry: scope 0 = ROW, 1 = TENSOR, 2 = GROUP. RHT signs are passed as
+// a 16-bit mask (bit i set <=> sign i is -1); rht = 0 disables the transform.
+hipError_t launch_quant_nvfp4(const void* xv, int64_t rows, int64_t cols, int64_t ld_x, int scope,
+                              int64_t group_rows, int transpose, int rht, uint32_t neg_mask,
+                              void* q, void* s, float* t, uint32_t* ws_amax, int64_t n_scopes,
+                              hipStream_t st) {
+  const uint16_t* x = (const uint16_t*)xv;
+  uint8_t *qp = (uint8_t*)q, *sp = (uint8_t*)s;
+  if (scope == 0) {  // per row, one pass (transpose excluded by validation)
+    if (rht) launch_rows<0, true>(x, rows, cols, ld_x, 1, neg_mask, nullptr, qp, sp, t, st);
+    else launch_rows<0, false>(x, rows, cols, ld_x, 1, 0u, nullptr, qp, sp, t, st);
+    return hipGetLastError();
+  }
+  const int64_t gr = scope == 1 ? (transpose ? cols : rows) : group_rows;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, 0u, n_scopes);
+  if (!transpose) {
+    if (rht) {
+      launch_rows<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st);
+      launch_rows<1, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st);
+    } else {
+      launch_rows<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
+      launch_rows<1, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
+    }
+  } else {
+    if (rht) {
+      launch_cols<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st);
+      launch_cols<1, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st);
+    } else {
+      launch_cols<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st);
+      launch_cols<1, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st);
+    }
+  }
+  hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

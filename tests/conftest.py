@@ -19,3 +19,18 @@ def read_golden(name):
     """Non-comment, non-empty lines of a golden fixture."""
     with open(os.path.join(GOLDEN, name)) as f:
         return [ln.strip() for ln in f if ln.strip() and not ln.lstrip().startswith("#")]
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a visible GPU; without one they are skipped (never faked)."""
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from microscaling_precision_quantization_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mxq.h")
+P = 0x10000          # a 16-byte aligned fake device address: validation never dereferences it
+MIS = 0x10004        # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:mxq_status|size_t|const char\*|int)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"libmxq.so does not export {n}"
+
+
+def test_abi_version_and_status_strings():
+    assert B.abi_version() == 1
+    for s in range(7):
+        assert B.status_string(s)
+
+
+def q8(*a):
+    return B.lib().quantize_mxfp8(*a)
+
+
+def test_quantize_mxfp8_validation():
+    assert q8(None, 32, 32, 32, P, P, None, None, None) == 1           # x NULL
+    assert q8(P, 32, 32, 32, None, None, None, None, None) == 1        # no output
+    assert q8(P, 32, 32, 32, P, None, None, None, None) == 1           # half a pair
+    assert q8(P, 32, 48, 48, P, P, None, None, None) == 2              # cols % 32
+    assert q8(P, 40, 32, 32, None, None, P, P, None) == 2              # rows % 32 with colwise
+    assert q8(P, 32, 64, 32, P, P, None, None, None) == 2              # ld_x < cols
+    assert q8(MIS, 32, 32, 32, P, P, None, None, None) == 3            # misaligned x
+    assert q8(P, 32, 32, 36, P, P, None, None, None) == 3              # ld_x % 8
+    assert q8(P, -1, 32, 32, P, P, None, None, None) == 2
+    assert q8(P, 0, 32, 32, P, P, P, P, None) == 0                     # empty: no-op
+
+
+def test_nvfp4_validation():
+    L = B.lib()
+    assert L.quantize_nvfp4_per_token(P, 4, 40, 40, P, P, P, None) == 2       # hidden % 16
+    assert L.quantize_nvfp4_per_token(P, 4, 32768, 32768, P, P, P, None) == 2  # beyond the row limit
+    assert L.quantize_nvfp4_per_token(P, 0, 32, 32, P, P, P, None) == 0
+    bad = (ctypes.c_int8 * 16)(*([1] * 15 + [0]))
+    assert L.quantize_nvfp4(P, 32, 32, 32, 1, 0, 0, bad, P, P, P, P, 256, None) == 4   # sign not +-1
+    assert L.quantize_nvfp4(P, 32, 32, 32, 0, 0, 1, None, P, P, P, None, 0, None) == 4  # ROW + transpose
+    assert L.quantize_nvfp4(P, 32, 32, 32, 1, 0, 0, None, P, P, P, None, 0, None) == 5  # no workspace
+    assert L.quantize_nvfp4(P, 32, 32, 32, 2, 5, 0, None, P, P, P, P, 256, None) == 2   # group rows
+    assert L.quantize_nvfp4(P, 32, 32, 32, 9, 0, 0, None, P, P, P, P, 256, None) == 4   # bad scope
+
+
+def test_gemm_validation():
+    L = B.lib()
+    g = L.gemm_block_scaled
+    assert g(1, 32, 32, 48, P, P, None, 0, P, P, None, 0, P, 32, None) == 2      # K % 32
+    assert g(1, 32, 32, 64, P, None, None, 0, P, P, None, 0, P, 32, None) == 1   # scales missing
+    assert g(2, 32, 32, 64, P, P, None, 0, P, P, P, 1, P, 32, None) == 1         # NVFP4 needs t's
+    assert g(2, 32, 32, 64, P, P, P, 2, P, P, P, 1, P, 32, None) == 4            # GROUP tA scope
+    assert g(9, 32, 32, 64, P, P, None, 0, P, P, None, 0, P, 32, None) == 4
+    assert g(1, 32, 32, 64, P, P, None, 0, P, P, None, 0, P, 16, None) == 2      # ldc < N
+    assert g(1, 32, 32, 64, MIS, P, None, 0, P, P, None, 0, P, 32, None) == 3
+    assert g(1, 0, 32, 64, P, P, None, 0, P, P, None, 0, P, 32, None) == 0       # empty
+    gg = L.grouped_gemm_block_scaled
+    assert gg(1, 4, P, 0, 64, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, None, 0, None) == 5
+    assert gg(2, 4, P, 1, 64, 32, 32, 64, None, 0, P, P, P, 0, P, P, P, 2, P, P, 4096, None) == 4   # NVFP4 vary_k
+    assert gg(1, 4, None, 0, 64, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, P, 4096, None) == 1
+    assert gg(1, 0, P, 0, 0, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, None, 0, None) == 0
+
+
+def test_dequant_and_moe_validation():
+    L = B.lib()
+    assert L.dequantize(2, P, P, None, 0, 0, 4, 32, P, 0, None) == 1      # NVFP4 without t
+    assert L.dequantize(1, P, P, None, 0, 0, 4, 48, P, 0, None) == 2
+    assert L.dequantize(3, P, P, None, 0, 0, 4, 32, P, 0, None) == 4
+    assert L.moe_swiglu_quantize_nvfp4(P, 4, 24, None, P, P, P, None) == 2
+    assert L.moe_combine(P, 8, 4, 2, 6, P, P, P, None) == 2
+    assert L.moe_combine(P, 8, 0, 2, 8, P, P, P, None) == 0
+
+
+def test_scale_and_workspace_sizes():
+    assert B.scale_bytes(B.MXFP8, 256, 512) == 256 * 16
+    assert B.scale_bytes(B.NVFP4, 4096, 2048) == 4096 * 128
+    assert B.scale_bytes(B.MXFP8, 4, 48) == 0
+    L = B.lib()
+    assert L.mxq_workspace_bytes(B.OP_QUANTIZE_NVFP4, 0, 0, 3) >= 12
+    assert L.mxq_workspace_bytes(B.OP_GROUPED_GEMM, 128, 0, 0) >= 129 * 8

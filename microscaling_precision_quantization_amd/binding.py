@@ -107,18 +107,22 @@ def _u8(shape, dev):
 # Quantizers
 # ---------------------------------------------------------------------------
 
-def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True):
+def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out=None):
     """MXFP8 rowwise (R, C) + columnwise-transposed (C, R) copies of BF16 x.
 
-    Returns (q_row, s_row, q_colT, s_colT); skipped copies are None.
+    Returns (q_row, s_row, q_colT, s_colT); skipped copies are None. `out` may
+    supply preallocated (q_row, s_row, q_colT, s_colT) buffers.
     """
     _bf16(x)
     R, C = x.shape
     dev = x.device
-    q_row = _u8((R, C), dev) if rowwise else None
-    s_row = _u8((R, C // 32), dev) if rowwise else None
-    q_col = _u8((C, R), dev) if colwise else None
-    s_col = _u8((C, R // 32), dev) if colwise else None
+    if out is not None:
+        q_row, s_row, q_col, s_col = out
+    else:
+        q_row = _u8((R, C), dev) if rowwise else None
+        s_row = _u8((R, C // 32), dev) if rowwise else None
+        q_col = _u8((C, R), dev) if colwise else None
+        s_col = _u8((C, R // 32), dev) if colwise else None
     _check("quantize_mxfp8", lib().quantize_mxfp8(_ptr(x), R, C, x.stride(0), _ptr(q_row), _ptr(s_row),
                                                   _ptr(q_col), _ptr(s_col), _stream(dev)))
     return q_row, s_row, q_col, s_col

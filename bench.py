@@ -41,7 +41,7 @@ GEMM_FLOP = 2 * T * DOUT * DIN                       # each of fprop, dgrad, wgr
 QUANT_BYTES_PER_ELEM = 2 + 1 + 1 + 2 / 32            # BF16 read + two E4M3 copies + two scale sets
 QUANT_BYTES = {"x": T * DIN * QUANT_BYTES_PER_ELEM, "w": DOUT * DIN * QUANT_BYTES_PER_ELEM,
                "dy": T * DOUT * QUANT_BYTES_PER_ELEM}
-GEMM_KERNEL_SOURCES = ["microscaling_precision_quantization_amd/csrc/gemm_bf16.hip",
+GEMM_KERNEL_SOURCES = ["microscaling_precision_quantization_amd/csrc/gemm_exact.hip",
                        "microscaling_precision_quantization_amd/csrc/common.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_gemm_mxfp8_linear_2048x8192x2048.md")
 N_SETS = 4
@@ -251,7 +251,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
-                     "kernel": "gemm_bf16_dense_kernel<1> (MXFP8 operands, exact BF16 on the BF16 MFMA)",
+                     "kernel": "exact_dense_kernel<1,...> (MXFP8 operands formed exactly in BF16, BF16 MFMA)",
                      "flop_per_launch": GEMM_FLOP, "avg_launch_ms": round(launch_ms, 4)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
     }

@@ -190,7 +190,8 @@ mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float*
  *   MXQ_BF16 : A (M, K) BF16, B (N, K) BF16; scales unused.
  *   C[m * ldc + n], ldc >= N, C 4-byte aligned. Accuracy: normwise relative error
  *   <= 2e-5 against the FP64 product of the exact dequantized operands.
- *   Requires K % 32 == 0 (MXFP8), K % 32 == 0 (NVFP4), K % 8 == 0 (BF16).
+ *   Requires K % 32 == 0 (MXFP8), K % 32 == 0 (NVFP4), K % 8 == 0 (BF16), and
+ *   K <= 2^22 (32-bit operand offsets); MXQ_ERR_SHAPE otherwise.
  * ------------------------------------------------------------------------- */
 mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                              const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
@@ -241,6 +242,8 @@ mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K,
  *              with vary_k = 1 every offset is a multiple of 32 (MXFP8) or 8 (BF16).
  *              The device checks this before any tile runs; offsets that break it
  *              make the call a no-op that leaves C unwritten.
+ *   Limits     : K <= 2^22 (vary_k = 1: total <= 2^22); with a_row_index, a_rows times
+ *              the bytes of one A row must stay below 2^31. MXQ_ERR_SHAPE otherwise.
  *   workspace: device scratch of mxq_workspace_bytes(MXQ_OP_GROUPED_GEMM, groups, 0, 0).
  * ------------------------------------------------------------------------- */
 mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64_t* offsets,

@@ -33,6 +33,12 @@ namespace {
 
 constexpr int64_t kMaxRowCols = 16384;       // register-resident NVFP4 row quantizer
 constexpr int64_t kMaxGridBlocks = 0x7FFFFFFF;
+// GEMM operand reads use 32-bit buffer offsets: a 256-row tile of K-contiguous rows,
+// or (gather) the whole gathered operand, must span less than 2^31 bytes.
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
+inline int64_t gemm_row_bytes(mxq_format fmt, int64_t k) {
+  return fmt == MXQ_BF16 ? 2 * k : fmt == MXQ_MXFP8 ? k : k / 2;
+}
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -185,7 +191,7 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K, co
   if (fmt == MXQ_MXFP8 && K % 32) return MXQ_ERR_SHAPE;
   if (fmt == MXQ_NVFP4 && K % 32) return MXQ_ERR_SHAPE;
   if (fmt == MXQ_BF16 && K % 8) return MXQ_ERR_SHAPE;
-  if (ldc < N) return MXQ_ERR_SHAPE;
+  if (K > kMaxGemmK || ldc < N) return MXQ_ERR_SHAPE;
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   if (M == 0 || N == 0) return MXQ_OK;
   return hip_status(mxq::launch_gemm((int)fmt, M, N, K, A, sA, tA, ta, B, sB, tB, tb, C, ldc, S(stream)));
@@ -225,8 +231,11 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
     if (fmt == MXQ_MXFP8 && K % 32) return MXQ_ERR_SHAPE;
     if (fmt == MXQ_NVFP4 && K % 32) return MXQ_ERR_SHAPE;
     if (fmt == MXQ_BF16 && K % 8) return MXQ_ERR_SHAPE;
+    if (K > kMaxGemmK) return MXQ_ERR_SHAPE;
+    if (a_row_index && a_rows * gemm_row_bytes(fmt, K) > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   } else {
     if (total % (fmt == MXQ_MXFP8 ? 32 : 8)) return MXQ_ERR_SHAPE;
+    if (total > kMaxGemmK) return MXQ_ERR_SHAPE;
   }
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   if (groups == 0 || N == 0 || (vary_k ? M == 0 : total == 0)) return MXQ_OK;

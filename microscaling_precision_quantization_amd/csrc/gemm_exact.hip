@@ -42,12 +42,9 @@ namespace mxq {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-__device__ __attribute__((aligned(16))) const uint4 kZero16 = {0u, 0u, 0u, 0u};
-// E8M0 1.0 (0x7F) bytes: the scale read for MXFP8 blocks past the end of K.
-__device__ __attribute__((aligned(16))) const uint4 kE8M0One16 = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-
 namespace gx {
 constexpr int BK = 64;                          // K elements per stage
+constexpr int kLdsBytes = 160 * 1024;           // gfx950 LDS per workgroup
 template <int LD> struct RowBytes;
 template <> struct RowBytes<0> { static constexpr int v = 128; };   // BF16
 template <> struct RowBytes<1> { static constexpr int v = 64; };    // MXFP8
@@ -69,7 +66,7 @@ struct Cfg {
   static constexpr int SU = ScaleDma<LD, AL>::SU, SZ = ScaleDma<LD, AL>::SZ;
   static constexpr int S_BYTES = SU * (BM + BN) * 4;            // scale slots of one stage
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int NS = (4 * STAGE <= 131072) ? 4 : (3 * STAGE <= 131072 ? 3 : 2);
+  static constexpr int NS = (4 * STAGE <= kLdsBytes) ? 4 : (3 * STAGE <= kLdsBytes ? 3 : 2);
   static constexpr int IA = A_BYTES / 4096, IB = B_BYTES / 4096;   // 1 KiB wave instructions per wave
   static constexpr int IS = SU * (BM + BN) / 256;                  // 64-row scale loads per wave
   static constexpr int TI = BM / 64, TJ = BN / 64;                // 32x32 MFMA tiles per wave
@@ -114,16 +111,40 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Direct global -> LDS loads, issued through inline asm so that the compiler does
-// not pair them with its own conservative waits: all ordering is explicit here
-// (vmcnt waits before each stage's barrier, and a final vmcnt(0)). M0 holds the
-// wave's LDS base; lane l's data lands at M0 + 16 l (4 l for 1/2/4-byte loads).
+// Raw buffer resource (stride 0): reads at offset o (VGPR offset + SGPR offset,
+// both counted in the range check) return zeros when o + size > num_records.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)base;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = __builtin_amdgcn_readfirstlane(0x00020000);     // 32-bit data format, no swizzle
+  return r;
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;            // beyond every num_records used here
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
 }
-__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+
+// Buffer -> LDS direct loads. M0 holds the wave's LDS destination; lane l's data
+// lands at M0 + 16 l (dwordx4) or M0 + 4 l (ubyte / ushort / dword, zero-extended).
+// Issued through inline asm so that the compiler adds none of its own waits: all
+// ordering is explicit (vmcnt waits before each stage barrier, a final vmcnt(0)).
+// M0 is not otherwise used by these kernels.
+template <int SZ>
+__device__ __forceinline__ void buf_dma(v4i rs, uint32_t voff, uint32_t soff, uint32_t m0) {
+  soff = __builtin_amdgcn_readfirstlane(soff);           // uniform values, kept in SGPRs
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  if constexpr (SZ == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  else if constexpr (SZ == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  else if constexpr (SZ == 2)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
 template <int LD>
@@ -131,58 +152,10 @@ __device__ __forceinline__ int64_t k_bytes(int64_t k) {
   return LD == 0 ? k * 2 : LD == 1 ? k : k / 2;
 }
 
-// Per-lane description of the rows this lane streams into LDS (fixed over K).
-template <int NI>
-struct LoadRows {
-  const uint8_t* base[NI];   // row start (or nullptr when the row is out of range)
-  int lc[NI];                // logical 16-byte chunk inside the 64-K slice
-};
-
-template <int LD, int RB, int NI, int ROWS>
-__device__ __forceinline__ void setup_rows(LoadRows<NI>& L, int wave, int lane, int64_t row0, int64_t valid,
-                                           const uint8_t* ptr, int64_t ld_bytes, const ExactProblem* pa) {
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int pos = (wave * NI + j) * 1024 + lane * 16;     // byte in the operand tile
-    const int row = pos / RB;
-    const int pc = (pos % RB) / 16;
-    L.lc[j] = pc ^ swz<RB>(row);
-    const int64_t r = row0 + row;
-    int64_t src = -1;
-    if (row < ROWS && r < valid) src = pa ? exact_src_row(*pa, r) : r;
-    L.base[j] = src >= 0 ? ptr + src * ld_bytes : nullptr;
-  }
-}
-
-template <int LD, int NI>
-__device__ __forceinline__ void issue_tile(const LoadRows<NI>& L, uint8_t* lds_op, int wave, int64_t k0,
-                                           int64_t k_end) {
-  constexpr int RB = gx::RowBytes<LD>::v;
-  constexpr int EPC = LD == 0 ? 8 : LD == 1 ? 16 : 32;     // elements per 16-byte chunk
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int64_t k = k0 + (int64_t)L.lc[j] * EPC;
-    const void* src = (L.base[j] && k < k_end) ? (const void*)(L.base[j] + k_bytes<LD>(k)) : (const void*)&kZero16;
-    lds_dma16(src, lds_op + (wave * NI + j) * 1024);
-  }
-  (void)RB;
-}
-
-// 1/2/4-byte direct loads into 4-byte LDS slots.
-template <int SZ>
-__device__ __forceinline__ void lds_dma_small(const void* src, uint8_t* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-  if constexpr (SZ == 1)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-  else if constexpr (SZ == 2)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint4 lds_read16(const uint8_t* lds_op, int row, int lchunk, int RB, int sw) {
-  return *reinterpret_cast<const uint4*>(lds_op + row * RB + ((lchunk ^ sw) << 4));
-}
+typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
+__device__ __forceinline__ lds_cptr as_lds(uint32_t a) { return (lds_cptr)(uintptr_t)a; }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 lds_ld16(lds_cptr p) { return *(const __attribute__((address_space(3))) u32x4*)p; }
 
 __device__ __forceinline__ void exact_drain() {
   __builtin_amdgcn_sched_barrier(0);
@@ -225,40 +198,187 @@ __device__ __forceinline__ void e4m3_split(uint32_t code, float& p2, v2h& m2) {
   m2[1] = mh;
 }
 
+template <int I> using ic = std::integral_constant<int, I>;
+
+// Compile-time loop: f(ic<0>), ..., f(ic<N-1>).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Tile of BM x BN outputs over K in [k_begin, k_end); 4 waves in a 2 x 2 grid,
+// each owning (BM/2) x (BN/2) accumulators.
+//
+// K advances in stages of 64 (NS stages in LDS, NS - 1 loads in flight); a stage
+// splits into SBS sub-blocks of one 16-byte chunk per lane and fragment (BF16: 4
+// of 16 K, MXFP8: 2 of 32 K, NVFP4: 1 of 64 K). The raw fragments of the next
+// sub-block are read from LDS while the matrix core works on the current one;
+// the loads of the stage NS - 1 ahead are interleaved with the first sub-block's
+// MFMAs, and the barrier that publishes the next stage sits halfway through the
+// last sub-block.
 template <int LD, int BM, int BN, bool AL>
-__device__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0, uint8_t* lds1,
-                                uint8_t* lds2, uint8_t* lds3) {
+__device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0,
+                                                uint8_t* lds1, uint8_t* lds2, uint8_t* lds3) {
   using C = gx::Cfg<LD, BM, BN, AL>;
-  constexpr int RB = C::RB, NS = C::NS, TI = C::TI, TJ = C::TJ;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int RB = C::RB, NS = C::NS, TI = C::TI, TJ = C::TJ, IA = C::IA, IB = C::IB, IS = C::IS;
+  constexpr int SBS = LD == 0 ? 4 : LD == 1 ? 2 : 1;     // sub-blocks per stage
+  constexpr int NF = TI + TJ;                             // fragments per lane and sub-block
+  constexpr int BS = LD == 1 ? 32 : 16;                   // elements per scale block
+  constexpr int EPC = LD == 0 ? 8 : LD == 1 ? 16 : 32;    // elements per 16-byte chunk
+  constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave
+  static_assert((NS * SBS) % 2 == 0, "fragment double buffer needs an even sub-block count per round");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, lr = lane & 31;
 
-  LoadRows<C::IA> LA;
-  LoadRows<C::IB> LB;
-  setup_rows<LD, RB, C::IA, BM>(LA, wave, lane, m0, p.m_valid, p.A, k_bytes<LD>(p.lda), &p);
-  setup_rows<LD, RB, C::IB, BN>(LB, wave, lane, n0, p.n_valid, p.B, k_bytes<LD>(p.ldb), nullptr);
+  const int64_t ldA = k_bytes<LD>(p.lda), ldB = k_bytes<LD>(p.ldb);
+  const int64_t a_rows_tile = max((int64_t)0, min((int64_t)BM, p.m_valid - m0));
+  const int64_t b_rows_tile = max((int64_t)0, min((int64_t)BN, p.n_valid - n0));
 
-  // Scale rows this lane streams into LDS: scale load instruction q (of IS per wave)
-  // covers 64 rows of the concatenated [A rows | B rows] list; unit u of SU.
-  constexpr int BS = LD == 1 ? 32 : 16;          // elements per scale block
-  const uint8_t* s_src[C::IS > 0 ? C::IS : 1];
+  // --- operand descriptors and per-lane offsets (fixed over K) -------------------
+  // A: rebased at the tile's first row, or (gather) at the operand start with
+  // per-row offsets; rows outside the tile's valid range read zeros.
+  const v4i rsA = p.a_idx ? make_rsrc(p.A, (uint32_t)min(p.a_rows * ldA, (int64_t)0x7FFFFFFF))
+                          : make_rsrc(p.A + (p.a_base + m0) * ldA, (uint32_t)(a_rows_tile * ldA));
+  const v4i rsB = make_rsrc(p.B + n0 * ldB, (uint32_t)(b_rows_tile * ldB));
+  uint32_t voA[IA], voB[IB];
 #pragma unroll
-  for (int q = 0; q < C::IS; ++q) {
-    const int item = (wave * C::IS + q) * 64 + lane;        // in [0, SU * (BM + BN))
-    const int row = item % (BM + BN);
-    const uint8_t* base = nullptr;
-    if (row < BM) {
-      const int64_t r = m0 + row;
-      const int64_t src = r < p.m_valid ? exact_src_row(p, r) : -1;
-      if (src >= 0) base = p.sA + src * (p.lda / BS);
-    } else {
-      const int64_t n = n0 + row - BM;
-      if (n < p.n_valid) base = p.sB + n * (p.ldb / BS);
+  for (int j = 0; j < IA; ++j) {
+    const int pos = (wave * IA + j) * 1024 + lane * 16;   // byte in the A tile
+    const int row = pos / RB;
+    const int lc = ((pos % RB) / 16) ^ swz<RB>(row);      // logical chunk stored at this position
+    uint32_t o = (uint32_t)(row * ldA + lc * 16);
+    if (p.a_idx) {
+      const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
+      o = src >= 0 ? (uint32_t)(src * ldA + lc * 16) : kOutOfRange;
     }
-    s_src[q] = base;
+    voA[j] = o;
   }
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int pos = (wave * IB + j) * 1024 + lane * 16;
+    const int row = pos / RB;
+    const int lc = ((pos % RB) / 16) ^ swz<RB>(row);
+    voB[j] = (uint32_t)(row * ldB + lc * 16);
+  }
+  // Scales: load q of IS per wave covers 64 consecutive items of the [A rows | B rows]
+  // list of unit u (SU units per stage); each lands in a 4-byte LDS slot per row.
+  constexpr int BPU = (LD == 1 ? 2 : 4) / (C::SU > 0 ? C::SU : 1);   // blocks per unit
+  v4i rsS[IS > 0 ? IS : 1];
+  uint32_t voS[IS > 0 ? IS : 1];
+#pragma unroll
+  for (int q = 0; q < IS; ++q) {
+    const int item0 = (wave * IS + q) * 64;
+    const int u = item0 / (BM + BN);
+    const int r0 = item0 % (BM + BN);
+    const int row = r0 + lane;
+    if (r0 < BM) {
+      const int64_t lds_ = p.lda / BS;
+      if (p.a_idx) {
+        rsS[q] = make_rsrc(p.sA, (uint32_t)min(p.a_rows * lds_, (int64_t)0x7FFFFFFF));
+        const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
+        voS[q] = src >= 0 ? (uint32_t)(src * lds_ + u * BPU) : kOutOfRange;
+      } else {
+        rsS[q] = make_rsrc(p.sA + (p.a_base + m0) * lds_, (uint32_t)(a_rows_tile * lds_));
+        voS[q] = (uint32_t)(row * lds_ + u * BPU);
+      }
+    } else {
+      const int64_t lds_ = p.ldb / BS;
+      rsS[q] = make_rsrc(p.sB + n0 * lds_, (uint32_t)(b_rows_tile * lds_));
+      voS[q] = (uint32_t)((row - BM) * lds_ + u * BPU);
+    }
+  }
+
+  const uint32_t lbase[4] = {lds_addr(lds0), lds_addr(lds1), lds_addr(lds2), lds_addr(lds3)};
+
+  const int kb = (int)p.k_begin, ke = (int)p.k_end;       // K <= 2^22
+  const int nk = (ke - kb + gx::BK - 1) / gx::BK;
+
+  // Uniform load parameters of tile t. Tiles past the end read zeros (out-of-range
+  // SGPR offset); in the last tile, chunks and scale units at or beyond k_end are
+  // turned out of range per lane.
+  struct TileK { uint32_t sod, sos; int k0; bool tail; };
+  auto tile_k = [&](int t) {
+    TileK r;
+    r.k0 = kb + t * gx::BK;
+    const bool past = t >= nk;
+    r.sod = past ? kOutOfRange : (uint32_t)(LD == 0 ? 2 * r.k0 : LD == 1 ? r.k0 : r.k0 / 2);
+    r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS);
+    r.tail = !past && r.k0 + gx::BK > ke;
+    return r;
+  };
+  // direct load number d (0 .. OPS-1) of a tile into slot S
+  auto issue_one = [&](const TileK& tk, auto SLOT, auto D) {
+    constexpr int S = decltype(SLOT)::value, d = decltype(D)::value;
+    const uint32_t lb = lbase[S];
+    if constexpr (d < IA + IB) {
+      constexpr bool isA = d < IA;
+      constexpr int j = isA ? d : d - IA;
+      constexpr int NI = isA ? IA : IB;
+      uint32_t vo = isA ? voA[j] : voB[j];
+      if (tk.tail) {
+        const int pos = (wave * NI + j) * 1024 + lane * 16;
+        const int lc = ((pos % RB) / 16) ^ swz<RB>(pos / RB);
+        if (tk.k0 + lc * EPC >= ke) vo = kOutOfRange;
+      }
+      const uint32_t m0v = lb + (isA ? 0 : C::A_BYTES) + (uint32_t)(wave * NI + j) * 1024u;
+      buf_dma<16>(isA ? rsA : rsB, vo, tk.sod, m0v);
+    } else if constexpr (IS > 0) {
+      constexpr int q = d - IA - IB;
+      const int u = ((wave * IS + q) * 64) / (BM + BN);
+      uint32_t vo = voS[q];
+      if (tk.tail && tk.k0 + u * BPU * BS >= ke) vo = kOutOfRange;
+      const uint32_t m0v = lb + C::A_BYTES + C::B_BYTES + (uint32_t)(wave * IS + q) * 256u;
+      buf_dma<C::SZ>(rsS[q], vo, tk.sos, m0v);
+    }
+  };
+  // loads [LO, HI) of a tile
+  auto issue_range = [&](const TileK& tk, auto SLOT, auto LO, auto HI) {
+    static_for<decltype(LO)::value, decltype(HI)::value>([&](auto D) { issue_one(tk, SLOT, D); });
+  };
+
+  // --- fragments ---------------------------------------------------------------
+  // raw[f]: the lane's 16-byte chunk of fragment f (A rows i = 0..TI-1, then B rows
+  // j = 0..TJ-1) for one sub-block; sc[f]: its scale byte(s).
+  struct Frag { u32x4 raw[NF]; uint32_t sc[NF]; };
+  Frag F[2];
+
+  // LDS addresses of the fragment reads. Fragment rows start at multiples of 32 and
+  // the swizzle period is 16 rows, so the swizzle depends on lr alone: the lane part
+  // (xo) is one VGPR per sub-block, the wave part is uniform and the fragment part
+  // is an instruction offset.
+  uint32_t xo[SBS];
+#pragma unroll
+  for (int b = 0; b < SBS; ++b) xo[b] = (uint32_t)(lr * RB + (((LD == 2 ? h : 2 * b + h) ^ swz<RB>(lr)) << 4));
+  const uint32_t wA = (uint32_t)(wm * (BM / 2) * RB), wB = (uint32_t)(C::A_BYTES + wn * (BN / 2) * RB);
+  const uint32_t xs = (uint32_t)(lr * 4);                 // scale slot of the lane's row
+  const uint32_t wsA = (uint32_t)(C::A_BYTES + C::B_BYTES + wm * (BM / 2) * 4);
+  const uint32_t wsB = (uint32_t)(C::A_BYTES + C::B_BYTES + (BM + wn * (BN / 2)) * 4);
+  constexpr int SC_UNIT = (BM + BN) * 4;                  // bytes between scale units (SU == 2)
+
+  auto read_sub = [&](auto SLOT, auto SB, Frag& fr) {
+    constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value;
+    const lds_cptr pa = as_lds(lbase[S] + wA + xo[b]);
+    const lds_cptr pb = as_lds(lbase[S] + wB + xo[b]);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fr.raw[TI + j] = lds_ld16(pb + j * 32 * RB);
+    if constexpr (LD != 0) {
+      const lds_cptr sa = as_lds(lbase[S] + wsA + xs), sb = as_lds(lbase[S] + wsB + xs);
+      // MXFP8: the byte of block b; NVFP4: the two bytes of blocks 2h, 2h+1
+      const int so = LD == 1 ? (C::SU == 1 ? b : b * SC_UNIT) : (C::SU == 1 ? 2 * h : h * SC_UNIT);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const lds_cptr q = (f < TI ? sa + f * 128 : sb + (f - TI) * 128) + so;
+        fr.sc[f] = LD == 1 ? (uint32_t)*q : (uint32_t)*(const __attribute__((address_space(3))) uint16_t*)q;
+      }
+    }
+  };
 
   v16f acc[TI][TJ];
 #pragma unroll
@@ -268,168 +388,119 @@ __device__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, u
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t kb = p.k_begin, ke = p.k_end;
-  const int64_t nk = (ke - kb + gx::BK - 1) / gx::BK;
-  constexpr int OPS = C::IA + C::IB + C::IS;     // VMEM ops per tile per wave
-
-  // one LDS object per stage: the direct loads into one stage provably never alias
-  // the fragment reads of another, so no extra waits are inserted between them
-  auto stage = [&](auto SLOT) -> uint8_t* {
-    constexpr int S = decltype(SLOT)::value;
-    if constexpr (S == 0) return lds0;
-    else if constexpr (S == 1) return lds1;
-    else if constexpr (S == 2) return lds2;
-    else return lds3;
-  };
-
-  auto issue = [&](int64_t t, auto SLOT) {
-    uint8_t* st = stage(SLOT);
-    const int64_t k0 = kb + t * gx::BK;
-    if (LD != 0) {
-      // scale unit u of a row starts at block k0 / BS + u * (blocks per unit)
-      constexpr int BPU = (LD == 1 ? 2 : 4) / (C::SU > 0 ? C::SU : 1);   // blocks per unit
-      const uint8_t* dflt = reinterpret_cast<const uint8_t*>(LD == 1 ? &kE8M0One16 : &kZero16);
+  // Convert + MFMA one sub-block; hook(jj) runs after the MFMAs of B fragment jj.
+  auto mma_sub = [&](const Frag& fr, auto&& hook) {
+    if constexpr (LD == 0) {
+      v8bf fa[TI];
 #pragma unroll
-      for (int q = 0; q < C::IS; ++q) {
-        const int item = (wave * C::IS + q) * 64;                     // first item of this instruction
-        const int u = item / (BM + BN);
-        const int64_t kb0 = k0 + (int64_t)u * BPU * BS;                // first element of the unit
-        const void* src = (s_src[q] && kb0 < ke) ? (const void*)(s_src[q] + kb0 / BS) : (const void*)dflt;
-        lds_dma_small<C::SZ>(src, st + C::A_BYTES + C::B_BYTES + item * 4);
-      }
-    }
-    issue_tile<LD, C::IA>(LA, st, wave, k0, ke);
-    issue_tile<LD, C::IB>(LB, st + C::A_BYTES, wave, k0, ke);
-  };
-
-  // scale byte `blk` (block index inside the K slice) of LDS row `row` (B rows follow A rows)
-  auto scale_at = [&](const uint8_t* st, int row, int blk) -> uint32_t {
-    const uint8_t* sc = st + C::A_BYTES + C::B_BYTES;
-    if (C::SU == 1) return sc[row * 4 + blk];
-    constexpr int BPU = (LD == 1 ? 2 : 4) / 2;
-    return sc[(blk / BPU) * (BM + BN) * 4 + row * 4 + blk % BPU];
-  };
-
-  auto compute = [&](auto SLOT) {
-    const uint8_t* la = stage(SLOT);
-    const uint8_t* lb = la + C::A_BYTES;
-    if (LD == 0) {
+      for (int i = 0; i < TI; ++i) __builtin_memcpy(&fa[i], &fr.raw[i], 16);
+      static_for<0, TJ>([&](auto JJ) {
+        constexpr int j = decltype(JJ)::value;
+        v8bf fb;
+        __builtin_memcpy(&fb, &fr.raw[TI + j], 16);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v8bf fa[TI], fb[TJ];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int row = wm * (BM / 2) + i * 32 + lr;
-          const uint4 w = lds_read16(la, row, 2 * s + h, RB, swz<RB>(row));
-          __builtin_memcpy(&fa[i], &w, 16);
-        }
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int row = wn * (BN / 2) + j * 32 + lr;
-          const uint4 w = lds_read16(lb, row, 2 * s + h, RB, swz<RB>(row));
-          __builtin_memcpy(&fb[j], &w, 16);
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      }
-    } else if (LD == 1) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        v8bf fa0[TI], fa1[TI];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int row = wm * (BM / 2) + i * 32 + lr;
-          const uint4 w = lds_read16(la, row, 2 * u + h, RB, swz<RB>(row));
-          const float sc = e8m0_to_float(scale_at(la, row, u));
-          fa0[i] = mx_to_bf16(w.x, w.y, sc);
-          fa1[i] = mx_to_bf16(w.z, w.w, sc);
-        }
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int row = wn * (BN / 2) + j * 32 + lr;
-          const uint4 w = lds_read16(lb, row, 2 * u + h, RB, swz<RB>(row));
-          const float sc = e8m0_to_float(scale_at(la, BM + row, u));
-          const v8bf fb0 = mx_to_bf16(w.x, w.y, sc), fb1 = mx_to_bf16(w.z, w.w, sc);
-#pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, acc[i][j], 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, acc[i][j], 0, 0, 0);
-        }
-      }
-    } else {
-      uint4 ra[TI], rb[TJ];
+        for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][j], 0, 0, 0);
+        hook(JJ);
+      });
+    } else if constexpr (LD == 1) {
+      v8bf fa0[TI], fa1[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int row = wm * (BM / 2) + i * 32 + lr;
-        ra[i] = lds_read16(la, row, h, RB, swz<RB>(row));
+        const float s = e8m0_to_float(fr.sc[i]);
+        fa0[i] = mx_to_bf16(fr.raw[i].x, fr.raw[i].y, s);
+        fa1[i] = mx_to_bf16(fr.raw[i].z, fr.raw[i].w, s);
       }
+      static_for<0, TJ>([&](auto JJ) {
+        constexpr int j = decltype(JJ)::value;
+        const float s = e8m0_to_float(fr.sc[TI + j]);
+        const v8bf fb0 = mx_to_bf16(fr.raw[TI + j].x, fr.raw[TI + j].y, s);
+        const v8bf fb1 = mx_to_bf16(fr.raw[TI + j].z, fr.raw[TI + j].w, s);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int row = wn * (BN / 2) + j * 32 + lr;
-        rb[j] = lds_read16(lb, row, h, RB, swz<RB>(row));
-      }
+        for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, acc[i][j], 0, 0, 0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {      // 16-block 2h + half of the lane's chunk
-        v8h fa0[TI], fa1[TI];
+        for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, acc[i][j], 0, 0, 0);
+        hook(JJ);
+      });
+    } else {
+      v8h fa[2][2][TI];        // [half][dword pair][i]
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int row = wm * (BM / 2) + i * 32 + lr;
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
           float p2;
           v2h m2;
-          e4m3_split(scale_at(la, row, 2 * h + half), p2, m2);
-          fa0[i] = nv_to_f16(half ? ra[i].z : ra[i].x, p2, m2);
-          fa1[i] = nv_to_f16(half ? ra[i].w : ra[i].y, p2, m2);
+          e4m3_split((fr.sc[i] >> (8 * hf)) & 0xFF, p2, m2);
+          fa[hf][0][i] = nv_to_f16(hf ? fr.raw[i].z : fr.raw[i].x, p2, m2);
+          fa[hf][1][i] = nv_to_f16(hf ? fr.raw[i].w : fr.raw[i].y, p2, m2);
         }
+      static_for<0, TJ>([&](auto JJ) {
+        constexpr int j = decltype(JJ)::value;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int row = wn * (BN / 2) + j * 32 + lr;
+        for (int hf = 0; hf < 2; ++hf) {
           float p2;
           v2h m2;
-          e4m3_split(scale_at(la, BM + row, 2 * h + half), p2, m2);
-          const v8h fb0 = nv_to_f16(half ? rb[j].z : rb[j].x, p2, m2);
-          const v8h fb1 = nv_to_f16(half ? rb[j].w : rb[j].y, p2, m2);
+          e4m3_split((fr.sc[TI + j] >> (8 * hf)) & 0xFF, p2, m2);
+          const v8h fb0 = nv_to_f16(hf ? fr.raw[TI + j].z : fr.raw[TI + j].x, p2, m2);
+          const v8h fb1 = nv_to_f16(hf ? fr.raw[TI + j].w : fr.raw[TI + j].y, p2, m2);
 #pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa0[i], fb0, acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][0][i], fb0, acc[i][j], 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa1[i], fb1, acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][1][i], fb1, acc[i][j], 0, 0, 0);
         }
-      }
+        hook(JJ);
+      });
     }
   };
 
-  // One K tile in slot S: wait for its loads (all waves), refill the slot freed by
-  // the previous tile, compute. Tiles past the end are still issued (they read the
-  // zero / default blocks), so every step has exactly NS - 2 tiles in flight behind
-  // tile kt and one unconditional vmcnt wait suffices.
-  auto step = [&](int64_t kt, auto SLOT) {
+  // The loads of tile t + NS - 1 are spread over the first PJ B-fragment steps of
+  // sub-block 0; the barrier comes after B fragment BJ of the last sub-block.
+  constexpr int BJ = TJ / 2 - 1;
+  constexpr int PJ = SBS == 1 ? BJ + 1 : TJ;
+
+  // One stage: tile kt in slot S.
+  auto stage = [&](int kt, auto SLOT) {
     constexpr int S = decltype(SLOT)::value;
-    wait_vmcnt<(NS - 2) * OPS>();
-    __builtin_amdgcn_s_barrier();     // LDS of tile kt complete for all waves (no extra fence)
-    issue(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
-    compute(SLOT);
+    const TileK tk = tile_k(kt + NS - 1);
+    constexpr int SN = (S + 1) % NS;                     // slot of the next tile
+    constexpr int SL = (S + NS - 1) % NS;                // slot refilled now
+    static_for<0, SBS>([&](auto SB) {
+      constexpr int b = decltype(SB)::value;
+      constexpr int cur = (S * SBS + b) & 1;
+      if constexpr (b + 1 < SBS) read_sub(SLOT, ic<b + 1>{}, F[cur ^ 1]);
+      mma_sub(F[cur], [&](auto JJ) {
+        constexpr int jj = decltype(JJ)::value;
+        if constexpr (b == 0 && jj < PJ) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_range(tk, ic<SL>{}, ic<(OPS * jj) / PJ>{}, ic<(OPS * (jj + 1)) / PJ>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (b + 1 == SBS && jj == BJ) {
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<(NS - 2) * OPS>();                 // tile kt + 1 has landed (this wave's loads)
+          __builtin_amdgcn_s_barrier();                 // ... and every wave's; slot S fully read
+          __builtin_amdgcn_sched_barrier(0);
+          read_sub(ic<SN>{}, ic<0>{}, F[cur ^ 1]);
+        }
+      });
+    });
   };
 
-  // prologue: NS - 1 tiles in flight
-  issue(0, std::integral_constant<int, 0>{});
-  if constexpr (NS > 2) issue(1, std::integral_constant<int, 1>{});
-  if constexpr (NS > 3) issue(2, std::integral_constant<int, 2>{});
-  static_assert(NS <= 4, "prologue covers up to 4 stages");
+  // prologue: tiles 0 .. NS-2 in flight, then the first sub-block's fragments
+  static_for<0, NS - 1>([&](auto T) { issue_range(tile_k(T.value), T, ic<0>{}, ic<OPS>{}); });
+  wait_vmcnt<(NS - 2) * OPS>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_sub(ic<0>{}, ic<0>{}, F[0]);
 
-  for (int64_t kt = 0; kt < nk;) {
-    step(kt, std::integral_constant<int, 0>{});
-    if (++kt >= nk) break;
-    step(kt, std::integral_constant<int, 1 % NS>{});
-    if (++kt >= nk) break;
-    if constexpr (NS > 2) {
-      step(kt, std::integral_constant<int, 2 % NS>{});
-      if (++kt >= nk) break;
-    }
-    if constexpr (NS > 3) {
-      step(kt, std::integral_constant<int, 3 % NS>{});
-      ++kt;
-    }
+  // Whole rounds of NS stages: stages past the end multiply zeros (their loads
+  // are out of range), which adds nothing to the accumulators.
+  const int rounds = (nk + NS - 1) / NS;
+  for (int r = 0; r < rounds; ++r) {
+    const int kt = r * NS;
+    stage(kt, ic<0>{});
+    stage(kt + 1, ic<1 % NS>{});
+    if constexpr (NS > 2) stage(kt + 2, ic<2 % NS>{});
+    if constexpr (NS > 3) stage(kt + 3, ic<3 % NS>{});
   }
   wait_vmcnt<0>();                    // no direct load may still target this workgroup's LDS
   exact_drain();

@@ -147,6 +147,29 @@ __device__ __forceinline__ void buf_dma(v4i rs, uint32_t voff, uint32_t soff, ui
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
+// N (1..4) dwordx4 loads sharing one M0 write: load n lands at M0 + 1024 n + 16 lane.
+// The instruction offset applies to the LDS destination and to the buffer offset
+// alike (32-bit wrap-around), so each VGPR offset is pre-biased by -1024 n.
+template <int N>
+__device__ __forceinline__ void buf_dma16_group(v4i rs, const uint32_t* vo, uint32_t soff, uint32_t m0) {
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  if constexpr (N == 1)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(vo[0]), "s"(rs), "s"(soff) : "memory");
+  else if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds" ::"s"(m0), "v"(vo[0]), "v"(vo[1]), "s"(rs), "s"(soff) : "memory");
+  else if constexpr (N == 3)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 lds\n\tbuffer_load_dwordx4 %3, %4, %5 offen offset:2048 lds"
+                 ::"s"(m0), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(rs), "s"(soff) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\tbuffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+                 ::"s"(m0), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(rs), "s"(soff) : "memory");
+}
+
 template <int LD>
 __device__ __forceinline__ int64_t k_bytes(int64_t k) {
   return LD == 0 ? k * 2 : LD == 1 ? k : k / 2;
@@ -187,15 +210,23 @@ __device__ __forceinline__ v8h nv_to_f16(uint32_t w, float p2, v2h m2) {
   return r;
 }
 
-// E4M3 code -> (2^e as float, mantissa factor in [1, 2) as packed FP16). Code 0 -> (0, 1).
-__device__ __forceinline__ void e4m3_split(uint32_t code, float& p2, v2h& m2) {
-  const float S = e4m3_to_f32(code & 0x7F);
-  const uint32_t bits = __float_as_uint(S);
-  p2 = __uint_as_float(bits & 0x7F800000u);
-  const float m = S == 0.0f ? 1.0f : __uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u);
-  const _Float16 mh = (_Float16)m;        // exact: at most 3 mantissa bits
-  m2[0] = mh;
-  m2[1] = mh;
+// The scaled converts use only the exponent field of their FP32 scale operand, an
+// exponent field of 0 acting as 2^-127 (measured on MI355X). So an E8M0 code s is
+// passed as the bits s << 23 (s = 0 included), and an E4M3 block scale S as S itself.
+
+// E8M0 code -> scale operand of the MXFP8 converts.
+__device__ __forceinline__ float mx_cvt_scale(uint32_t s) { return __uint_as_float(s << 23); }
+
+// Byte SEL of `codes` (a positive E4M3 block scale S) -> the converts' scale operand
+// (applies the power-of-two part 2^e of S) and the mantissa factor S / 2^e = 1.mmm as
+// packed FP16 (exact). E4M3 subnormals are normal in FP32, so the split holds for
+// them too; S = 0 scales by 2^-127, which flushes every E2M1 value to zero in FP16.
+template <int SEL>
+__device__ __forceinline__ void e4m3_split(uint32_t codes, float& p2, v2h& m2) {
+  p2 = __builtin_amdgcn_cvt_f32_fp8((int)codes, SEL);
+  const uint32_t mh = 0x3C00u | ((__float_as_uint(p2) >> 13) & 0x3FFu);
+  const uint32_t pair = mh | (mh << 16);
+  __builtin_memcpy(&m2, &pair, 4);
 }
 
 template <int I> using ic = std::integral_constant<int, I>;
@@ -256,14 +287,14 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
       o = src >= 0 ? (uint32_t)(src * ldA + lc * 16) : kOutOfRange;
     }
-    voA[j] = o;
+    voA[j] = o - 1024u * (uint32_t)(j % 4);                // see buf_dma16_group
   }
 #pragma unroll
   for (int j = 0; j < IB; ++j) {
     const int pos = (wave * IB + j) * 1024 + lane * 16;
     const int row = pos / RB;
     const int lc = ((pos % RB) / 16) ^ swz<RB>(row);
-    voB[j] = (uint32_t)(row * ldB + lc * 16);
+    voB[j] = (uint32_t)(row * ldB + lc * 16) - 1024u * (uint32_t)(j % 4);
   }
   // Scales: load q of IS per wave covers 64 consecutive items of the [A rows | B rows]
   // list of unit u (SU units per stage); each lands in a 4-byte LDS slot per row.
@@ -308,37 +339,49 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     const bool past = t >= nk;
     r.sod = past ? kOutOfRange : (uint32_t)(LD == 0 ? 2 * r.k0 : LD == 1 ? r.k0 : r.k0 / 2);
     r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS);
-    r.tail = !past && r.k0 + gx::BK > ke;
+    r.tail = !AL && !past && r.k0 + gx::BK > ke;
     return r;
   };
-  // direct load number d (0 .. OPS-1) of a tile into slot S
-  auto issue_one = [&](const TileK& tk, auto SLOT, auto D) {
+  // DMA unit d of a tile into slot S: units 0 .. GA-1 are groups of up to 4 A loads,
+  // GA .. GA+GB-1 groups of B loads, then the IS scale loads.
+  constexpr int GA = (IA + 3) / 4, GB = (IB + 3) / 4, UNITS = GA + GB + IS;
+  auto issue_unit = [&](const TileK& tk, auto SLOT, auto D) {
     constexpr int S = decltype(SLOT)::value, d = decltype(D)::value;
     const uint32_t lb = lbase[S];
-    if constexpr (d < IA + IB) {
-      constexpr bool isA = d < IA;
-      constexpr int j = isA ? d : d - IA;
+    if constexpr (d < GA + GB) {
+      constexpr bool isA = d < GA;
+      constexpr int g = isA ? d : d - GA;
       constexpr int NI = isA ? IA : IB;
-      uint32_t vo = isA ? voA[j] : voB[j];
-      if (tk.tail) {
-        const int pos = (wave * NI + j) * 1024 + lane * 16;
-        const int lc = ((pos % RB) / 16) ^ swz<RB>(pos / RB);
-        if (tk.k0 + lc * EPC >= ke) vo = kOutOfRange;
+      constexpr int N = (NI - 4 * g) < 4 ? NI - 4 * g : 4;
+      uint32_t vo[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const int j = 4 * g + n;
+        vo[n] = isA ? voA[j] : voB[j];
+        if constexpr (!AL) {
+          if (tk.tail) {
+            const int pos = (wave * NI + j) * 1024 + lane * 16;
+            const int lc = ((pos % RB) / 16) ^ swz<RB>(pos / RB);
+            if (tk.k0 + lc * EPC >= ke) vo[n] = kOutOfRange - 1024u * (uint32_t)n;
+          }
+        }
       }
-      const uint32_t m0v = lb + (isA ? 0 : C::A_BYTES) + (uint32_t)(wave * NI + j) * 1024u;
-      buf_dma<16>(isA ? rsA : rsB, vo, tk.sod, m0v);
+      const uint32_t m0v = lb + (isA ? 0 : C::A_BYTES) + (uint32_t)(wave * NI + 4 * g) * 1024u;
+      buf_dma16_group<N>(isA ? rsA : rsB, vo, tk.sod, m0v);
     } else if constexpr (IS > 0) {
-      constexpr int q = d - IA - IB;
-      const int u = ((wave * IS + q) * 64) / (BM + BN);
+      constexpr int q = d - GA - GB;
       uint32_t vo = voS[q];
-      if (tk.tail && tk.k0 + u * BPU * BS >= ke) vo = kOutOfRange;
+      if constexpr (!AL) {
+        const int u = ((wave * IS + q) * 64) / (BM + BN);
+        if (tk.tail && tk.k0 + u * BPU * BS >= ke) vo = kOutOfRange;
+      }
       const uint32_t m0v = lb + C::A_BYTES + C::B_BYTES + (uint32_t)(wave * IS + q) * 256u;
       buf_dma<C::SZ>(rsS[q], vo, tk.sos, m0v);
     }
   };
-  // loads [LO, HI) of a tile
+  // units [LO, HI) of a tile
   auto issue_range = [&](const TileK& tk, auto SLOT, auto LO, auto HI) {
-    static_for<decltype(LO)::value, decltype(HI)::value>([&](auto D) { issue_one(tk, SLOT, D); });
+    static_for<decltype(LO)::value, decltype(HI)::value>([&](auto D) { issue_unit(tk, SLOT, D); });
   };
 
   // --- fragments ---------------------------------------------------------------
@@ -406,13 +449,13 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       v8bf fa0[TI], fa1[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const float s = e8m0_to_float(fr.sc[i]);
+        const float s = mx_cvt_scale(fr.sc[i]);
         fa0[i] = mx_to_bf16(fr.raw[i].x, fr.raw[i].y, s);
         fa1[i] = mx_to_bf16(fr.raw[i].z, fr.raw[i].w, s);
       }
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
-        const float s = e8m0_to_float(fr.sc[TI + j]);
+        const float s = mx_cvt_scale(fr.sc[TI + j]);
         const v8bf fb0 = mx_to_bf16(fr.raw[TI + j].x, fr.raw[TI + j].y, s);
         const v8bf fb1 = mx_to_bf16(fr.raw[TI + j].z, fr.raw[TI + j].w, s);
 #pragma unroll
@@ -425,28 +468,30 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       v8h fa[2][2][TI];        // [half][dword pair][i]
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float p2;
-          v2h m2;
-          e4m3_split((fr.sc[i] >> (8 * hf)) & 0xFF, p2, m2);
-          fa[hf][0][i] = nv_to_f16(hf ? fr.raw[i].z : fr.raw[i].x, p2, m2);
-          fa[hf][1][i] = nv_to_f16(hf ? fr.raw[i].w : fr.raw[i].y, p2, m2);
-        }
+      {
+        float p2;
+        v2h m2;
+        e4m3_split<0>(fr.sc[i], p2, m2);
+        fa[0][0][i] = nv_to_f16(fr.raw[i].x, p2, m2);
+        fa[0][1][i] = nv_to_f16(fr.raw[i].y, p2, m2);
+        e4m3_split<1>(fr.sc[i], p2, m2);
+        fa[1][0][i] = nv_to_f16(fr.raw[i].z, p2, m2);
+        fa[1][1][i] = nv_to_f16(fr.raw[i].w, p2, m2);
+      }
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        static_for<0, 2>([&](auto HF) {
+          constexpr int hf = decltype(HF)::value;
           float p2;
           v2h m2;
-          e4m3_split((fr.sc[TI + j] >> (8 * hf)) & 0xFF, p2, m2);
+          e4m3_split<hf>(fr.sc[TI + j], p2, m2);
           const v8h fb0 = nv_to_f16(hf ? fr.raw[TI + j].z : fr.raw[TI + j].x, p2, m2);
           const v8h fb1 = nv_to_f16(hf ? fr.raw[TI + j].w : fr.raw[TI + j].y, p2, m2);
 #pragma unroll
           for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][0][i], fb0, acc[i][j], 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][1][i], fb1, acc[i][j], 0, 0, 0);
-        }
+        });
         hook(JJ);
       });
     }
@@ -466,12 +511,15 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     static_for<0, SBS>([&](auto SB) {
       constexpr int b = decltype(SB)::value;
       constexpr int cur = (S * SBS + b) & 1;
-      if constexpr (b + 1 < SBS) read_sub(SLOT, ic<b + 1>{}, F[cur ^ 1]);
+      if constexpr (b + 1 < SBS) {
+        read_sub(SLOT, ic<b + 1>{}, F[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);              // keep the prefetch ahead of this sub-block's MFMAs
+      }
       mma_sub(F[cur], [&](auto JJ) {
         constexpr int jj = decltype(JJ)::value;
         if constexpr (b == 0 && jj < PJ) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_range(tk, ic<SL>{}, ic<(OPS * jj) / PJ>{}, ic<(OPS * (jj + 1)) / PJ>{});
+          issue_range(tk, ic<SL>{}, ic<(UNITS * jj) / PJ>{}, ic<(UNITS * (jj + 1)) / PJ>{});
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (b + 1 == SBS && jj == BJ) {
@@ -480,17 +528,19 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           __builtin_amdgcn_s_barrier();                 // ... and every wave's; slot S fully read
           __builtin_amdgcn_sched_barrier(0);
           read_sub(ic<SN>{}, ic<0>{}, F[cur ^ 1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       });
     });
   };
 
   // prologue: tiles 0 .. NS-2 in flight, then the first sub-block's fragments
-  static_for<0, NS - 1>([&](auto T) { issue_range(tile_k(T.value), T, ic<0>{}, ic<OPS>{}); });
+  static_for<0, NS - 1>([&](auto T) { issue_range(tile_k(T.value), T, ic<0>{}, ic<UNITS>{}); });
   wait_vmcnt<(NS - 2) * OPS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_sub(ic<0>{}, ic<0>{}, F[0]);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Whole rounds of NS stages: stages past the end multiply zeros (their loads
   // are out of range), which adds nothing to the accumulators.
@@ -551,7 +601,7 @@ __device__ __forceinline__ bool exact_map_tile(int64_t b, int64_t tiles_m, int64
   __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::NS > 3 ? C::STAGE : 16];
 
 template <int LD, int BM, int BN, bool SU16>
-__global__ void __launch_bounds__(256, 1) exact_dense_kernel(ExactProblem p, int64_t tiles_m, int64_t tiles_n) {
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) exact_dense_kernel(ExactProblem p, int64_t tiles_m, int64_t tiles_n) {
   using C = gx::Cfg<LD, BM, BN, SU16>;
   MXQ_EXACT_LDS(C)
   int64_t tm, tn;
@@ -563,7 +613,7 @@ __global__ void __launch_bounds__(256, 1) exact_dense_kernel(ExactProblem p, int
 //   vary_k = 0: group g covers slots [off[g], off[g+1]), B_g = expert g of a stacked B;
 //   vary_k = 1: group g reduces over k in [off[g], off[g+1]) into C_g = C + g*M*N.
 template <int LD, int BM, int BN, bool SU16>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, const int64_t* __restrict__ tile_prefix,
                      int64_t groups, int vary_k, int64_t M, int64_t N, int64_t tiles_n) {
   using C = gx::Cfg<LD, BM, BN, SU16>;
@@ -602,10 +652,8 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-static int pick_tile(int ld, int64_t M, int64_t N) {
+static int pick_tile(int64_t M, int64_t N) {
   // 256 x 256 unless that leaves most of the 256 CUs idle; then 128 x 128.
-  // NVFP4 always 128 x 128: its 256-wide variant does not fit the register file.
-  if (ld == 2) return 128;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   return t256 >= 192 ? 256 : 128;
 }
@@ -619,13 +667,11 @@ static void launch_dense_t(const ExactProblem& p, int64_t M, int64_t N, hipStrea
 
 template <int LD>
 static void launch_dense_ld(const ExactProblem& p, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const bool su16 = LD == 0 || (K % 64 == 0);      // 64-aligned scale rows and slices
-  const int bt = pick_tile(LD, M, N);
-  if constexpr (LD != 2) {
-    if (bt == 256) {
-      if (su16) launch_dense_t<LD, 256, true>(p, M, N, st); else launch_dense_t<LD, 256, false>(p, M, N, st);
-      return;
-    }
+  const bool su16 = K % 64 == 0;                   // every K tile full and 64-aligned
+  const int bt = pick_tile(M, N);
+  if (bt == 256) {
+    if (su16) launch_dense_t<LD, 256, true>(p, M, N, st); else launch_dense_t<LD, 256, false>(p, M, N, st);
+    return;
   }
   if (su16) launch_dense_t<LD, 128, true>(p, M, N, st); else launch_dense_t<LD, 128, false>(p, M, N, st);
 }
@@ -697,9 +743,9 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   } else {
     p.m_valid = M; p.lda = total; p.n_valid = N; p.ldb = total; p.k_begin = 0; p.k_end = 0;
   }
-  // Scale rows and K slices are 64-aligned unless K % 64 == 32 (or vary_k slices,
-  // which start at multiples of 32 only).
-  const bool su16 = fmt == 3 || (p.lda % 64 == 0 && !vary_k);
+  // Every K tile is full and 64-aligned unless K % 64 != 0 or the groups split K
+  // (vary_k group boundaries are multiples of 32 / 8 only).
+  const bool su16 = p.lda % 64 == 0 && !vary_k;
   if (fmt == 1) {
     if (su16) launch_grouped_t<1, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
     else launch_grouped_t<1, BT, false>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
@@ -707,7 +753,8 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
     if (su16) launch_grouped_t<2, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
     else launch_grouped_t<2, BT, false>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
   } else {
-    launch_grouped_t<0, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+    if (su16) launch_grouped_t<0, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+    else launch_grouped_t<0, BT, false>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
   }
   return hipGetLastError();
 }

@@ -138,6 +138,30 @@ def test_bf16_gemm_dense(mnk):
     assert_gemm_close(host(c), ref, f"bf16 {mnk}")
 
 
+@pytest.mark.parametrize("K", [512, 544])
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4", "bf16"])
+def test_dense_256_tiles_ragged(fmt, K):
+    """M, N large enough for the 256 x 256 tile kernel, ragged in M and N; K = 544
+    leaves a half K stage (per-lane tail handling and 1-block scale loads)."""
+    M, N = 4196, 3112
+    g = inputs.rng(86, K + len(fmt))
+    a = inputs.to_bf16_bits(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))
+    b = inputs.normal_bf16(g, (N, K), 0.05)
+    if fmt == "mxfp8":
+        qa, sa, ah = mx_operands(a)
+        qb, sb, bh = mx_operands(b)
+        c = mxq.gemm_block_scaled(mxq.MXFP8, qa, sa, qb, sb)
+    elif fmt == "nvfp4":
+        qa, sa, ta, ah = nv_token(a)
+        qb, sb, tb = mxq.quantize_nvfp4(dev_bf16(b), scope="tensor")
+        bh = onv.dequantize_exact(host(qb), host(sb), np.repeat(host(tb), N))
+        c = mxq.gemm_block_scaled(mxq.NVFP4, qa, sa, qb, sb, tA=ta, tB=tb, tA_scope="row", tB_scope="tensor")
+    else:
+        c = mxq.gemm_block_scaled(mxq.BF16, dev_bf16(a), None, dev_bf16(b), None)
+        ah, bh = F.bf16_bits_to_f32(a), F.bf16_bits_to_f32(b)
+    assert_gemm_close(host(c), og.gemm_tn_fp64(ah, bh), f"{fmt} 256-tile {M}x{N}x{K}")
+
+
 # ------------------------------- grouped -----------------------------------
 
 def small_moe(T=96, H=256, G=8, k=2, N=192, seed=0):

@@ -50,29 +50,38 @@ template <> struct RowBytes<0> { static constexpr int v = 128; };   // BF16
 template <> struct RowBytes<1> { static constexpr int v = 64; };    // MXFP8
 template <> struct RowBytes<2> { static constexpr int v = 32; };    // NVFP4
 
-// Scale staging per K slice: SU direct loads of SZ bytes per row, each landing in a
-// 4-byte LDS slot per row (gfx950 places 1/2/4-byte direct loads at base + 4 lane).
-//   MXFP8, K % 64 == 0: one 2-byte load (32-blocks 0, 1); otherwise two 1-byte loads.
-//   NVFP4, K % 64 == 0: one 4-byte load (16-blocks 0..3); otherwise two 2-byte loads.
-template <int LD, bool AL> struct ScaleDma {
-  static constexpr int SU = LD == 0 ? 0 : (AL ? 1 : 2);
-  static constexpr int SZ = LD == 1 ? (AL ? 2 : 1) : (AL ? 4 : 2);
+// Scale modes (SM):
+//   0  general: K tiles may end early; per stage, one direct load per row and scale
+//      unit (MXFP8: 1 byte = one 32-block per unit, NVFP4: 2 bytes = two 16-blocks).
+//   1  K % 64 == 0: per stage, one load per row of all the stage's blocks (2 / 4 bytes).
+//   2  K % 64 == 0 and 16-byte aligned scale rows: 16 bytes per row (8 MXFP8 / 4 NVFP4
+//      stages) in one load, double-buffered in a separate LDS area; cuts the scale
+//      cache-line requests by 8 / 4.
+// Each per-stage load lands in a 4-byte LDS slot per row (gfx950 places 1/2/4-byte
+// direct loads at base + 4 lane); chunked scales in a 16-byte slot per row.
+template <int LD, int SM> struct ScaleDma {
+  static constexpr int SU = (LD == 0 || SM == 2) ? 0 : (SM == 1 ? 1 : 2);
+  static constexpr int SZ = LD == 1 ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
 };
 
-template <int LD, int BM, int BN, bool AL = true>
+template <int LD, int BM, int BN, int SM>
 struct Cfg {
   static constexpr int RB = RowBytes<LD>::v;
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-  static constexpr int SU = ScaleDma<LD, AL>::SU, SZ = ScaleDma<LD, AL>::SZ;
-  static constexpr int S_BYTES = SU * (BM + BN) * 4;            // scale slots of one stage
+  static constexpr int SU = ScaleDma<LD, SM>::SU, SZ = ScaleDma<LD, SM>::SZ;
+  static constexpr bool CH = SM == 2 && LD != 0;                 // chunked scales
+  static constexpr int SPC = LD == 1 ? 8 : 4;                     // stages per scale chunk
+  static constexpr int CH_HALF = CH ? (BM + BN) * 16 : 0;         // one chunk buffer
+  static constexpr int S_BYTES = SU * (BM + BN) * 4;              // scale slots of one stage
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int NS = (4 * STAGE <= kLdsBytes) ? 4 : (3 * STAGE <= kLdsBytes ? 3 : 2);
-  static constexpr int IA = A_BYTES / 4096, IB = B_BYTES / 4096;   // 1 KiB wave instructions per wave
-  static constexpr int IS = SU * (BM + BN) / 256;                  // 64-row scale loads per wave
+  static constexpr int FREE = kLdsBytes - 2 * CH_HALF;
+  static constexpr int NS = (4 * STAGE <= FREE) ? 4 : (3 * STAGE <= FREE ? 3 : 2);
+  static constexpr int IA = A_BYTES / 4096, IB = B_BYTES / 4096;  // 1 KiB wave instructions per wave
+  static constexpr int IS = SU * (BM + BN) / 256;                 // 64-row scale loads per wave
+  static constexpr int XS = CH ? (BM + BN) / 256 : 0;             // chunk loads per wave
   static constexpr int TI = BM / 64, TJ = BN / 64;                // 32x32 MFMA tiles per wave
-  static constexpr int ROWS256 = 256 / RB;                         // rows per 256-byte bank span
-  static constexpr int CHUNKS = RB / 16;
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile must split into 1 KiB wave loads");
+  static_assert(!CH || NS == 4, "chunked scales assume four stages");
 };
 }  // namespace gx
 
@@ -250,17 +259,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the loads of the stage NS - 1 ahead are interleaved with the first sub-block's
 // MFMAs, and the barrier that publishes the next stage sits halfway through the
 // last sub-block.
-template <int LD, int BM, int BN, bool AL>
+template <int LD, int BM, int BN, int SM>
 __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0,
-                                                uint8_t* lds1, uint8_t* lds2, uint8_t* lds3) {
-  using C = gx::Cfg<LD, BM, BN, AL>;
+                                                uint8_t* lds1, uint8_t* lds2, uint8_t* lds3, uint8_t* ldsc) {
+  using C = gx::Cfg<LD, BM, BN, SM>;
+  constexpr bool AL = SM >= 1;                            // every K tile full and 64-aligned
+  constexpr bool CH = C::CH;
+  constexpr int XS = C::XS, SPC = C::SPC;
   constexpr int RB = C::RB, NS = C::NS, TI = C::TI, TJ = C::TJ, IA = C::IA, IB = C::IB, IS = C::IS;
   constexpr int SBS = LD == 0 ? 4 : LD == 1 ? 2 : 1;     // sub-blocks per stage
   constexpr int NF = TI + TJ;                             // fragments per lane and sub-block
   constexpr int BS = LD == 1 ? 32 : 16;                   // elements per scale block
   constexpr int EPC = LD == 0 ? 8 : LD == 1 ? 16 : 32;    // elements per 16-byte chunk
-  constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave
-  static_assert((NS * SBS) % 2 == 0, "fragment double buffer needs an even sub-block count per round");
+  constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave (chunks aside)
+  constexpr int R = CH ? (SPC > NS ? SPC : NS) : NS;      // stages per unrolled round
+  static_assert(R % NS == 0 && (!CH || R % SPC == 0), "round must cover whole slot and chunk cycles");
+  static_assert((R * SBS) % 2 == 0, "fragment double buffer needs an even sub-block count per round");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -324,6 +338,33 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     }
   }
 
+  // Chunked scales: load q of XS per wave covers rows (wave XS + q) 64 + lane of the
+  // [A rows | B rows] list, 16 bytes (one chunk) per row; all loads of a wave fall in
+  // one operand (BM is a multiple of 64 XS) and share one M0 write.
+  v4i rsX = rsA;
+  uint32_t voX[XS > 0 ? XS : 1];
+  if constexpr (CH) {
+    static_assert(BM % (64 * XS) == 0, "chunk loads of a wave must stay in one operand");
+    const bool xa = wave * XS * 64 < BM;
+    const int64_t lds_ = (xa ? p.lda : p.ldb) / BS;        // scale bytes per row
+#pragma unroll
+    for (int q = 0; q < XS; ++q) {
+      const int row = (wave * XS + q) * 64 + lane;
+      uint32_t o;
+      if (xa && p.a_idx) {
+        const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
+        o = src >= 0 ? (uint32_t)(src * lds_) : kOutOfRange;
+      } else {
+        o = (uint32_t)((xa ? row : row - BM) * lds_);
+      }
+      voX[q] = o - 1024u * (uint32_t)q;
+    }
+    if (xa) rsX = p.a_idx ? make_rsrc(p.sA, (uint32_t)min(p.a_rows * lds_, (int64_t)0x7FFFFFFF))
+                          : make_rsrc(p.sA + (p.a_base + m0) * lds_, (uint32_t)(a_rows_tile * lds_));
+    else rsX = make_rsrc(p.sB + n0 * lds_, (uint32_t)(b_rows_tile * lds_));
+  }
+  const uint32_t lbase_c = lds_addr(ldsc);
+
   const uint32_t lbase[4] = {lds_addr(lds0), lds_addr(lds1), lds_addr(lds2), lds_addr(lds3)};
 
   const int kb = (int)p.k_begin, ke = (int)p.k_end;       // K <= 2^22
@@ -383,6 +424,14 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   auto issue_range = [&](const TileK& tk, auto SLOT, auto LO, auto HI) {
     static_for<decltype(LO)::value, decltype(HI)::value>([&](auto D) { issue_unit(tk, SLOT, D); });
   };
+  // scale chunk c (stages [SPC c, SPC c + SPC)) into chunk buffer c % 2
+  auto issue_chunk = [&](int c) {
+    if constexpr (CH) {
+      const uint32_t so = c * SPC < nk ? (uint32_t)(16 * c) : kOutOfRange;
+      const uint32_t m0v = lbase_c + (uint32_t)(c & 1) * C::CH_HALF + (uint32_t)(wave * XS) * 1024u;
+      buf_dma16_group<XS>(rsX, voX, so, m0v);
+    }
+  };
 
   // --- fragments ---------------------------------------------------------------
   // raw[f]: the lane's 16-byte chunk of fragment f (A rows i = 0..TI-1, then B rows
@@ -403,7 +452,14 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   const uint32_t wsB = (uint32_t)(C::A_BYTES + C::B_BYTES + (BM + wn * (BN / 2)) * 4);
   constexpr int SC_UNIT = (BM + BN) * 4;                  // bytes between scale units (SU == 2)
 
-  auto read_sub = [&](auto SLOT, auto SB, Frag& fr) {
+  // scales of stage t in the chunk buffers: row r's byte (MXFP8 block b) or byte pair
+  // (NVFP4 blocks 2h, 2h+1) at chunk + 16 r + (t % SPC) * bytes per stage
+  const uint32_t xsc = (uint32_t)(lr * 16 + (LD == 2 ? 2 * h : 0));
+  const uint32_t wcA = (uint32_t)(wm * (BM / 2) * 16), wcB = (uint32_t)((BM + wn * (BN / 2)) * 16);
+  auto chunk_base = [&](int t) -> uint32_t {
+    return lbase_c + (uint32_t)((t / SPC) & 1) * C::CH_HALF + (uint32_t)(t % SPC) * (LD == 1 ? 2 : 4);
+  };
+  auto read_sub = [&](int t, auto SLOT, auto SB, Frag& fr) {
     constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value;
     const lds_cptr pa = as_lds(lbase[S] + wA + xo[b]);
     const lds_cptr pb = as_lds(lbase[S] + wB + xo[b]);
@@ -411,7 +467,15 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     for (int i = 0; i < TI; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) fr.raw[TI + j] = lds_ld16(pb + j * 32 * RB);
-    if constexpr (LD != 0) {
+    if constexpr (CH) {
+      const uint32_t cb = chunk_base(t);
+      const lds_cptr sa = as_lds(cb + wcA + xsc), sb = as_lds(cb + wcB + xsc);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const lds_cptr q = (f < TI ? sa + f * 512 : sb + (f - TI) * 512) + (LD == 1 ? b : 0);
+        fr.sc[f] = LD == 1 ? (uint32_t)*q : (uint32_t)*(const __attribute__((address_space(3))) uint16_t*)q;
+      }
+    } else if constexpr (LD != 0) {
       const lds_cptr sa = as_lds(lbase[S] + wsA + xs), sb = as_lds(lbase[S] + wsB + xs);
       // MXFP8: the byte of block b; NVFP4: the two bytes of blocks 2h, 2h+1
       const int so = LD == 1 ? (C::SU == 1 ? b : b * SC_UNIT) : (C::SU == 1 ? 2 * h : h * SC_UNIT);
@@ -502,21 +566,41 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   constexpr int BJ = TJ / 2 - 1;
   constexpr int PJ = SBS == 1 ? BJ + 1 : TJ;
 
-  // One stage: tile kt in slot S.
-  auto stage = [&](int kt, auto SLOT) {
-    constexpr int S = decltype(SLOT)::value;
+  // Loads issued after tile t+1's data (issued in stage t+2-NS): the data of the
+  // NS-2 later tiles, plus the chunk loads of chunk-start stages among the last NS-2
+  // stages (issued ahead of their stage's data).
+  auto allowed = [](auto RI) constexpr {
+    constexpr int ri = decltype(RI)::value;
+    int n = (NS - 2) * OPS;
+    if constexpr (CH)
+      for (int d = 0; d <= NS - 3; ++d)
+        if (((ri - d) % R + R) % R % SPC == 0) n += XS;
+    return n;
+  };
+
+  // One stage: tile kt (round position RI) in slot RI % NS.
+  auto stage = [&](int kt, auto RI) {
+    constexpr int ri = decltype(RI)::value;
+    constexpr int S = ri % NS;
+    constexpr int SN = (ri + 1) % NS;                    // slot of the next tile
+    constexpr int SL = (ri + NS - 1) % NS;               // slot refilled now
+    constexpr int WAIT = allowed(RI);
+    static_assert(WAIT < 64, "vmcnt range");
     const TileK tk = tile_k(kt + NS - 1);
-    constexpr int SN = (S + 1) % NS;                     // slot of the next tile
-    constexpr int SL = (S + NS - 1) % NS;                // slot refilled now
     static_for<0, SBS>([&](auto SB) {
       constexpr int b = decltype(SB)::value;
-      constexpr int cur = (S * SBS + b) & 1;
+      constexpr int cur = (ri * SBS + b) & 1;
       if constexpr (b + 1 < SBS) {
-        read_sub(SLOT, ic<b + 1>{}, F[cur ^ 1]);
+        read_sub(kt, ic<S>{}, ic<b + 1>{}, F[cur ^ 1]);
         __builtin_amdgcn_sched_barrier(0);              // keep the prefetch ahead of this sub-block's MFMAs
       }
       mma_sub(F[cur], [&](auto JJ) {
         constexpr int jj = decltype(JJ)::value;
+        if constexpr (b == 0 && jj == 0 && CH && ri % SPC == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_chunk(kt / SPC + 1);                    // the next chunk, ahead of this stage's data loads
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (b == 0 && jj < PJ) {
           __builtin_amdgcn_sched_barrier(0);
           issue_range(tk, ic<SL>{}, ic<(UNITS * jj) / PJ>{}, ic<(UNITS * (jj + 1)) / PJ>{});
@@ -524,33 +608,31 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         }
         if constexpr (b + 1 == SBS && jj == BJ) {
           __builtin_amdgcn_sched_barrier(0);
-          wait_vmcnt<(NS - 2) * OPS>();                 // tile kt + 1 has landed (this wave's loads)
+          wait_vmcnt<WAIT>();                           // tile kt + 1 has landed (this wave's loads)
           __builtin_amdgcn_s_barrier();                 // ... and every wave's; slot S fully read
           __builtin_amdgcn_sched_barrier(0);
-          read_sub(ic<SN>{}, ic<0>{}, F[cur ^ 1]);
+          read_sub(kt + 1, ic<SN>{}, ic<0>{}, F[cur ^ 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       });
     });
   };
 
-  // prologue: tiles 0 .. NS-2 in flight, then the first sub-block's fragments
+  // prologue: scale chunk 0, tiles 0 .. NS-2 in flight, then the first sub-block's fragments
+  issue_chunk(0);
   static_for<0, NS - 1>([&](auto T) { issue_range(tile_k(T.value), T, ic<0>{}, ic<UNITS>{}); });
   wait_vmcnt<(NS - 2) * OPS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_sub(ic<0>{}, ic<0>{}, F[0]);
+  read_sub(0, ic<0>{}, ic<0>{}, F[0]);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Whole rounds of NS stages: stages past the end multiply zeros (their loads
-  // are out of range), which adds nothing to the accumulators.
-  const int rounds = (nk + NS - 1) / NS;
+  // Whole rounds of R stages: stages past the end multiply zeros (their loads are
+  // out of range), which adds nothing to the accumulators.
+  const int rounds = (nk + R - 1) / R;
   for (int r = 0; r < rounds; ++r) {
-    const int kt = r * NS;
-    stage(kt, ic<0>{});
-    stage(kt + 1, ic<1 % NS>{});
-    if constexpr (NS > 2) stage(kt + 2, ic<2 % NS>{});
-    if constexpr (NS > 3) stage(kt + 3, ic<3 % NS>{});
+    const int kt = r * R;
+    static_for<0, R>([&](auto RI) { stage(kt + RI.value, RI); });
   }
   wait_vmcnt<0>();                    // no direct load may still target this workgroup's LDS
   exact_drain();
@@ -598,25 +680,26 @@ __device__ __forceinline__ bool exact_map_tile(int64_t b, int64_t tiles_m, int64
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE];                    \
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];                    \
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::NS > 2 ? C::STAGE : 16];   \
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::NS > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::NS > 3 ? C::STAGE : 16];                 \
+  __shared__ __attribute__((aligned(1024))) uint8_t ldsc[C::CH ? 2 * C::CH_HALF : 16];
 
-template <int LD, int BM, int BN, bool SU16>
+template <int LD, int BM, int BN, int SM>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) exact_dense_kernel(ExactProblem p, int64_t tiles_m, int64_t tiles_n) {
-  using C = gx::Cfg<LD, BM, BN, SU16>;
+  using C = gx::Cfg<LD, BM, BN, SM>;
   MXQ_EXACT_LDS(C)
   int64_t tm, tn;
   if (!exact_map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
-  exact_gemm_tile<LD, BM, BN, SU16>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3);
+  exact_gemm_tile<LD, BM, BN, SM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // Grouped: tile_prefix[g] = first tile of group g.
 //   vary_k = 0: group g covers slots [off[g], off[g+1]), B_g = expert g of a stacked B;
 //   vary_k = 1: group g reduces over k in [off[g], off[g+1]) into C_g = C + g*M*N.
-template <int LD, int BM, int BN, bool SU16>
+template <int LD, int BM, int BN, int SM>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, const int64_t* __restrict__ tile_prefix,
                      int64_t groups, int vary_k, int64_t M, int64_t N, int64_t tiles_n) {
-  using C = gx::Cfg<LD, BM, BN, SU16>;
+  using C = gx::Cfg<LD, BM, BN, SM>;
   MXQ_EXACT_LDS(C)
   const int64_t tile = blockIdx.x;
   if (tile >= tile_prefix[groups]) return;
@@ -646,7 +729,7 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.k_end = offsets[g + 1];
     p.C = base.C + g * M * N;
   }
-  exact_gemm_tile<LD, BM, BN, SU16>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3);
+  exact_gemm_tile<LD, BM, BN, SM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // ---------------------------------------------------------------------------
@@ -658,22 +741,37 @@ static int pick_tile(int64_t M, int64_t N) {
   return t256 >= 192 ? 256 : 128;
 }
 
-template <int LD, int BT, bool SU16>
+template <int LD, int BT, int SM>
 static void launch_dense_t(const ExactProblem& p, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tm = (M + BT - 1) / BT, tn = (N + BT - 1) / BT;
   const int64_t blocks = (tm * tn + 7) / 8 * 8;
-  hipLaunchKernelGGL((exact_dense_kernel<LD, BT, BT, SU16>), dim3((unsigned)blocks), dim3(256), 0, st, p, tm, tn);
+  hipLaunchKernelGGL((exact_dense_kernel<LD, BT, BT, SM>), dim3((unsigned)blocks), dim3(256), 0, st, p, tm, tn);
+}
+
+// Scale mode: 2 when K % 64 == 0 and every scale row starts 16-byte aligned
+// (K % 512 == 0 for MXFP8, K % 256 == 0 for NVFP4), 1 when K % 64 == 0, else 0.
+static int scale_mode(int ld, int64_t K, bool vary_k) {
+  if (vary_k || K % 64) return 0;
+  if (ld == 1 && K % 512 == 0) return 2;
+  if (ld == 2 && K % 256 == 0) return 2;
+  return 1;
+}
+
+template <int LD, int BT>
+static void launch_dense_bt(const ExactProblem& p, int64_t M, int64_t N, int sm, hipStream_t st) {
+  if constexpr (LD != 0) {
+    if (sm == 2) { launch_dense_t<LD, BT, 2>(p, M, N, st); return; }
+  }
+  if (sm == 2) launch_dense_t<LD, BT, 1>(p, M, N, st);
+  else if (sm == 1) launch_dense_t<LD, BT, 1>(p, M, N, st);
+  else launch_dense_t<LD, BT, 0>(p, M, N, st);
 }
 
 template <int LD>
 static void launch_dense_ld(const ExactProblem& p, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const bool su16 = K % 64 == 0;                   // every K tile full and 64-aligned
-  const int bt = pick_tile(M, N);
-  if (bt == 256) {
-    if (su16) launch_dense_t<LD, 256, true>(p, M, N, st); else launch_dense_t<LD, 256, false>(p, M, N, st);
-    return;
-  }
-  if (su16) launch_dense_t<LD, 128, true>(p, M, N, st); else launch_dense_t<LD, 128, false>(p, M, N, st);
+  const int sm = scale_mode(LD, K, false);
+  if (pick_tile(M, N) == 256) launch_dense_bt<LD, 256>(p, M, N, sm, st);
+  else launch_dense_bt<LD, 128>(p, M, N, sm, st);
 }
 
 hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const float* tA,
@@ -712,11 +810,11 @@ __global__ void tile_prefix_kernel(const int64_t* __restrict__ offsets, int64_t 
 
 size_t grouped_gemm_ws_bytes(int64_t groups) { return (size_t)(((groups + 1) * 8 + 255) / 256 * 256); }
 
-template <int LD, int BT, bool SU16>
+template <int LD, int BT, int SM>
 static void launch_grouped_t(const ExactProblem& p, const int64_t* offsets, const int64_t* prefix, int64_t max_tiles,
                              int64_t groups, int vary_k, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tn = (N + BT - 1) / BT;
-  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SU16>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
+  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
                      prefix, groups, vary_k, M, N, tn);
 }
 
@@ -743,19 +841,21 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   } else {
     p.m_valid = M; p.lda = total; p.n_valid = N; p.ldb = total; p.k_begin = 0; p.k_end = 0;
   }
-  // Every K tile is full and 64-aligned unless K % 64 != 0 or the groups split K
-  // (vary_k group boundaries are multiples of 32 / 8 only).
-  const bool su16 = p.lda % 64 == 0 && !vary_k;
-  if (fmt == 1) {
-    if (su16) launch_grouped_t<1, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
-    else launch_grouped_t<1, BT, false>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
-  } else if (fmt == 2) {
-    if (su16) launch_grouped_t<2, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
-    else launch_grouped_t<2, BT, false>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
-  } else {
-    if (su16) launch_grouped_t<0, BT, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
-    else launch_grouped_t<0, BT, false>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
-  }
+  const int sm = scale_mode(fmt == 1 ? 1 : fmt == 2 ? 2 : 0, p.lda, vary_k != 0);
+  auto go = [&](auto LDC, auto SMC) {
+    launch_grouped_t<decltype(LDC)::value, BT, decltype(SMC)::value>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+  };
+  auto by_sm = [&](auto LDC) {
+    if constexpr (decltype(LDC)::value != 0) {
+      if (sm == 2) { go(LDC, ic<2>{}); return; }
+    }
+    if (sm == 2) go(LDC, ic<1>{});
+    else if (sm == 1) go(LDC, ic<1>{});
+    else go(LDC, ic<0>{});
+  };
+  if (fmt == 1) by_sm(ic<1>{});
+  else if (fmt == 2) by_sm(ic<2>{});
+  else by_sm(ic<0>{});
   return hipGetLastError();
 }
 

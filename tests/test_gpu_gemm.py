@@ -138,11 +138,12 @@ def test_bf16_gemm_dense(mnk):
     assert_gemm_close(host(c), ref, f"bf16 {mnk}")
 
 
-@pytest.mark.parametrize("K", [512, 544])
+@pytest.mark.parametrize("K", [512, 544, 576])
 @pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4", "bf16"])
 def test_dense_256_tiles_ragged(fmt, K):
-    """M, N large enough for the 256 x 256 tile kernel, ragged in M and N; K = 544
-    leaves a half K stage (per-lane tail handling and 1-block scale loads)."""
+    """M, N large enough for the 256 x 256 tile kernel, ragged in M and N. K = 512:
+    16-byte scale chunks; K = 576: per-stage scale loads; K = 544: a half K stage
+    (per-lane tail handling and 1-block scale loads)."""
     M, N = 4196, 3112
     g = inputs.rng(86, K + len(fmt))
     a = inputs.to_bf16_bits(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))

@@ -7,16 +7,20 @@
 // GEMM needs its blocks along its own reduction dimension (same page, section
 // "Un Cuantizador Compartido Es el Mecanismo Real"; aib.vote, MXFP8 paragraph).
 //
-// Work decomposition (one wave = 32 rows x 128 columns of BF16 = 8 KiB):
-//   lane = 16*m + c16 holds rows 8m .. 8m+7 and columns 8*c16 .. 8*c16+7 of
-//   its wave's slab as eight 16-byte loads (each load instruction of the wave
-//   reads 4 full 256-byte row segments: fully coalesced).
+// Work decomposition: a workgroup (4 waves) owns a 128 x 128 BF16 tile; wave w
+// owns rows 32w .. 32w+31 of it. Lane = 16*m + c16 holds rows 8m .. 8m+7 and
+// columns 8*c16 .. 8*c16+7 of its wave's 32 x 128 slab as eight 16-byte loads
+// (each load instruction of the wave reads 4 full 256-byte row segments).
 //   * rowwise block (1 row x 32 cols) = 4 consecutive lanes: amax via two DPP
-//     quad exchanges; each lane converts and stores its 8 bytes.
+//     quad exchanges; each lane converts and stores its 8 bytes (16 lanes write
+//     one 128-byte row segment).
 //   * columnwise block (32 rows x 1 col) = the 4 lanes c16, c16+16, c16+32,
-//     c16+48: amax via two lane-xor exchanges; each lane converts its 8 rows
-//     of a column into 8 consecutive bytes of the transposed copy.
-//   No LDS is needed: the register tile of a lane already covers 8 rows.
+//     c16+48: amax via two lane-xor exchanges; each lane converts its 8 rows of
+//     a column into 8 bytes of the transposed copy, which go to LDS first: the
+//     workgroup then writes every column of its tile as one 128-byte segment
+//     (16 bytes per lane) instead of four scattered 32-byte pieces.
+//   * scales: the 4 row scales of a row and the 4 column scales of a column
+//     in the tile are gathered in LDS and leave as one dword each.
 // The BF16 values are converted straight from their packed form with the
 // gfx950 scaled converts (1 instruction per 2 values).
 #include "common.h"
@@ -28,27 +32,31 @@ __global__ void __launch_bounds__(256)
 quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
                    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                    uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT,
-                   int64_t col_tiles) {
+                   int64_t col_tiles, int row_scale_dw, int col_scale_dw) {
+  // Transposed FP8 tile: column cl at cl * 128; its 8-byte granule g (rows 8g .. 8g+7)
+  // sits at granule g ^ 4 * (cl / 8 % 4), which spreads one wave's writes over more banks.
+  __shared__ __attribute__((aligned(16))) uint8_t lcol[DO_COL ? 128 * 128 : 16];
+  __shared__ uint32_t lsrow[DO_ROW ? 128 : 1];     // 4 row-scale bytes per tile row
+  __shared__ uint32_t lscol[DO_COL ? 128 : 1];     // 4 column-scale bytes per tile column
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int w = threadIdx.x >> 6;
   const int m = lane >> 4;          // row group of 8 inside the wave slab
   const int c16 = lane & 15;        // column group of 8 inside the 128 columns
-  const int64_t slab = (int64_t)blockIdx.x / col_tiles * 4 + wave;   // 32-row slab index
+  const int64_t band = (int64_t)blockIdx.x / col_tiles;
   const int64_t ct = (int64_t)blockIdx.x % col_tiles;
-  const int64_t r0 = slab * 32 + 8 * m;
-  const int64_t c = ct * 128 + 8 * c16;
-  if (slab * 32 >= rows) return;                 // whole wave out of range (uniform)
-  const bool col_ok = c < cols;                  // cols % 32 == 0: 4-lane groups agree
+  const int64_t R0 = band * 128, C0 = ct * 128;
+  const int rl0 = 32 * w + 8 * m;   // tile row of v[0]
+  const int64_t c = C0 + 8 * c16;
+  const bool col_ok = c < cols;     // cols % 32 == 0: 4-lane groups agree
 
   uint4 v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bool ok = col_ok && (r0 + j < rows);
-    v[j] = ok ? *reinterpret_cast<const uint4*>(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
+    const int64_t r = R0 + rl0 + j;
+    v[j] = (col_ok && r < rows) ? *reinterpret_cast<const uint4*>(x + r * ld_x + c) : make_uint4(0, 0, 0, 0);
   }
 
   if (DO_ROW) {
-    const int64_t sblocks = cols / 32;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t a = pk_max_u16(pk_max_u16(v[j].x & 0x7FFF7FFFu, v[j].y & 0x7FFF7FFFu),
@@ -64,11 +72,9 @@ quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, i
       lo = cvt_fp8x2_bf16(lo, v[j].y, sc, true);
       uint32_t hi = cvt_fp8x2_bf16(0u, v[j].z, sc, false);
       hi = cvt_fp8x2_bf16(hi, v[j].w, sc, true);
-      const int64_t r = r0 + j;
-      if (col_ok && r < rows) {
-        *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(lo, hi);
-        if ((c16 & 3) == 0) s_row[r * sblocks + c / 32] = (uint8_t)s;
-      }
+      const int64_t r = R0 + rl0 + j;
+      if (col_ok && r < rows) *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(lo, hi);
+      if ((c16 & 3) == 0) reinterpret_cast<uint8_t*>(lsrow)[(rl0 + j) * 4 + (c16 >> 2)] = (uint8_t)s;
     }
   }
 
@@ -80,36 +86,70 @@ quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, i
       uint32_t a = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t w = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
-        a = pk_max_u16(a, w & 0x7FFF7FFFu);
+        const uint32_t wd = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
+        a = pk_max_u16(a, wd & 0x7FFF7FFFu);
       }
       a = pk_max_u16(a, shfl_xor_u32(a, 16));
       a = pk_max_u16(a, shfl_xor_u32(a, 32));
       cm[p] = a;
     }
-    const int64_t sblocks = rows / 32;
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       const uint32_t amax = (cc & 1) ? (cm[cc >> 1] >> 16) : (cm[cc >> 1] & 0xFFFFu);
       const uint32_t s = e8m0_from_bf16_amax(amax);
       const float sc = e8m0_to_float(s);
       const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t w[8];
+      uint32_t wd[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t p = cc >> 1;
-        w[j] = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
+        wd[j] = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
       }
       // pair (row j, row j+1) of column cc -> one packed BF16x2 dword
-      uint32_t out0 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(w[1], w[0], sel), sc, false);
-      out0 = cvt_fp8x2_bf16(out0, __builtin_amdgcn_perm(w[3], w[2], sel), sc, true);
-      uint32_t out1 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(w[5], w[4], sel), sc, false);
-      out1 = cvt_fp8x2_bf16(out1, __builtin_amdgcn_perm(w[7], w[6], sel), sc, true);
-      if (col_ok) {
-        const int64_t col = c + cc;
-        *reinterpret_cast<uint2*>(q_colT + col * rows + r0) = make_uint2(out0, out1);
-        if (m == 0) s_colT[col * sblocks + slab] = (uint8_t)s;
+      uint32_t out0 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(wd[1], wd[0], sel), sc, false);
+      out0 = cvt_fp8x2_bf16(out0, __builtin_amdgcn_perm(wd[3], wd[2], sel), sc, true);
+      uint32_t out1 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(wd[5], wd[4], sel), sc, false);
+      out1 = cvt_fp8x2_bf16(out1, __builtin_amdgcn_perm(wd[7], wd[6], sel), sc, true);
+      const int cl = 8 * c16 + cc;
+      const int g = (4 * w + m) ^ ((c16 & 3) * 4);
+      *reinterpret_cast<uint2*>(lcol + cl * 128 + g * 8) = make_uint2(out0, out1);
+      if (m == 0) reinterpret_cast<uint8_t*>(lscol)[cl * 4 + w] = (uint8_t)s;
+    }
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  if (DO_COL) {
+    // 16-byte chunk i = k * 256 + t of the tile's transposed copy: column i / 8, rows 16 (i % 8) ..
+    // rows % 32 == 0, so a chunk is either wholly inside the tensor or wholly outside.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = k * 256 + t;
+      const int cl = i >> 3, ch = i & 7;
+      const int g0 = (2 * ch) ^ (((cl >> 3) & 3) * 4);   // granules 2ch, 2ch+1 stay adjacent
+      const int64_t col = C0 + cl, r = R0 + 16 * ch;
+      if (col < cols && r < rows)
+        *reinterpret_cast<uint4*>(q_colT + col * rows + r) = *reinterpret_cast<const uint4*>(lcol + cl * 128 + g0 * 8);
+    }
+    if (t < 128 && C0 + t < cols) {
+      const int64_t sb = rows / 32;
+      uint8_t* dst = s_colT + (C0 + t) * sb + band * 4;
+      const int64_t ns = min((int64_t)4, sb - band * 4);
+      if (col_scale_dw && ns == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = lscol[t];
+      } else {
+        for (int b = 0; b < ns; ++b) dst[b] = (uint8_t)(lscol[t] >> (8 * b));
       }
+    }
+  }
+  if (DO_ROW && t < 128 && R0 + t < rows) {
+    const int64_t sb = cols / 32;
+    uint8_t* dst = s_row + (R0 + t) * sb + ct * 4;
+    const int64_t nb = min((int64_t)4, sb - ct * 4);
+    if (row_scale_dw && nb == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = lsrow[t];
+    } else {
+      for (int b = 0; b < nb; ++b) dst[b] = (uint8_t)(lsrow[t] >> (8 * b));
     }
   }
 }
@@ -118,17 +158,19 @@ hipError_t launch_quant_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t
                               void* q_row, void* s_row, void* q_colT, void* s_colT,
                               hipStream_t stream) {
   const int64_t col_tiles = (cols + 127) / 128;
-  const int64_t slabs = (rows + 31) / 32;
-  const int64_t blocks = (slabs + 3) / 4 * col_tiles;
+  const int64_t blocks = (rows + 127) / 128 * col_tiles;
   dim3 grid((unsigned)blocks), block(256);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t *qr = (uint8_t*)q_row, *sr = (uint8_t*)s_row, *qc = (uint8_t*)q_colT, *sc = (uint8_t*)s_colT;
+  // dword scale stores need 4-byte aligned scale rows
+  const int row_dw = sr && ((uintptr_t)sr & 3) == 0 && (cols / 32) % 4 == 0;
+  const int col_dw = sc && ((uintptr_t)sc & 3) == 0 && (rows / 32) % 4 == 0;
   if (q_row && q_colT)
-    hipLaunchKernelGGL((quant_mxfp8_kernel<true, true>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles);
+    hipLaunchKernelGGL((quant_mxfp8_kernel<true, true>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles, row_dw, col_dw);
   else if (q_row)
-    hipLaunchKernelGGL((quant_mxfp8_kernel<true, false>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles);
+    hipLaunchKernelGGL((quant_mxfp8_kernel<true, false>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles, row_dw, col_dw);
   else
-    hipLaunchKernelGGL((quant_mxfp8_kernel<false, true>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles);
+    hipLaunchKernelGGL((quant_mxfp8_kernel<false, true>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles, row_dw, col_dw);
   return hipGetLastError();
 }
 

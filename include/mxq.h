@@ -170,6 +170,30 @@ mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float*
                       void* out, mxq_out_dtype out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dequantize_transposed -- dequantize to BF16 and transpose per group, with an
+ * optional row gather: the K-contiguous BF16 operands that the dequantized-
+ * backward GEMMs consume (dgrad reads each expert weight transposed, wgrad reads
+ * gradients and activations with the slots along K).
+ *   Defined by: the dequantized-backward mode ("Miles Blackwell RL", remio.ai,
+ *   section "La Compatibilidad ..."; aib.vote, backward-modes paragraph); the value
+ *   of every element is that of dequantize(..., MXQ_OUT_BF16) above.
+ *
+ *   out[(g * cols + c) * ld_out + j] = BF16 of input element (g * group_rows + src(j), c)
+ *   for g < groups, c < cols, j < out_cols, where src(j) = src_row[j] (DEVICE int32,
+ *   out_cols entries; an index outside [0, group_rows) gives a zero element) or j
+ *   when src_row is NULL (then out_cols <= group_rows).
+ *   fmt  : MXQ_MXFP8, MXQ_NVFP4 (t per t_scope; GROUP uses group_rows) or MXQ_BF16
+ *          (q is BF16 data, s and t unused: a plain transpose).
+ *   Input rows are (groups * group_rows, cols) in the layouts of dequantize().
+ *   Requires cols % 32 (MXFP8) / % 16 (others) == 0, out_cols % 8 == 0,
+ *   ld_out >= out_cols with ld_out % 8 == 0, groups <= 65535.
+ * ------------------------------------------------------------------------- */
+mxq_status dequantize_transposed(mxq_format fmt, const void* q, const void* s, const float* t,
+                                 mxq_scope t_scope, int64_t groups, int64_t group_rows, int64_t cols,
+                                 const int32_t* src_row, int64_t out_cols, void* out_bf16,
+                                 int64_t ld_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * gemm_block_scaled -- C = (A_hat) (B_hat)^T with FP32 output, both operands
  * K-contiguous ("TN"), scaling blocks along K.
  *   Defined by: microscaling blocks must follow the reduction dimension of the

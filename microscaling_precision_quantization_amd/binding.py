@@ -33,6 +33,8 @@ _SIGS = {
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
     "dequantize": [_int, _c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _i64, _c_void_p, _int, _c_void_p],
+    "dequantize_transposed": [_int, _c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _i64, _c_void_p, _i64,
+                              _c_void_p, _i64, _c_void_p],
     "gemm_block_scaled": [_int, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p,
                           _c_void_p, _int, _c_void_p, _i64, _c_void_p],
     "gemm_mxfp8_matrix_core": [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
@@ -171,6 +173,25 @@ def dequantize(fmt: int, q: torch.Tensor, s: torch.Tensor, t: torch.Tensor | Non
     od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
     _check("dequantize", lib().dequantize(fmt, _ptr(q), _ptr(s), _ptr(t), SCOPE[t_scope], group_rows, rows, cols,
                                           _ptr(out), od, _stream(q.device)))
+    return out
+
+
+def dequantize_transposed(fmt: int, q: torch.Tensor, s=None, t=None, t_scope: str = "row", groups: int = 1,
+                          group_rows: int | None = None, cols: int | None = None, src_row=None,
+                          out_cols: int | None = None, out=None):
+    """BF16 (groups, cols, out_cols): out[g, c, j] = dequantized input (g * group_rows + src(j), c)."""
+    rows = q.shape[0]
+    if cols is None:
+        cols = q.shape[1] * (2 if fmt == NVFP4 else 1)
+    if group_rows is None:
+        group_rows = rows // max(groups, 1)
+    if out_cols is None:
+        out_cols = src_row.numel() if src_row is not None else group_rows
+    if out is None:
+        out = torch.empty((groups, cols, out_cols), dtype=torch.bfloat16, device=q.device)
+    _check("dequantize_transposed", lib().dequantize_transposed(
+        fmt, _ptr(q), _ptr(s), _ptr(t), SCOPE[t_scope], groups, group_rows, cols, _ptr(src_row), out_cols,
+        _ptr(out), out.stride(-2), _stream(q.device)))
     return out
 
 

@@ -14,6 +14,8 @@ hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64
                               float*, uint32_t*, int64_t, hipStream_t);
 hipError_t launch_dequant(int, const void*, const void*, const float*, int, int64_t, int64_t, int64_t, void*, int,
                           hipStream_t);
+hipError_t launch_dequant_t(int, const void*, const void*, const float*, int, int64_t, int64_t, int64_t,
+                            const int32_t*, int64_t, void*, int64_t, hipStream_t);
 hipError_t launch_swiglu_nvfp4(const float*, int64_t, int64_t, void*, void*, void*, float*, hipStream_t);
 hipError_t launch_combine(const float*, int64_t, int64_t, int64_t, int64_t, const int64_t*, const float*, float*,
                           hipStream_t);
@@ -167,6 +169,29 @@ mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float*
   if (rows == 0 || cols == 0) return MXQ_OK;
   return hip_status(mxq::launch_dequant(fmt == MXQ_NVFP4, q, s, t, tm, group_rows, rows, cols, out,
                                         out_dtype == MXQ_OUT_F32, S(stream)));
+}
+
+mxq_status dequantize_transposed(mxq_format fmt, const void* q, const void* s, const float* t, mxq_scope t_scope,
+                                 int64_t groups, int64_t group_rows, int64_t cols, const int32_t* src_row,
+                                 int64_t out_cols, void* out_bf16, int64_t ld_out, void* stream) {
+  if (groups < 0 || group_rows < 0 || cols < 0 || out_cols < 0) return MXQ_ERR_SHAPE;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16) return MXQ_ERR_FORMAT;
+  if (!q || !out_bf16 || (fmt != MXQ_BF16 && !s) || (fmt == MXQ_NVFP4 && !t)) return MXQ_ERR_NULL;
+  int tm = 0;
+  if (fmt == MXQ_NVFP4) {
+    if (t_scope == MXQ_SCOPE_ROW) tm = 0;
+    else if (t_scope == MXQ_SCOPE_TENSOR) tm = 1;
+    else if (t_scope == MXQ_SCOPE_GROUP) tm = 2;
+    else return MXQ_ERR_FORMAT;
+  }
+  if (cols % (fmt == MXQ_MXFP8 ? 32 : 16)) return MXQ_ERR_SHAPE;
+  if (!src_row && out_cols > group_rows) return MXQ_ERR_SHAPE;
+  if (out_cols % 8 || ld_out < out_cols || ld_out % 8) return MXQ_ERR_SHAPE;
+  if (groups > 65535 || (cols + 63) / 64 > 65535 || (out_cols + 63) / 64 > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  if (!al16(q) || !al16(out_bf16)) return MXQ_ERR_ALIGN;
+  if (groups == 0 || group_rows == 0 || cols == 0 || out_cols == 0) return MXQ_OK;
+  return hip_status(mxq::launch_dequant_t((int)fmt, q, s, t, tm, groups, group_rows, cols, src_row, out_cols,
+                                          out_bf16, ld_out, S(stream)));
 }
 
 static int scope_mode(mxq_scope sc) {

@@ -69,6 +69,89 @@ hipError_t launch_dequant(int nv, const void* q, const void* s, const float* t, 
 }
 
 // ---------------------------------------------------------------------------
+// Dequantize + transpose (+ row gather): the BF16 operands of the backward GEMMs
+// in the K-contiguous layout the "TN" GEMMs consume.
+//   out[g][c][j] = BF16(deq(in[g * group_rows + src(j)][c])),  src(j) = src_row[j]
+//   (a gather; -1 gives a zero column) or j. Tile: 64 output columns (j) x 64
+//   input columns (c) per workgroup; each thread dequantizes 16 consecutive
+//   elements of one input row, the tile is transposed through LDS and leaves as
+//   16-byte row segments of the output.
+// FMT: 1 MXFP8, 2 NVFP4, 3 BF16 (plain transpose).
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ void __launch_bounds__(256)
+dequant_t_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, const float* __restrict__ t,
+                 int t_mode, int64_t group_rows, int64_t cols, const int32_t* __restrict__ src_row,
+                 int64_t out_cols, uint16_t* __restrict__ out, int64_t ld_out) {
+  constexpr int P = 72;                                   // LDS row pitch (BF16), 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  {
+    const int jl = tid >> 2, cl = (tid & 3) * 16;
+    const int64_t j = j0 + jl, c = c0 + cl;
+    int64_t r = -1;
+    if (j < out_cols && c < cols) {
+      const int64_t sr = src_row ? (int64_t)src_row[j] : j;
+      if (sr >= 0 && sr < group_rows) r = g * group_rows + sr;
+    }
+    uint32_t p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (r >= 0) {
+      if (FMT == 3) {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + r * cols + c);
+        const uint4 a = src[0], b = src[1];
+        p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+      } else {
+        float v[16];
+        if (FMT == 1) {
+          const uint4 b = *reinterpret_cast<const uint4*>(q + r * cols + c);
+          const float sc = e8m0_to_float(s[r * (cols / 32) + c / 32]);
+          const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFF) * sc;
+        } else {
+          const uint2 b = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c / 2);
+          const float S = e4m3_to_f32(s[r * (cols / 16) + c / 16]);
+          const float tt = t_mode == 0 ? t[r] : t_mode == 1 ? t[0] : t[r / group_rows];
+          const uint32_t w[2] = {b.x, b.y};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = (e2m1_to_f32((w[i / 8] >> (4 * (i % 8))) & 0xF) * S) * tt;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = f32_to_bf16_rne(v[2 * i]) | (f32_to_bf16_rne(v[2 * i + 1]) << 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tile[(cl + 2 * i) * P + jl] = (uint16_t)(p[i] & 0xFFFFu);
+      tile[(cl + 2 * i + 1) * P + jl] = (uint16_t)(p[i] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = k * 256 + tid;
+    const int cl = i >> 3, jc = (i & 7) * 8;
+    const int64_t c = c0 + cl, j = j0 + jc;
+    if (c < cols && j < out_cols)
+      *reinterpret_cast<uint4*>(out + (g * cols + c) * ld_out + j) = *reinterpret_cast<const uint4*>(tile + cl * P + jc);
+  }
+}
+
+hipError_t launch_dequant_t(int fmt, const void* q, const void* s, const float* t, int t_mode, int64_t groups,
+                            int64_t group_rows, int64_t cols, const int32_t* src_row, int64_t out_cols, void* out,
+                            int64_t ld_out, hipStream_t st) {
+  dim3 grid((unsigned)((out_cols + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)groups), block(256);
+  const uint8_t *qp = (const uint8_t*)q, *sp = (const uint8_t*)s;
+  uint16_t* o = (uint16_t*)out;
+  if (fmt == 1) hipLaunchKernelGGL((dequant_t_kernel<1>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, cols, src_row, out_cols, o, ld_out);
+  else if (fmt == 2) hipLaunchKernelGGL((dequant_t_kernel<2>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, cols, src_row, out_cols, o, ld_out);
+  else hipLaunchKernelGGL((dequant_t_kernel<3>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, cols, src_row, out_cols, o, ld_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // SwiGLU + per-row NVFP4: one wave per slot row; the row stays in registers.
 // h = silu(g) * u = g / (1 + exp(-g)) * u in binary32, rounded to BF16, then the
 // per-token quantizer's arithmetic on the BF16 row.

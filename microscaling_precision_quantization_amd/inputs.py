@@ -91,7 +91,10 @@ class Routing:
     slot_of: np.ndarray       # (T, k) int64 slot holding token t's j-th choice
 
 
-def route_topk(logits: np.ndarray, k: int) -> Routing:
+def route_topk(logits: np.ndarray, k: int, pad: int = 1) -> Routing:
+    """Top-k routing of FP32 logits (T, G). With pad > 1 every expert's slot range
+    starts at a multiple of `pad` (its length rounded up); padding slots carry
+    row_index -1 and are never named by slot_of."""
     logits = np.asarray(logits, dtype=np.float32)
     T, G = logits.shape
     # stable sort on -logit: ties keep the lower expert index first
@@ -105,15 +108,21 @@ def route_topk(logits: np.ndarray, k: int) -> Routing:
     w = pk.astype(np.float32)
     # order is by descending logit == descending weight
     counts = np.bincount(order.reshape(-1), minlength=G)
+    padded = (counts + pad - 1) // pad * pad
     offsets = np.zeros(G + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(counts)
+    offsets[1:] = np.cumsum(padded)
     flat_e = order.reshape(-1)
     flat_t = np.repeat(np.arange(T), k)
     flat_j = np.tile(np.arange(k), T)
     perm = np.lexsort((flat_t, flat_e))          # expert-major, token ascending
-    row_index = flat_t[perm].astype(np.int32)
+    e_sorted = flat_e[perm]
+    first = np.zeros(G + 1, dtype=np.int64)
+    first[1:] = np.cumsum(counts)
+    slot = offsets[e_sorted] + (np.arange(T * k) - first[e_sorted])
+    row_index = np.full(int(offsets[-1]), -1, dtype=np.int32)
+    row_index[slot] = flat_t[perm]
     slot_of = np.empty((T, k), dtype=np.int64)
-    slot_of[flat_t[perm], flat_j[perm]] = np.arange(T * k)
+    slot_of[flat_t[perm], flat_j[perm]] = slot
     return Routing(order.astype(np.int32), w, offsets, row_index, slot_of)
 
 
@@ -132,6 +141,51 @@ def workload_moe_qwen3(tokens=4096, hidden=2048, experts=128, inter=768, topk=8,
     if with_weights:
         out["w_gu"] = normal_bf16(rng(3, 3), (experts, 2 * inter, hidden), 0.02)
         out["w_d"] = normal_bf16(rng(3, 4), (experts, hidden, inter), 0.02)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Workload 4: DeepSeek-V3-shaped MoE layer (routed NVFP4 experts + BF16 shared expert)
+# --------------------------------------------------------------------------
+
+def workload_moe_deepseek(tokens=16384, hidden=7168, experts=256, inter=2048, topk=8, pad=32):
+    """Activations and routing on the host (numpy, as above). The expert weights and
+    the synthetic upstream gradients are ~11 G and ~1.6 G values: they are drawn on
+    the device by `deepseek_device_tensors`."""
+    x = normal_bf16(rng(4, 0), (tokens, hidden), 1.0)
+    logits = rng(4, 1).standard_normal((tokens, experts)).astype(np.float32)
+    return {"x": x, "logits": logits, "routing": route_topk(logits, topk, pad=pad), "hidden": hidden,
+            "experts": experts, "inter": inter, "topk": topk}
+
+
+def device_normal_bf16(torch, dev, shape, std, seed):
+    """N(0, std) drawn in FP32 by torch's seeded device generator (Philox), rounded
+    to BF16 (RNE). Used where a host draw of the tensor would take minutes."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def deepseek_device_tensors(torch, dev, w, shared=True, grads=True):
+    """Routed expert weights W_gu (G*2I, H) (gate rows then up rows per expert) and
+    W_d (G*H, I), ~N(0, 0.02); the shared expert's W_sgu (2I, H) and W_sd (H, I);
+    synthetic upstream gradients ~N(0, 1e-3) of the routed down / gate_up outputs
+    (padding slots zero) and of the shared expert's outputs. Seeds 4000 + tensor id."""
+    H, G, I = w["hidden"], w["experts"], w["inter"]
+    S = int(w["routing"].offsets[-1])
+    T = w["x"].shape[0]
+    out = {"w_gu": device_normal_bf16(torch, dev, (G * 2 * I, H), 0.02, 4002),
+           "w_d": device_normal_bf16(torch, dev, (G * H, I), 0.02, 4003)}
+    if shared:
+        out["w_sgu"] = device_normal_bf16(torch, dev, (2 * I, H), 0.02, 4004)
+        out["w_sd"] = device_normal_bf16(torch, dev, (H, I), 0.02, 4005)
+    if grads:
+        live = torch.from_numpy(w["routing"].row_index >= 0).to(dev)[:, None]
+        out["d_o"] = device_normal_bf16(torch, dev, (S, H), 1e-3, 4006) * live
+        out["d_gu"] = device_normal_bf16(torch, dev, (S, 2 * I), 1e-3, 4007) * live
+        if shared:
+            out["d_os"] = device_normal_bf16(torch, dev, (T, H), 1e-3, 4008)
+            out["d_gus"] = device_normal_bf16(torch, dev, (T, 2 * I), 1e-3, 4009)
     return out
 
 

@@ -87,6 +87,16 @@ def test_dequant_and_moe_validation():
     assert L.dequantize(2, P, P, None, 0, 0, 4, 32, P, 0, None) == 1      # NVFP4 without t
     assert L.dequantize(1, P, P, None, 0, 0, 4, 48, P, 0, None) == 2
     assert L.dequantize(3, P, P, None, 0, 0, 4, 32, P, 0, None) == 4
+    dt = L.dequantize_transposed
+    assert dt(2, P, P, None, 0, 1, 64, 32, None, 64, P, 64, None) == 1       # NVFP4 without t
+    assert dt(1, P, P, None, 0, 1, 64, 48, None, 64, P, 64, None) == 2       # cols % 32 (MXFP8)
+    assert dt(3, P, None, None, 0, 1, 64, 32, None, 12, P, 16, None) == 2    # out_cols % 8
+    assert dt(3, P, None, None, 0, 1, 64, 32, None, 72, P, 72, None) == 2    # no gather: out_cols > group_rows
+    assert dt(3, P, None, None, 0, 1, 64, 32, None, 64, P, 56, None) == 2    # ld_out < out_cols
+    assert dt(3, P, None, None, 0, 70000, 64, 32, None, 64, P, 64, None) == 2  # too many groups
+    assert dt(3, MIS, None, None, 0, 1, 64, 32, None, 64, P, 64, None) == 3
+    assert dt(2, P, P, P, 7, 1, 64, 32, None, 64, P, 64, None) == 4          # bad scope
+    assert dt(3, P, None, None, 0, 0, 64, 32, None, 64, P, 64, None) == 0    # empty
     assert L.moe_swiglu_quantize_nvfp4(P, 4, 24, None, P, P, P, None) == 2
     assert L.moe_combine(P, 8, 4, 2, 6, P, P, P, None) == 2
     assert L.moe_combine(P, 8, 0, 2, 8, P, P, P, None) == 0

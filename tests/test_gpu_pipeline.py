@@ -174,3 +174,146 @@ def test_shared_expert_bf16_forward_backward():
     assert_gemm_close(host(sh.dw_sd), f64(d_o).T @ f64(h), "shared down wgrad")
     assert_gemm_close(host(sh.dx), f64(d_gu) @ f64(w_sgu), "shared gate_up dgrad")
     assert_gemm_close(host(sh.dw_sgu), f64(d_gu).T @ f64(x), "shared gate_up wgrad")
+
+
+# ------------------------- full-size workloads (sampled) -------------------------
+
+def check_moe_sampled(m, r, x_bits, w_gu_bits_of, w_d_bits_of, experts, tokens, what):
+    """Stage-wise parity of a full-size MoE forward on sampled experts and tokens.
+    w_*_bits_of(e) returns expert e's BF16 weight bits."""
+    T, H, G, I = m.T, m.H, m.G, m.I
+    live = r.row_index >= 0
+    eq, es, et = onv.quantize_per_token(x_bits)
+    assert_bytes_equal(host(m.qx), eq, f"{what} tokens packed")
+    assert_bytes_equal(host(m.sx), es, f"{what} tokens scales")
+    assert_bytes_equal(host(m.tx).view(np.uint32), et.view(np.uint32), f"{what} token scales")
+    xh = onv.dequantize_exact(eq, es, et)
+    qg, sg, tg = m.wq["gu"]
+    qd, sd, td = m.wq["d"]
+    tg, td = host(tg), host(td)
+    for e in experts:
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        # A4 for this expert
+        gq, gs, gt = onv.quantize_per_group(w_gu_bits_of(e), [0, 2 * I])
+        assert_bytes_equal(host(qg[e * 2 * I:(e + 1) * 2 * I]), gq, f"{what} w_gu[{e}] packed")
+        assert_bytes_equal(host(sg[e * 2 * I:(e + 1) * 2 * I]), gs, f"{what} w_gu[{e}] scales")
+        assert tg.view(np.uint32)[e] == gt.view(np.uint32)[0]
+        dq, ds, dt = onv.quantize_per_group(w_d_bits_of(e), [0, H])
+        assert_bytes_equal(host(qd[e * H:(e + 1) * H]), dq, f"{what} w_d[{e}] packed")
+        assert td.view(np.uint32)[e] == dt.view(np.uint32)[0]
+        if hi == lo:
+            continue
+        rows = r.row_index[lo:hi]
+        a = np.zeros((hi - lo, H))
+        a[rows >= 0] = xh[rows[rows >= 0]]
+        gu = host(m.gu[lo:hi])
+        assert_gemm_close(gu, a @ onv.dequantize_exact(gq, gs, np.repeat(gt, 2 * I)).T, f"{what} gate_up[{e}]")
+        if m.h is not None:
+            assert np.max(omoe.bf16_ulp_distance(host(m.h[lo:hi]), omoe.swiglu_bf16_ref(gu))) <= 1
+        hq, hs, ht = host(m.qh[lo:hi]), host(m.sh[lo:hi]), host(m.th[lo:hi])
+        o = host(m.o[lo:hi])
+        assert_gemm_close(o, onv.dequantize_exact(hq, hs, ht) @ onv.dequantize_exact(dq, ds, np.repeat(dt, H)).T,
+                          f"{what} down[{e}]")
+    # combine on sampled tokens, from the device's slot outputs
+    so = r.slot_of[tokens]
+    o_rows = host(m.o[torch.from_numpy(so.reshape(-1)).cuda()]).reshape(len(tokens), so.shape[1], H)
+    ref = np.einsum("tj,tjh->th", r.topk_w[tokens].astype(np.float64), o_rows.astype(np.float64))
+    assert_gemm_close(host(m.y[torch.from_numpy(tokens).cuda()]), ref, f"{what} combine (sampled tokens)")
+    assert not np.any(live[r.slot_of.reshape(-1)] == 0)
+
+
+def test_moe_qwen3_full_size_sampled():
+    w = inputs.workload_moe_qwen3()
+    T, H, G, I = w["x"].shape[0], w["hidden"], w["experts"], w["inter"]
+    d = torch.device("cuda")
+    rd = pipeline.MoeRoutingDevice(w["routing"], d)
+    m = pipeline.MoeNvfp4(T, H, G, I, rd, d, keep_h=True)
+    m.quantize_weights(dev_bf16(w["w_gu"].reshape(G * 2 * I, H)), dev_bf16(w["w_d"].reshape(G * H, I)))
+    m.forward(dev_bf16(w["x"]))
+    torch.cuda.synchronize()
+    experts = [0, 37, 64, 127]
+    tokens = np.sort(np.random.default_rng(7).choice(T, 64, replace=False))
+    check_moe_sampled(m, w["routing"], w["x"], lambda e: w["w_gu"][e], lambda e: w["w_d"][e], experts, tokens,
+                      "qwen3")
+
+
+def test_moe_deepseek_full_size_sampled():
+    w = inputs.workload_moe_deepseek()
+    T, H, G, I = w["x"].shape[0], w["hidden"], w["experts"], w["inter"]
+    d = torch.device("cuda")
+    t = inputs.deepseek_device_tensors(torch, d, w)
+    r = w["routing"]
+    rd = pipeline.MoeRoutingDevice(r, d)
+    m = pipeline.MoeNvfp4(T, H, G, I, rd, d, keep_h=True)
+    m.quantize_weights(t["w_gu"], t["w_d"])
+    x = dev_bf16(w["x"])
+    m.forward(x)
+    b = pipeline.MoeDequantBackward(m)
+    b.dequantize_weights()
+    b.backward(t["d_o"], t["d_gu"])
+    sh = pipeline.SharedExpertBf16(T, H, I, d)
+    sh.forward(x, t["w_sgu"], t["w_sd"])
+    sh.backward(x, t["w_sgu"], t["w_sd"], t["d_os"], t["d_gus"])
+    torch.cuda.synchronize()
+    bits = lambda ten: host(ten)
+    experts = [3, 200]
+    tokens = np.sort(np.random.default_rng(8).choice(T, 32, replace=False))
+    check_moe_sampled(m, r, w["x"], lambda e: bits(t["w_gu"][e * 2 * I:(e + 1) * 2 * I]),
+                      lambda e: bits(t["w_d"][e * H:(e + 1) * H]), experts, tokens, "deepseek")
+    # dequantized backward on the sampled experts
+    f64 = lambda b16: F.bf16_bits_to_f32(b16).astype(np.float64)
+    qg, sg, tg = (host(a) for a in m.wq["gu"])
+    xq = onv.dequantize_bf16_bits(host(m.qx), host(m.sx), host(m.tx))
+    for e in experts:
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        wgu_b = onv.dequantize_bf16_bits(qg[e * 2 * I:(e + 1) * 2 * I], sg[e * 2 * I:(e + 1) * 2 * I],
+                                         np.repeat(tg[e:e + 1], 2 * I))
+        assert_bytes_equal(host(b.w_guT[e]), np.ascontiguousarray(wgu_b.T), f"W_gu^T[{e}]")
+        qd, sd, td = (host(a[e * H:(e + 1) * H]) if a.dim() == 2 else host(a) for a in m.wq["d"])
+        wd_b = onv.dequantize_bf16_bits(qd, sd, np.repeat(td[e:e + 1], H))
+        d_o, d_gu = host(t["d_o"][lo:hi]), host(t["d_gu"][lo:hi])
+        h_b = onv.dequantize_bf16_bits(host(m.qh[lo:hi]), host(m.sh[lo:hi]), host(m.th[lo:hi]))
+        rows = r.row_index[lo:hi]
+        xs = np.zeros((hi - lo, H), dtype=np.uint16)
+        xs[rows >= 0] = xq[rows[rows >= 0]]
+        assert_gemm_close(host(b.dh[lo:hi]), f64(d_o) @ f64(wd_b), f"down dgrad[{e}]")
+        assert_gemm_close(host(b.dw_d[e]), f64(d_o).T @ f64(h_b), f"down wgrad[{e}]")
+        assert_gemm_close(host(b.dx[lo:hi]), f64(d_gu) @ f64(wgu_b), f"gate_up dgrad[{e}]")
+        assert_gemm_close(host(b.dw_gu[e]), f64(d_gu).T @ f64(xs), f"gate_up wgrad[{e}]")
+    # shared expert on sampled token rows (its weight gradients in full)
+    xb, wsgu, wsd = w["x"], host(t["w_sgu"]), host(t["w_sd"])
+    gu = host(sh.gu[torch.from_numpy(tokens).cuda()])
+    assert_gemm_close(gu, f64(xb[tokens]) @ f64(wsgu).T, "shared gate_up (sampled rows)")
+    h = host(sh.h)
+    assert np.max(omoe.bf16_ulp_distance(h[tokens], omoe.swiglu_bf16_ref(gu))) <= 1
+    assert_gemm_close(host(sh.o[torch.from_numpy(tokens).cuda()]), f64(h[tokens]) @ f64(wsd).T, "shared down")
+    d_os, d_gus = host(t["d_os"]), host(t["d_gus"])
+    assert_gemm_close(host(sh.dw_sd), f64(d_os).T @ f64(h), "shared down wgrad")
+    assert_gemm_close(host(sh.dx[torch.from_numpy(tokens).cuda()]), f64(d_gus[tokens]) @ f64(wsgu),
+                      "shared gate_up dgrad (sampled rows)")
+
+
+def test_stress_nvfp4_rht_wgrad_full_size_sampled():
+    n = 8192
+    w = inputs.workload_stress(n)
+    st = pipeline.StressStep(n, w["signs"], torch.device("cuda"))
+    a, b = dev_bf16(w["a"]), dev_bf16(w["b"])
+    st.quantize_rht(a, b)
+    st.nvfp4_wgrad()
+    torch.cuda.synchronize()
+    qa, sa, ta = (host(v) for v in st.nv["a"])
+    qb, sb, tb = (host(v) for v in st.nv["b"])
+    rows = np.sort(np.random.default_rng(9).choice(n, 32, replace=False))
+    ah = onv.dequantize_exact(qa[rows], sa[rows], np.repeat(ta, len(rows)))
+    bh = onv.dequantize_exact(qb, sb, np.repeat(tb, n))
+    c = host(st.c["wgrad_nvfp4"][torch.from_numpy(rows).cuda()])
+    assert_gemm_close(c, ah @ bh.T, "8192^3 NVFP4 RHT wgrad (sampled rows)")
+    # RHT keeps the product: the FP64 product of the unquantized transformed operands
+    # equals A^T B up to FP32 rounding of the transform (orthogonality of H16 diag(s) / 4)
+    x = inputs.bf16_bits_to_float(w["a"])
+    y = inputs.bf16_bits_to_float(w["b"])
+    cols = rows[:8]
+    ua = onv.rht16_rows(np.ascontiguousarray(x[:, cols].T), w["signs"]).astype(np.float64)
+    ub = onv.rht16_rows(np.ascontiguousarray(y.T[:256]), w["signs"]).astype(np.float64)
+    direct = x[:, cols].T.astype(np.float64) @ y[:, :256].astype(np.float64)
+    assert np.linalg.norm(ua @ ub.T - direct) <= 1e-6 * np.linalg.norm(direct)

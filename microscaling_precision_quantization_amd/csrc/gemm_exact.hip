@@ -64,7 +64,8 @@ template <int LD, int SM> struct ScaleDma {
   static constexpr int SZ = LD == 1 ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
 };
 
-template <int LD, int BM, int BN, int SM>
+// OCC = workgroups meant to share one CU: the LDS budget of a workgroup is 1 / OCC of it.
+template <int LD, int BM, int BN, int SM, int OCC = 1>
 struct Cfg {
   static constexpr int RB = RowBytes<LD>::v;
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
@@ -74,7 +75,7 @@ struct Cfg {
   static constexpr int CH_HALF = CH ? (BM + BN) * 16 : 0;         // one chunk buffer
   static constexpr int S_BYTES = SU * (BM + BN) * 4;              // scale slots of one stage
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int FREE = kLdsBytes - 2 * CH_HALF;
+  static constexpr int FREE = kLdsBytes / OCC - 2 * CH_HALF;
   static constexpr int NS = (4 * STAGE <= FREE) ? 4 : (3 * STAGE <= FREE ? 3 : 2);
   static constexpr int IA = A_BYTES / 4096, IB = B_BYTES / 4096;  // 1 KiB wave instructions per wave
   static constexpr int IS = SU * (BM + BN) / 256;                 // 64-row scale loads per wave
@@ -259,10 +260,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the loads of the stage NS - 1 ahead are interleaved with the first sub-block's
 // MFMAs, and the barrier that publishes the next stage sits halfway through the
 // last sub-block.
-template <int LD, int BM, int BN, int SM>
+template <int LD, int BM, int BN, int SM, int OCC = 1>
 __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0,
                                                 uint8_t* lds1, uint8_t* lds2, uint8_t* lds3, uint8_t* ldsc) {
-  using C = gx::Cfg<LD, BM, BN, SM>;
+  using C = gx::Cfg<LD, BM, BN, SM, OCC>;
   constexpr bool AL = SM >= 1;                            // every K tile full and 64-aligned
   constexpr bool CH = C::CH;
   constexpr int XS = C::XS, SPC = C::SPC;
@@ -452,15 +453,16 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   const uint32_t wsB = (uint32_t)(C::A_BYTES + C::B_BYTES + (BM + wn * (BN / 2)) * 4);
   constexpr int SC_UNIT = (BM + BN) * 4;                  // bytes between scale units (SU == 2)
 
-  // scales of stage t in the chunk buffers: row r's byte (MXFP8 block b) or byte pair
-  // (NVFP4 blocks 2h, 2h+1) at chunk + 16 r + (t % SPC) * bytes per stage
-  const uint32_t xsc = (uint32_t)(lr * 16 + (LD == 2 ? 2 * h : 0));
+  // Chunked scales: the 16-byte chunk row of each fragment row (one per lane) is read into
+  // registers once per chunk (SPC stages), at its first stage, and the stage's bytes are
+  // taken from there: row r's byte (MXFP8 block b) or byte pair (NVFP4 blocks 2h, 2h+1)
+  // of stage t sits at chunk + 16 r + (t % SPC) * bytes per stage. (Byte-wise LDS reads of
+  // 16-byte-strided rows would each take several conflicting passes.)
   const uint32_t wcA = (uint32_t)(wm * (BM / 2) * 16), wcB = (uint32_t)((BM + wn * (BN / 2)) * 16);
-  auto chunk_base = [&](int t) -> uint32_t {
-    return lbase_c + (uint32_t)((t / SPC) & 1) * C::CH_HALF + (uint32_t)(t % SPC) * (LD == 1 ? 2 : 4);
-  };
-  auto read_sub = [&](int t, auto SLOT, auto SB, Frag& fr) {
-    constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value;
+  u32x4 chr[CH ? NF : 1];
+  // TP = t % SPC, known at compile time in the unrolled rounds (R is a multiple of SPC)
+  auto read_sub = [&](int t, auto SLOT, auto SB, auto TP, Frag& fr) {
+    constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value, tp = decltype(TP)::value;
     const lds_cptr pa = as_lds(lbase[S] + wA + xo[b]);
     const lds_cptr pb = as_lds(lbase[S] + wB + xo[b]);
 #pragma unroll
@@ -468,12 +470,20 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 #pragma unroll
     for (int j = 0; j < TJ; ++j) fr.raw[TI + j] = lds_ld16(pb + j * 32 * RB);
     if constexpr (CH) {
-      const uint32_t cb = chunk_base(t);
-      const lds_cptr sa = as_lds(cb + wcA + xsc), sb = as_lds(cb + wcB + xsc);
+      if constexpr (tp == 0 && b == 0) {
+        const uint32_t cb = lbase_c + (uint32_t)((t / SPC) & 1) * C::CH_HALF + (uint32_t)(lr * 16);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          chr[f] = lds_ld16(as_lds(cb + (f < TI ? wcA + f * 512 : wcB + (f - TI) * 512)));
+      }
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const lds_cptr q = (f < TI ? sa + f * 512 : sb + (f - TI) * 512) + (LD == 1 ? b : 0);
-        fr.sc[f] = LD == 1 ? (uint32_t)*q : (uint32_t)*(const __attribute__((address_space(3))) uint16_t*)q;
+        if constexpr (LD == 1) {
+          constexpr int idx = tp * 2 + b;
+          fr.sc[f] = (chr[f][idx / 4] >> (8 * (idx % 4))) & 0xFFu;
+        } else {
+          fr.sc[f] = (chr[f][tp] >> (16 * h)) & 0xFFFFu;
+        }
       }
     } else if constexpr (LD != 0) {
       const lds_cptr sa = as_lds(lbase[S] + wsA + xs), sb = as_lds(lbase[S] + wsB + xs);
@@ -591,7 +601,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       constexpr int b = decltype(SB)::value;
       constexpr int cur = (ri * SBS + b) & 1;
       if constexpr (b + 1 < SBS) {
-        read_sub(kt, ic<S>{}, ic<b + 1>{}, F[cur ^ 1]);
+        read_sub(kt, ic<S>{}, ic<b + 1>{}, ic<ri % SPC>{}, F[cur ^ 1]);
         __builtin_amdgcn_sched_barrier(0);              // keep the prefetch ahead of this sub-block's MFMAs
       }
       mma_sub(F[cur], [&](auto JJ) {
@@ -611,7 +621,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           wait_vmcnt<WAIT>();                           // tile kt + 1 has landed (this wave's loads)
           __builtin_amdgcn_s_barrier();                 // ... and every wave's; slot S fully read
           __builtin_amdgcn_sched_barrier(0);
-          read_sub(kt + 1, ic<SN>{}, ic<0>{}, F[cur ^ 1]);
+          read_sub(kt + 1, ic<SN>{}, ic<0>{}, ic<(ri + 1) % SPC>{}, F[cur ^ 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -624,7 +634,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   wait_vmcnt<(NS - 2) * OPS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_sub(0, ic<0>{}, ic<0>{}, F[0]);
+  read_sub(0, ic<0>{}, ic<0>{}, ic<0>{}, F[0]);
   __builtin_amdgcn_sched_barrier(0);
 
   // Whole rounds of R stages: stages past the end multiply zeros (their loads are
@@ -692,23 +702,39 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   exact_gemm_tile<LD, BM, BN, SM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
+// Group of a tile: the largest g with tile_prefix[g] <= tile (tile_prefix is non-decreasing
+// and tile < tile_prefix[groups]). Each wave narrows the range 64-fold per round with one
+// load per lane and a ballot (two rounds for up to 4096 groups).
+__device__ __forceinline__ int64_t find_group(const int64_t* __restrict__ prefix, int64_t groups, int64_t tile) {
+  const int lane = threadIdx.x & 63;
+  int64_t lo = 0, span = groups;                 // answer in [lo, lo + span)
+  while (span > 1) {
+    const int64_t step = (span + 63) / 64;
+    const int64_t g = lo + (int64_t)lane * step;
+    const bool ok = g < lo + span && prefix[g] <= tile;
+    const uint64_t m = __ballot(ok);              // lanes 0 .. last are set (lane 0 always)
+    const int last = 63 - __builtin_clzll(m);
+    const int64_t nlo = lo + (int64_t)last * step;
+    span = min(step, lo + span - nlo);
+    lo = nlo;
+  }
+  return lo;
+}
+
 // Grouped: tile_prefix[g] = first tile of group g.
 //   vary_k = 0: group g covers slots [off[g], off[g+1]), B_g = expert g of a stacked B;
 //   vary_k = 1: group g reduces over k in [off[g], off[g+1]) into C_g = C + g*M*N.
-template <int LD, int BM, int BN, int SM>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// OCC = 2 gives each workgroup half the LDS, so two share a CU and one's prologue and
+// epilogue overlap the other's main loop (expert tiles are short in K or in rows).
+template <int LD, int BM, int BN, int SM, int OCC>
+__global__ void __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, const int64_t* __restrict__ tile_prefix,
                      int64_t groups, int vary_k, int64_t M, int64_t N, int64_t tiles_n) {
-  using C = gx::Cfg<LD, BM, BN, SM>;
+  using C = gx::Cfg<LD, BM, BN, SM, OCC>;
   MXQ_EXACT_LDS(C)
   const int64_t tile = blockIdx.x;
   if (tile >= tile_prefix[groups]) return;
-  int64_t lo = 0, hi = groups - 1;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) / 2;
-    if (tile_prefix[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int64_t g = lo;
+  const int64_t g = find_group(tile_prefix, groups, tile);
   const int64_t local = tile - tile_prefix[g];
   const int64_t tm = local / tiles_n, tn = local % tiles_n;
   ExactProblem p = base;
@@ -729,7 +755,7 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.k_end = offsets[g + 1];
     p.C = base.C + g * M * N;
   }
-  exact_gemm_tile<LD, BM, BN, SM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
+  exact_gemm_tile<LD, BM, BN, SM, OCC>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // ---------------------------------------------------------------------------
@@ -788,24 +814,41 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, 
   return hipGetLastError();
 }
 
-__global__ void tile_prefix_kernel(const int64_t* __restrict__ offsets, int64_t groups, int64_t total, int vary_k,
-                                   int64_t align, int64_t bm, int64_t tiles_m_fixed, int64_t tiles_n,
-                                   int64_t* __restrict__ prefix) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  // The offsets must describe a partition of [0, total) (aligned to `align` when
-  // they split the reduction axis); otherwise no tile runs.
-  bool ok = offsets[0] == 0 && offsets[groups] == total;
-  for (int64_t g = 0; g < groups && ok; ++g) {
-    ok = offsets[g + 1] >= offsets[g];
-    if (vary_k) ok = ok && (offsets[g] % align == 0);
+// One wave: checks that the offsets partition [0, total) (aligned to `align` when they
+// split the reduction axis) and writes the exclusive prefix of the per-group tile counts,
+// 64 groups per round (lane scan with shuffles). Invalid offsets give an all-zero prefix,
+// so no tile runs.
+__global__ void __launch_bounds__(64) tile_prefix_kernel(const int64_t* __restrict__ offsets, int64_t groups,
+                                                         int64_t total, int vary_k, int64_t align, int64_t bm,
+                                                         int64_t tiles_m_fixed, int64_t tiles_n,
+                                                         int64_t* __restrict__ prefix) {
+  const int lane = threadIdx.x;
+  bool bad = false;
+  for (int64_t g0 = 0; g0 < groups; g0 += 64) {
+    const int64_t g = g0 + lane;
+    if (g < groups) {
+      const int64_t a = offsets[g], b = offsets[g + 1];
+      bad = bad || b < a || (vary_k && (a % align != 0));
+    }
   }
-  int64_t acc = 0;
-  for (int64_t g = 0; g < groups; ++g) {
-    prefix[g] = ok ? acc : 0;
-    const int64_t mg = vary_k ? tiles_m_fixed : (offsets[g + 1] - offsets[g] + bm - 1) / bm;
-    if (ok) acc += mg * tiles_n;
+  bad = bad || offsets[0] != 0 || offsets[groups] != total;
+  const bool ok = __ballot(bad) == 0;
+  int64_t carry = 0;
+  for (int64_t g0 = 0; g0 < groups; g0 += 64) {
+    const int64_t g = g0 + lane;
+    int64_t cnt = 0;
+    if (g < groups) cnt = vary_k ? tiles_m_fixed : (offsets[g + 1] - offsets[g] + bm - 1) / bm;
+    cnt *= tiles_n;
+    int64_t incl = cnt;                                   // inclusive scan over the 64 lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (g < groups) prefix[g] = ok ? carry + incl - cnt : 0;
+    carry += __shfl(incl, 63, 64);
   }
-  prefix[groups] = ok ? acc : 0;
+  if (lane == 0) prefix[groups] = ok ? carry : 0;
 }
 
 size_t grouped_gemm_ws_bytes(int64_t groups) { return (size_t)(((groups + 1) * 8 + 255) / 256 * 256); }
@@ -814,7 +857,7 @@ template <int LD, int BT, int SM>
 static void launch_grouped_t(const ExactProblem& p, const int64_t* offsets, const int64_t* prefix, int64_t max_tiles,
                              int64_t groups, int vary_k, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tn = (N + BT - 1) / BT;
-  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
+  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, 2>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
                      prefix, groups, vary_k, M, N, tn);
 }
 

@@ -21,14 +21,17 @@
 // consecutive K products in a ~13-bit window (measured), which breaks the
 // 2e-5 bound on outlier-heavy data (see gemm_mxfp8.hip).
 //
-// Data movement: raw operand tiles (64 K per stage: 128 B/row BF16, 64 B/row
-// MXFP8, 32 B/row NVFP4) go global -> LDS with gfx950's direct loads
-// (global_load_lds_dwordx4: lane l of a wave instruction lands at LDS
-// base + 16 l), through a 16-byte XOR swizzle chosen so that each 16-lane
-// fragment read (ds_read_b128) covers all 64 banks. NS stages (up to 4) keep
-// NS - 1 tiles in flight; explicit vmcnt waits + one barrier per K tile.
-// Scales (MXFP8/NVFP4) are loaded per lane straight into registers NS - 1
-// tiles ahead. Out-of-range rows and K chunks read a 16-byte zero block.
+// Data movement: raw operand tiles go global -> LDS with gfx950's direct loads
+// (buffer_load_dwordx4 ... lds: lane l of a wave instruction lands at LDS base +
+// 16 l), through a 16-byte XOR swizzle chosen so that each 16-lane fragment read
+// (ds_read_b128) covers all 64 banks (measured conflict-free). A stage holds 64 K
+// (128 B/row BF16, 64 B/row MXFP8, 32 B/row NVFP4), or 128 B/row for every format
+// in the dense kernels when K allows chunked scales (128 K MXFP8, 256 K NVFP4:
+// fewer barriers, larger loads). NS stages keep NS - 1 tiles in flight; explicit
+// vmcnt waits + one barrier per stage. Scales travel either per stage into
+// 4-byte LDS slots, or as 16-byte chunks per row (16 blocks) double-buffered in
+// LDS and read into registers once per chunk. Out-of-range rows and K chunks
+// read zeros (buffer range checks).
 //
 // Operand layouts of the 32x32x16 16-bit MFMAs (measured): lane l supplies row
 // l % 32 and 8 consecutive K; accumulator r of lane l is
@@ -65,24 +68,33 @@ template <int LD, int SM> struct ScaleDma {
 };
 
 // OCC = workgroups meant to share one CU: the LDS budget of a workgroup is 1 / OCC of it.
-template <int LD, int BM, int BN, int SM, int OCC = 1>
+// WIDE (chunked-scale mode only): 128 bytes per row and stage for every format (MXFP8 128 K,
+// NVFP4 256 K per stage), i.e. fewer barriers and larger loads per stage.
+template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false>
 struct Cfg {
-  static constexpr int RB = RowBytes<LD>::v;
+  static constexpr int RB = (WIDE && LD != 0) ? 128 : RowBytes<LD>::v;
+  static constexpr int BK = LD == 0 ? RB / 2 : LD == 1 ? RB : 2 * RB;   // K elements per stage
+  static constexpr int SBS = RB / 32;                                     // sub-blocks per stage
+  static_assert(!WIDE || SM == 2, "wide stages need chunked scales");
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int SU = ScaleDma<LD, SM>::SU, SZ = ScaleDma<LD, SM>::SZ;
   static constexpr bool CH = SM == 2 && LD != 0;                 // chunked scales
-  static constexpr int SPC = LD == 1 ? 8 : 4;                     // stages per scale chunk
+  // stages per 16-byte scale chunk (16 blocks)
+  static constexpr int SPC = LD == 1 ? 16 / (BK / 32) : LD == 2 ? 16 / (BK / 16) : 4;
   static constexpr int CH_HALF = CH ? (BM + BN) * 16 : 0;         // one chunk buffer
   static constexpr int S_BYTES = SU * (BM + BN) * 4;              // scale slots of one stage
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
   static constexpr int FREE = kLdsBytes / OCC - 2 * CH_HALF;
-  static constexpr int NS = (4 * STAGE <= FREE) ? 4 : (3 * STAGE <= FREE ? 3 : 2);
+  static constexpr int NS_LDS = (4 * STAGE <= FREE) ? 4 : (3 * STAGE <= FREE ? 3 : 2);
+  static constexpr int NS = (CH && NS_LDS > SPC + 1) ? SPC + 1 : NS_LDS;
   static constexpr int IA = A_BYTES / 4096, IB = B_BYTES / 4096;  // 1 KiB wave instructions per wave
   static constexpr int IS = SU * (BM + BN) / 256;                 // 64-row scale loads per wave
   static constexpr int XS = CH ? (BM + BN) / 256 : 0;             // chunk loads per wave
   static constexpr int TI = BM / 64, TJ = BN / 64;                // 32x32 MFMA tiles per wave
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "tile must split into 1 KiB wave loads");
-  static_assert(!CH || NS == 4, "chunked scales assume four stages");
+  // chunk c + 1 is issued at stage SPC c ahead of that stage's loads (tile SPC c + NS - 1);
+  // the wait for tile SPC (c + 1) must cover it
+  static_assert(!CH || NS - 1 <= SPC, "scale chunk must land with the tiles it covers");
 };
 }  // namespace gx
 
@@ -260,15 +272,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the loads of the stage NS - 1 ahead are interleaved with the first sub-block's
 // MFMAs, and the barrier that publishes the next stage sits halfway through the
 // last sub-block.
-template <int LD, int BM, int BN, int SM, int OCC = 1>
+template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false>
 __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0,
                                                 uint8_t* lds1, uint8_t* lds2, uint8_t* lds3, uint8_t* ldsc) {
-  using C = gx::Cfg<LD, BM, BN, SM, OCC>;
+  using C = gx::Cfg<LD, BM, BN, SM, OCC, WIDE>;
   constexpr bool AL = SM >= 1;                            // every K tile full and 64-aligned
   constexpr bool CH = C::CH;
   constexpr int XS = C::XS, SPC = C::SPC;
   constexpr int RB = C::RB, NS = C::NS, TI = C::TI, TJ = C::TJ, IA = C::IA, IB = C::IB, IS = C::IS;
-  constexpr int SBS = LD == 0 ? 4 : LD == 1 ? 2 : 1;     // sub-blocks per stage
+  constexpr int SBS = C::SBS;                             // sub-blocks per stage
   constexpr int NF = TI + TJ;                             // fragments per lane and sub-block
   constexpr int BS = LD == 1 ? 32 : 16;                   // elements per scale block
   constexpr int EPC = LD == 0 ? 8 : LD == 1 ? 16 : 32;    // elements per 16-byte chunk
@@ -369,7 +381,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   const uint32_t lbase[4] = {lds_addr(lds0), lds_addr(lds1), lds_addr(lds2), lds_addr(lds3)};
 
   const int kb = (int)p.k_begin, ke = (int)p.k_end;       // K <= 2^22
-  const int nk = (ke - kb + gx::BK - 1) / gx::BK;
+  const int nk = (ke - kb + C::BK - 1) / C::BK;
 
   // Uniform load parameters of tile t. Tiles past the end read zeros (out-of-range
   // SGPR offset); in the last tile, chunks and scale units at or beyond k_end are
@@ -377,11 +389,11 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   struct TileK { uint32_t sod, sos; int k0; bool tail; };
   auto tile_k = [&](int t) {
     TileK r;
-    r.k0 = kb + t * gx::BK;
+    r.k0 = kb + t * C::BK;
     const bool past = t >= nk;
     r.sod = past ? kOutOfRange : (uint32_t)(LD == 0 ? 2 * r.k0 : LD == 1 ? r.k0 : r.k0 / 2);
     r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS);
-    r.tail = !AL && !past && r.k0 + gx::BK > ke;
+    r.tail = !AL && !past && r.k0 + C::BK > ke;
     return r;
   };
   // DMA unit d of a tile into slot S: units 0 .. GA-1 are groups of up to 4 A loads,
@@ -446,7 +458,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // is an instruction offset.
   uint32_t xo[SBS];
 #pragma unroll
-  for (int b = 0; b < SBS; ++b) xo[b] = (uint32_t)(lr * RB + (((LD == 2 ? h : 2 * b + h) ^ swz<RB>(lr)) << 4));
+  for (int b = 0; b < SBS; ++b) xo[b] = (uint32_t)(lr * RB + (((2 * b + h) ^ swz<RB>(lr)) << 4));
   const uint32_t wA = (uint32_t)(wm * (BM / 2) * RB), wB = (uint32_t)(C::A_BYTES + wn * (BN / 2) * RB);
   const uint32_t xs = (uint32_t)(lr * 4);                 // scale slot of the lane's row
   const uint32_t wsA = (uint32_t)(C::A_BYTES + C::B_BYTES + wm * (BM / 2) * 4);
@@ -478,11 +490,11 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       }
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        if constexpr (LD == 1) {
-          constexpr int idx = tp * 2 + b;
+        if constexpr (LD == 1) {                      // one block per sub-block
+          constexpr int idx = tp * SBS + b;
           fr.sc[f] = (chr[f][idx / 4] >> (8 * (idx % 4))) & 0xFFu;
-        } else {
-          fr.sc[f] = (chr[f][tp] >> (16 * h)) & 0xFFFFu;
+        } else {                                      // four blocks per sub-block, two per lane
+          fr.sc[f] = (chr[f][tp * SBS + b] >> (16 * h)) & 0xFFFFu;
         }
       }
     } else if constexpr (LD != 0) {
@@ -693,13 +705,13 @@ __device__ __forceinline__ bool exact_map_tile(int64_t b, int64_t tiles_m, int64
   __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::NS > 3 ? C::STAGE : 16];                 \
   __shared__ __attribute__((aligned(1024))) uint8_t ldsc[C::CH ? 2 * C::CH_HALF : 16];
 
-template <int LD, int BM, int BN, int SM>
+template <int LD, int BM, int BN, int SM, bool WIDE>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) exact_dense_kernel(ExactProblem p, int64_t tiles_m, int64_t tiles_n) {
-  using C = gx::Cfg<LD, BM, BN, SM>;
+  using C = gx::Cfg<LD, BM, BN, SM, 1, WIDE>;
   MXQ_EXACT_LDS(C)
   int64_t tm, tn;
   if (!exact_map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
-  exact_gemm_tile<LD, BM, BN, SM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
+  exact_gemm_tile<LD, BM, BN, SM, 1, WIDE>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // Group of a tile: the largest g with tile_prefix[g] <= tile (tile_prefix is non-decreasing
@@ -726,11 +738,11 @@ __device__ __forceinline__ int64_t find_group(const int64_t* __restrict__ prefix
 //   vary_k = 1: group g reduces over k in [off[g], off[g+1]) into C_g = C + g*M*N.
 // OCC = 2 gives each workgroup half the LDS, so two share a CU and one's prologue and
 // epilogue overlap the other's main loop (expert tiles are short in K or in rows).
-template <int LD, int BM, int BN, int SM, int OCC>
+template <int LD, int BM, int BN, int SM, int OCC, bool WIDE>
 __global__ void __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, const int64_t* __restrict__ tile_prefix,
                      int64_t groups, int vary_k, int64_t M, int64_t N, int64_t tiles_n) {
-  using C = gx::Cfg<LD, BM, BN, SM, OCC>;
+  using C = gx::Cfg<LD, BM, BN, SM, OCC, WIDE>;
   MXQ_EXACT_LDS(C)
   const int64_t tile = blockIdx.x;
   if (tile >= tile_prefix[groups]) return;
@@ -755,12 +767,13 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.k_end = offsets[g + 1];
     p.C = base.C + g * M * N;
   }
-  exact_gemm_tile<LD, BM, BN, SM, OCC>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
+  exact_gemm_tile<LD, BM, BN, SM, OCC, WIDE>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+
 static int pick_tile(int64_t M, int64_t N) {
   // 256 x 256 unless that leaves most of the 256 CUs idle; then 128 x 128.
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
@@ -771,7 +784,8 @@ template <int LD, int BT, int SM>
 static void launch_dense_t(const ExactProblem& p, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tm = (M + BT - 1) / BT, tn = (N + BT - 1) / BT;
   const int64_t blocks = (tm * tn + 7) / 8 * 8;
-  hipLaunchKernelGGL((exact_dense_kernel<LD, BT, BT, SM>), dim3((unsigned)blocks), dim3(256), 0, st, p, tm, tn);
+  constexpr bool WIDE = SM == 2 && LD != 0;       // measured: 3-6% faster dense tiles
+  hipLaunchKernelGGL((exact_dense_kernel<LD, BT, BT, SM, WIDE>), dim3((unsigned)blocks), dim3(256), 0, st, p, tm, tn);
 }
 
 // Scale mode: 2 when K % 64 == 0 and every scale row starts 16-byte aligned
@@ -857,7 +871,8 @@ template <int LD, int BT, int SM>
 static void launch_grouped_t(const ExactProblem& p, const int64_t* offsets, const int64_t* prefix, int64_t max_tiles,
                              int64_t groups, int vary_k, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tn = (N + BT - 1) / BT;
-  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, 2>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
+  // expert tiles keep the narrow stages: wide NVFP4 stages leave two LDS stages at half LDS
+  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, 2, false>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
                      prefix, groups, vary_k, M, N, tn);
 }
 

@@ -125,9 +125,8 @@ class Linear:
         import microscaling_precision_quantization_amd as mxq
         s = self.sets[i % self.N_SETS]
         L = self.layer
-        out = [Stage("quantize_mxfp8_rowcol", (lambda n=n: mxq.quantize_mxfp8(s[n], out=L.q[n])),
-                     n_el * MX_ROWCOL, "hbm")
-               for n, n_el in (("x", self.T * self.DIN), ("w", self.DOUT * self.DIN), ("dy", self.T * self.DOUT))]
+        n_el = self.T * self.DIN + self.DOUT * self.DIN + self.T * self.DOUT
+        out = [Stage("quantize_mxfp8_rowcol", lambda: L.quantize(s["x"], s["w"], s["dy"]), n_el * MX_ROWCOL, "hbm")]
         out += [Stage("gemm_block_scaled_mxfp8", (lambda g=g: L.gemm(g)), self.gemm_flop, "mfma", "bf16")
                 for g in ("fprop", "dgrad", "wgrad")]
         return out
@@ -168,10 +167,8 @@ class Small:
 
     def stages(self, i):
         import microscaling_precision_quantization_amd as mxq
-        return [Stage("quantize_mxfp8_rowcol", lambda: mxq.quantize_mxfp8(self.x, out=self.qx), 256 * 512 * MX_ROWCOL,
-                      "hbm"),
-                Stage("quantize_mxfp8_rowcol", lambda: mxq.quantize_mxfp8(self.w2, out=self.qw),
-                      256 * 512 * MX_ROWCOL, "hbm"),
+        return [Stage("quantize_mxfp8_rowcol", lambda: mxq.quantize_mxfp8_multi([self.x, self.w2], [self.qx, self.qw]),
+                      2 * 256 * 512 * MX_ROWCOL, "hbm"),
                 Stage("gemm_block_scaled_mxfp8", lambda: mxq.gemm_block_scaled(mxq.MXFP8, self.qx[0], self.qx[1],
                                                                                self.qw[2], self.qw[3], out=self.c),
                       self.gemm_flop, "mfma", "bf16")]
@@ -369,8 +366,7 @@ class Stress:
         s = self.sets[i % self.N_SETS]
         st, n = self.st, self.N
         import microscaling_precision_quantization_amd as mxq
-        out = [Stage("quantize_mxfp8_rowcol", lambda: mxq.quantize_mxfp8(s["a"], out=st.qa), n * n * MX_ROWCOL, "hbm"),
-               Stage("quantize_mxfp8_rowcol", lambda: mxq.quantize_mxfp8(s["b"], out=st.qb), n * n * MX_ROWCOL, "hbm")]
+        out = [Stage("quantize_mxfp8_rowcol", lambda: st.quantize_mxfp8(s["a"], s["b"]), 2 * n * n * MX_ROWCOL, "hbm")]
         out += [Stage("gemm_block_scaled_mxfp8", (lambda g=g: st.mxfp8_gemm(g)), 2 * n ** 3, "mfma", "bf16")
                 for g in ("fprop", "dgrad", "wgrad")]
         out += [Stage("quantize_nvfp4_rht_colwise", lambda: st.quantize_rht(s["a"], s["b"]),

@@ -95,6 +95,31 @@ mxq_status quantize_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_
                           void* stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_mxfp8_multi -- quantize_mxfp8 over several tensors in one launch (e.g.
+ * the input, weight and output gradient of a linear layer, whose fprop, dgrad and
+ * wgrad GEMMs need all six copies): the same operation and output bytes as
+ * `count` calls of quantize_mxfp8, with one kernel launch instead of `count`.
+ *   Defined by: as quantize_mxfp8 (remio.ai, sections "La Compatibilidad ..." and
+ *   "Un Cuantizador Compartido Es el Mecanismo Real").
+ *   tensors : HOST array of `count` descriptors (1 <= count <= MXQ_MXFP8_MULTI_MAX);
+ *             each descriptor's fields follow quantize_mxfp8's arguments. All
+ *             tensors must request the same copies (rowwise, columnwise or both),
+ *             else MXQ_ERR_FORMAT. Any invalid descriptor fails the whole call
+ *             before anything is launched; empty tensors (rows or cols 0) are
+ *             skipped without looking at their pointers.
+ * ------------------------------------------------------------------------- */
+#define MXQ_MXFP8_MULTI_MAX 8
+typedef struct {
+  const void* x;
+  int64_t rows, cols, ld_x;
+  void* q_row;
+  void* s_row;
+  void* q_colT;
+  void* s_colT;
+} mxq_mxfp8_tensor;
+mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream);
+
+/* ---------------------------------------------------------------------------
  * quantize_nvfp4_per_token -- NVFP4 with one FP32 scale per token (row),
  * computed online in the same kernel that emits the packed E2M1 values and the
  * E4M3 block scales.

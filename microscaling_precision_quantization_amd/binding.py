@@ -29,6 +29,7 @@ _size = ctypes.c_size_t
 
 _SIGS = {
     "quantize_mxfp8": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "quantize_mxfp8_multi": [_c_void_p, _int, _c_void_p],
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
@@ -128,6 +129,25 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, 
     _check("quantize_mxfp8", lib().quantize_mxfp8(_ptr(x), R, C, x.stride(0), _ptr(q_row), _ptr(s_row),
                                                   _ptr(q_col), _ptr(s_col), _stream(dev)))
     return q_row, s_row, q_col, s_col
+
+
+class _Mxfp8Tensor(ctypes.Structure):
+    _fields_ = [("x", _c_void_p), ("rows", _i64), ("cols", _i64), ("ld_x", _i64), ("q_row", _c_void_p),
+                ("s_row", _c_void_p), ("q_colT", _c_void_p), ("s_colT", _c_void_p)]
+
+
+def quantize_mxfp8_multi(xs, outs):
+    """quantize_mxfp8 of several BF16 tensors in one launch; outs[i] = (q_row, s_row,
+    q_colT, s_colT) preallocated (a skipped copy is (None, None) in its slots)."""
+    n = len(xs)
+    arr = (_Mxfp8Tensor * n)()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        _bf16(x)
+        q_row, s_row, q_col, s_col = o
+        arr[i] = _Mxfp8Tensor(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0),
+                              *(None if t is None else t.data_ptr() for t in (q_row, s_row, q_col, s_col)))
+    _check("quantize_mxfp8_multi", lib().quantize_mxfp8_multi(ctypes.cast(arr, _c_void_p), n, _stream(xs[0].device)))
+    return outs
 
 
 def quantize_nvfp4_per_token(x: torch.Tensor):

@@ -9,6 +9,8 @@
 
 namespace mxq {
 hipError_t launch_quant_mxfp8(const void*, int64_t, int64_t, int64_t, void*, void*, void*, void*, hipStream_t);
+hipError_t launch_quant_mxfp8_multi(int, const void* const*, const int64_t*, const int64_t*, const int64_t*,
+                                    void* const*, void* const*, void* const*, void* const*, hipStream_t);
 hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
 hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
                               float*, uint32_t*, int64_t, hipStream_t);
@@ -94,6 +96,38 @@ mxq_status quantize_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_
   if (((rows + 127) / 128) * ((cols + 127) / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
   return hip_status(mxq::launch_quant_mxfp8(x, rows, cols, ld_x, do_row ? q_row : nullptr, s_row,
                                             do_col ? q_colT : nullptr, s_colT, S(stream)));
+}
+
+mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream) {
+  if (count < 1 || count > MXQ_MXFP8_MULTI_MAX) return MXQ_ERR_SHAPE;
+  if (!tensors) return MXQ_ERR_NULL;
+  const void* x[MXQ_MXFP8_MULTI_MAX];
+  int64_t rows[MXQ_MXFP8_MULTI_MAX], cols[MXQ_MXFP8_MULTI_MAX], ld[MXQ_MXFP8_MULTI_MAX];
+  void *qr[MXQ_MXFP8_MULTI_MAX], *sr[MXQ_MXFP8_MULTI_MAX], *qc[MXQ_MXFP8_MULTI_MAX], *sc[MXQ_MXFP8_MULTI_MAX];
+  int n = 0;
+  int64_t blocks = 0;
+  bool mode_set = false, mode_row = false, mode_col = false;
+  for (int i = 0; i < count; ++i) {
+    const mxq_mxfp8_tensor& t = tensors[i];
+    if (t.rows < 0 || t.cols < 0) return MXQ_ERR_SHAPE;
+    if (t.rows == 0 || t.cols == 0) continue;                 // empty tensors are skipped
+    const bool do_row = t.q_row || t.s_row, do_col = t.q_colT || t.s_colT;
+    if (!t.x || (!do_row && !do_col)) return MXQ_ERR_NULL;
+    if ((do_row && (!t.q_row || !t.s_row)) || (do_col && (!t.q_colT || !t.s_colT))) return MXQ_ERR_NULL;
+    if (mode_set && (do_row != mode_row || do_col != mode_col)) return MXQ_ERR_FORMAT;
+    mode_set = true; mode_row = do_row; mode_col = do_col;
+    if (t.cols % 32) return MXQ_ERR_SHAPE;
+    if (do_col && t.rows % 32) return MXQ_ERR_SHAPE;
+    if (t.ld_x < t.cols) return MXQ_ERR_SHAPE;
+    if (t.ld_x % 8 || !al16(t.x) || (do_row && !al16(t.q_row)) || (do_col && !al16(t.q_colT))) return MXQ_ERR_ALIGN;
+    blocks += ((t.rows + 127) / 128) * ((t.cols + 127) / 128);
+    x[n] = t.x; rows[n] = t.rows; cols[n] = t.cols; ld[n] = t.ld_x;
+    qr[n] = do_row ? t.q_row : nullptr; sr[n] = t.s_row; qc[n] = do_col ? t.q_colT : nullptr; sc[n] = t.s_colT;
+    ++n;
+  }
+  if (blocks > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  if (n == 0) return MXQ_OK;
+  return hip_status(mxq::launch_quant_mxfp8_multi(n, x, rows, cols, ld, qr, sr, qc, sc, S(stream)));
 }
 
 mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x, void* q_packed,

@@ -27,12 +27,37 @@
 
 namespace mxq {
 
+// Up to kMaxQJobs tensors per launch (e.g. the input, weight and gradient of a linear
+// layer): workgroups [block0, block0 + blocks) of the grid belong to job j.
+constexpr int kMaxQJobs = 8;
+struct QJob {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  uint8_t *q_row, *s_row, *q_colT, *s_colT;
+  int64_t col_tiles, block0;
+  int row_scale_dw, col_scale_dw;   // dword scale stores allowed (4-byte aligned scale rows)
+};
+struct QJobs {
+  QJob j[kMaxQJobs];
+  int n;
+};
+
 template <bool DO_ROW, bool DO_COL>
 __global__ void __launch_bounds__(256)
-quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-                   uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
-                   uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT,
-                   int64_t col_tiles, int row_scale_dw, int col_scale_dw) {
+quant_mxfp8_kernel(const QJobs jobs) {
+  // job of this workgroup (static indices only: the table stays in kernel arguments)
+  QJob jb = jobs.j[0];
+#pragma unroll
+  for (int i = 1; i < kMaxQJobs; ++i)
+    if (i < jobs.n && (int64_t)blockIdx.x >= jobs.j[i].block0) jb = jobs.j[i];
+  const uint16_t* __restrict__ x = jb.x;
+  const int64_t rows = jb.rows, cols = jb.cols, ld_x = jb.ld_x, col_tiles = jb.col_tiles;
+  uint8_t* __restrict__ q_row = jb.q_row;
+  uint8_t* __restrict__ s_row = jb.s_row;
+  uint8_t* __restrict__ q_colT = jb.q_colT;
+  uint8_t* __restrict__ s_colT = jb.s_colT;
+  const int row_scale_dw = jb.row_scale_dw, col_scale_dw = jb.col_scale_dw;
+  const int64_t blk = (int64_t)blockIdx.x - jb.block0;
   // Transposed FP8 tile: column cl at cl * 128; its 8-byte granule g (rows 8g .. 8g+7)
   // sits at granule g ^ 4 * (cl / 8 % 4), which spreads one wave's writes over more banks.
   __shared__ __attribute__((aligned(16))) uint8_t lcol[DO_COL ? 128 * 128 : 16];
@@ -42,8 +67,8 @@ quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, i
   const int w = threadIdx.x >> 6;
   const int m = lane >> 4;          // row group of 8 inside the wave slab
   const int c16 = lane & 15;        // column group of 8 inside the 128 columns
-  const int64_t band = (int64_t)blockIdx.x / col_tiles;
-  const int64_t ct = (int64_t)blockIdx.x % col_tiles;
+  const int64_t band = blk / col_tiles;
+  const int64_t ct = blk % col_tiles;
   const int64_t R0 = band * 128, C0 = ct * 128;
   const int rl0 = 32 * w + 8 * m;   // tile row of v[0]
   const int64_t c = C0 + 8 * c16;
@@ -154,24 +179,38 @@ quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, i
   }
 }
 
+// Tensors of one launch must request the same copies (row, column or both).
+hipError_t launch_quant_mxfp8_multi(int n, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                    const int64_t* ld_x, void* const* q_row, void* const* s_row,
+                                    void* const* q_colT, void* const* s_colT, hipStream_t stream) {
+  QJobs jobs;
+  jobs.n = n;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    QJob& j = jobs.j[i];
+    j.x = static_cast<const uint16_t*>(x[i]);
+    j.rows = rows[i]; j.cols = cols[i]; j.ld_x = ld_x[i];
+    j.q_row = (uint8_t*)q_row[i]; j.s_row = (uint8_t*)s_row[i];
+    j.q_colT = (uint8_t*)q_colT[i]; j.s_colT = (uint8_t*)s_colT[i];
+    j.col_tiles = (cols[i] + 127) / 128;
+    j.block0 = blocks;
+    blocks += (rows[i] + 127) / 128 * j.col_tiles;
+    j.row_scale_dw = j.s_row && ((uintptr_t)j.s_row & 3) == 0 && (cols[i] / 32) % 4 == 0;
+    j.col_scale_dw = j.s_colT && ((uintptr_t)j.s_colT & 3) == 0 && (rows[i] / 32) % 4 == 0;
+  }
+  if (blocks == 0) return hipSuccess;
+  dim3 grid((unsigned)blocks), block(256);
+  const bool do_row = q_row[0] != nullptr, do_col = q_colT[0] != nullptr;
+  if (do_row && do_col) hipLaunchKernelGGL((quant_mxfp8_kernel<true, true>), grid, block, 0, stream, jobs);
+  else if (do_row) hipLaunchKernelGGL((quant_mxfp8_kernel<true, false>), grid, block, 0, stream, jobs);
+  else hipLaunchKernelGGL((quant_mxfp8_kernel<false, true>), grid, block, 0, stream, jobs);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                               void* q_row, void* s_row, void* q_colT, void* s_colT,
                               hipStream_t stream) {
-  const int64_t col_tiles = (cols + 127) / 128;
-  const int64_t blocks = (rows + 127) / 128 * col_tiles;
-  dim3 grid((unsigned)blocks), block(256);
-  const uint16_t* xp = static_cast<const uint16_t*>(x);
-  uint8_t *qr = (uint8_t*)q_row, *sr = (uint8_t*)s_row, *qc = (uint8_t*)q_colT, *sc = (uint8_t*)s_colT;
-  // dword scale stores need 4-byte aligned scale rows
-  const int row_dw = sr && ((uintptr_t)sr & 3) == 0 && (cols / 32) % 4 == 0;
-  const int col_dw = sc && ((uintptr_t)sc & 3) == 0 && (rows / 32) % 4 == 0;
-  if (q_row && q_colT)
-    hipLaunchKernelGGL((quant_mxfp8_kernel<true, true>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles, row_dw, col_dw);
-  else if (q_row)
-    hipLaunchKernelGGL((quant_mxfp8_kernel<true, false>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles, row_dw, col_dw);
-  else
-    hipLaunchKernelGGL((quant_mxfp8_kernel<false, true>), grid, block, 0, stream, xp, rows, cols, ld_x, qr, sr, qc, sc, col_tiles, row_dw, col_dw);
-  return hipGetLastError();
+  return launch_quant_mxfp8_multi(1, &x, &rows, &cols, &ld_x, &q_row, &s_row, &q_colT, &s_colT, stream);
 }
 
 }  // namespace mxq

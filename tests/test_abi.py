@@ -51,6 +51,23 @@ def test_quantize_mxfp8_validation():
     assert q8(P, 0, 32, 32, P, P, P, P, None) == 0                     # empty: no-op
 
 
+def multi(descs):
+    arr = (B._Mxfp8Tensor * max(len(descs), 1))(*[B._Mxfp8Tensor(*d) for d in descs])
+    return B.lib().quantize_mxfp8_multi(ctypes.cast(arr, ctypes.c_void_p), len(descs), None)
+
+
+def test_quantize_mxfp8_multi_validation():
+    ok = (P, 64, 64, 64, P, P, P, P)
+    assert multi([]) == 2                                               # count 0
+    assert multi([ok] * 9) == 2                                         # beyond the maximum
+    assert multi([ok, (P, 64, 64, 64, P, P, None, None)]) == 4          # mixed copies
+    assert multi([ok, (P, 64, 48, 48, P, P, P, P)]) == 2                # cols % 32 in the 2nd tensor
+    assert multi([ok, (MIS, 64, 64, 64, P, P, P, P)]) == 3
+    assert multi([ok, (None, 64, 64, 64, P, P, P, P)]) == 1
+    assert multi([(P, 0, 64, 64, P, P, P, P)]) == 0                     # all empty: no-op
+    assert B.lib().quantize_mxfp8_multi(None, 1, None) == 1
+
+
 def test_nvfp4_validation():
     L = B.lib()
     assert L.quantize_nvfp4_per_token(P, 4, 40, 40, P, P, P, None) == 2       # hidden % 16

@@ -109,6 +109,34 @@ def test_mxfp8_stress_full_size_sampled():
         assert_bytes_equal(sc[:, b:b + 1], es, f"band {b} colwise scales")
 
 
+def test_mxfp8_multi_matches_single_calls():
+    """One launch over several tensors writes exactly the bytes of one call per tensor."""
+    g = inputs.rng(95, 0)
+    shapes = [(4128, 96), (32, 32), (0, 64), (256, 544), (96, 160)]
+    xs = [inputs.to_bf16_bits(g.standard_normal(sh) * g.lognormal(0, 2, (sh[0], 1))) for sh in shapes]
+    dx = [dev_bf16(x) for x in xs]
+    outs = [tuple(torch.empty(s, dtype=torch.uint8, device="cuda") for s in ((r, c), (r, c // 32), (c, r), (c, r // 32)))
+            for r, c in shapes]
+    mxq.quantize_mxfp8_multi(dx, outs)
+    for x, o, sh in zip(dx, outs, shapes):
+        if sh[0] == 0:
+            continue
+        ref = mxq.quantize_mxfp8(x)
+        for a, b, nm in zip(o, ref, ("q_row", "s_row", "q_colT", "s_colT")):
+            assert_bytes_equal(host(a), host(b), f"multi {sh} {nm}")
+    # rowwise only, rows not a multiple of 32
+    xs2 = [dev_bf16(inputs.normal_bf16(g, (37, 64), 1.0)), dev_bf16(inputs.normal_bf16(g, (1, 128), 1.0))]
+    outs2 = [(torch.empty((37, 64), dtype=torch.uint8, device="cuda"), torch.empty((37, 2), dtype=torch.uint8, device="cuda"),
+              None, None),
+             (torch.empty((1, 128), dtype=torch.uint8, device="cuda"), torch.empty((1, 4), dtype=torch.uint8, device="cuda"),
+              None, None)]
+    mxq.quantize_mxfp8_multi(xs2, outs2)
+    for x, o in zip(xs2, outs2):
+        ref = mxq.quantize_mxfp8(x, colwise=False)
+        assert_bytes_equal(host(o[0]), host(ref[0]), "multi rowwise q")
+        assert_bytes_equal(host(o[1]), host(ref[1]), "multi rowwise s")
+
+
 # ------------------------------- NVFP4 -------------------------------------
 
 def check_token(xb, what=""):

@@ -184,9 +184,16 @@ nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
 }
 
 // ---------------------------------------------------------------------------
-// Column-blocked (transposed) quantizer: blocks of 16 consecutive ROWS of x,
-// output row c of (cols, rows/2) holds column c of x. One wave = 16 rows x 512
-// columns; lane holds 8 columns x 16 rows.
+// Column-blocked (transposed) quantizer: blocks of 16 consecutive ROWS of x;
+// output row c of (cols, rows/2) holds column c of x.
+// A workgroup (4 waves) owns a 256-row x 128-column tile; wave w owns rows
+// 64w .. 64w+63 of it and lane = 16*m + c16 holds rows 16m .. 16m+15 and
+// columns 8*c16 .. 8*c16+7 as sixteen 16-byte loads (each load instruction of
+// the wave reads 4 full 256-byte row segments). Every 16-row block of a column
+// is then inside one lane: transform, block amax and quantization need no lane
+// exchange. The packed bytes (8 per column and lane) and block scales go
+// through LDS, so each column of the tile leaves as one 128-byte segment and
+// its 16 scale bytes as one 16-byte store.
 //   MODE 1: scope amax from scope_amax[c / group_rows]; MODE 2: pass 1 (amax only).
 // ---------------------------------------------------------------------------
 template <int MODE, bool RHT>
@@ -194,13 +201,18 @@ __global__ void __launch_bounds__(256)
 nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
                   int64_t group_rows, uint32_t neg_mask,
                   uint32_t* __restrict__ scope_amax,
-                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t col_tiles) {
-  const int lane = threadIdx.x & 63;
-  const int64_t band = (int64_t)blockIdx.x / col_tiles * 4 + (threadIdx.x >> 6);   // 16-row band
-  const int64_t c = ((int64_t)blockIdx.x % col_tiles) * 512 + 8 * lane;
-  if (band * 16 >= rows) return;
-  const bool ok = c < cols;
-  const int64_t r0 = band * 16;
+                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t col_tiles, int wide_stores) {
+  // packed tile: column cl at cl * 128, 8-byte granule g = 4w + m at (g ^ 4 * (cl / 8 % 4))
+  __shared__ __attribute__((aligned(16))) uint8_t lq[MODE == 1 ? 128 * 128 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ls[MODE == 1 ? 128 * 16 : 16];
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane >> 4, c16 = lane & 15;
+  const int64_t band = (int64_t)blockIdx.x / col_tiles, ct = (int64_t)blockIdx.x % col_tiles;
+  const int64_t R0 = band * 256, C0 = ct * 128;
+  const int64_t r0 = R0 + 64 * w + 16 * m;          // first row of the lane's block
+  const int64_t c = C0 + 8 * c16;
+  const bool ok = c < cols && r0 < rows;            // cols % 8 == 0, rows % 16 == 0: whole blocks
   uint4 v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j)
@@ -211,65 +223,100 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
 #pragma unroll
     for (int i = 0; i < 16; ++i) sg[i] = ((neg_mask >> i) & 1u) ? -1.0f : 1.0f;
   }
-  // two columns (one dword position p) at a time
-  float mloc[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // per-group max (MODE 2)
+  float mloc = 0.0f;                                 // MODE 2: max over the lane's 8 columns
+  float s_enc = 1.0f;
+  if (MODE == 1 && ok) {
+    float tt;
+    scope_scales(__uint_as_float(scope_amax[c / group_rows]), s_enc, tt);   // 8 columns, one scope
+  }
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
+  for (int cc = 0; cc < 8; ++cc) {
+    float f[16];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float f[16];
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t wd = (cc >> 1) == 0 ? v[j].x : (cc >> 1) == 1 ? v[j].y : (cc >> 1) == 2 ? v[j].z : v[j].w;
+      f[j] = (cc & 1) ? bf16_hi(wd) : bf16_lo(wd);
+    }
+    if (RHT) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t w = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
-        f[j] = half ? bf16_hi(w) : bf16_lo(w);
-      }
-      if (RHT) {
+      for (int i = 0; i < 16; ++i) f[i] *= sg[i];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) f[i] *= sg[i];
+      for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
-        for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (i & h) continue;
-            const float a = f[i], b = f[i + h];
-            f[i] = a + b;
-            f[i + h] = a - b;
-          }
+        for (int i = 0; i < 16; ++i) {
+          if (i & h) continue;
+          const float a = f[i], b = f[i + h];
+          f[i] = a + b;
+          f[i + h] = a - b;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) f[i] *= 0.25f;
       }
-      float a = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(f[k]));
-      const int64_t col = c + 2 * p + half;
-      if (MODE == 2) {
-        mloc[0] = fmaxf(mloc[0], a);
-        continue;
-      }
-      if (!ok) continue;
-      float s_enc, t;
-      scope_scales(__uint_as_float(scope_amax[col / group_rows]), s_enc, t);
+      for (int i = 0; i < 16; ++i) f[i] *= 0.25f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(f[k]));
+    if (MODE == 2) {
+      mloc = fmaxf(mloc, a);
+    } else {
       float r;
       const uint32_t code = block_scale(a, s_enc, r);
       const uint32_t lo = pack8_e2m1(f, r), hi = pack8_e2m1(f + 8, r);
-      *reinterpret_cast<uint2*>(q + col * (rows / 2) + r0 / 2) = make_uint2(lo, hi);
-      s[col * (rows / 16) + band] = (uint8_t)code;
+      const int cl = 8 * c16 + cc;
+      const int g = (4 * w + m) ^ ((c16 & 3) * 4);
+      *reinterpret_cast<uint2*>(lq + cl * 128 + g * 8) = make_uint2(lo, hi);
+      ls[cl * 16 + 4 * w + m] = (uint8_t)code;
     }
   }
+
   if (MODE == 2) {
     // The lane's 8 columns share a scope (group_rows % 8 == 0). Reduce over the
     // workgroup when its whole column tile lies in one scope.
-    const int64_t tile_c0 = ((int64_t)blockIdx.x % col_tiles) * 512;
-    const int64_t tile_c1 = min(tile_c0 + 512, cols) - 1;
-    const bool shared = tile_c0 / group_rows == tile_c1 / group_rows;
+    const int64_t tile_c1 = min(C0 + 128, cols) - 1;
+    const bool shared = C0 / group_rows == tile_c1 / group_rows;
     if (!shared) {
-      if (ok && mloc[0] > 0.0f) atomicMax(scope_amax + c / group_rows, __float_as_uint(mloc[0]));
+      if (ok && mloc > 0.0f) atomicMax(scope_amax + c / group_rows, __float_as_uint(mloc));
       return;
     }
-    float m = wave_max_f32(mloc[0]);
-    // waves whose band is past the end returned early; only use an atomic per wave
-    if (lane == 0 && m > 0.0f) atomicMax(scope_amax + tile_c0 / group_rows, __float_as_uint(m));
+    const float wm = wave_max_f32(mloc);
+    if (lane == 0) red[w] = __float_as_uint(wm);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t mm = max(max(red[0], red[1]), max(red[2], red[3]));
+      if (mm) atomicMax(scope_amax + C0 / group_rows, mm);
+    }
+    return;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int64_t rb = rows / 2;                       // packed bytes per output row
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = k * 256 + t;                       // 16-byte chunk: column i / 8, rows 32 (i % 8) ..
+    const int cl = i >> 3, ch = i & 7;
+    const int64_t col = C0 + cl, rr = R0 + 32 * ch;
+    if (col >= cols || rr >= rows) continue;
+    const int g0 = (2 * ch) ^ (((cl >> 3) & 3) * 4);  // granules 2ch, 2ch+1 stay adjacent
+    const uint4 d = *reinterpret_cast<const uint4*>(lq + cl * 128 + g0 * 8);
+    uint8_t* dst = q + col * rb + rr / 2;
+    if (wide_stores) {                               // rows % 32 == 0: aligned whole chunks
+      *reinterpret_cast<uint4*>(dst) = d;
+    } else {                                         // 8-byte halves (rows % 16 == 0)
+      *reinterpret_cast<uint2*>(dst) = make_uint2(d.x, d.y);
+      if (rr + 16 < rows) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(d.z, d.w);
+    }
+  }
+  if (t < 128 && C0 + t < cols) {
+    const int64_t sb = rows / 16;                    // scale bytes per output row
+    const int64_t nb = min((int64_t)16, sb - band * 16);
+    uint8_t* dst = s + (C0 + t) * sb + band * 16;
+    const uint4 d = *reinterpret_cast<const uint4*>(ls + t * 16);
+    if (wide_stores && (sb % 16) == 0) {
+      *reinterpret_cast<uint4*>(dst) = d;
+    } else {
+      const uint32_t wv[4] = {d.x, d.y, d.z, d.w};
+      for (int b = 0; b < nb; ++b) dst[b] = (uint8_t)(wv[b / 4] >> (8 * (b % 4)));
+    }
   }
 }
 
@@ -305,10 +352,13 @@ static void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
 template <int MODE, bool RHT>
 static void launch_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
                         uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, hipStream_t st) {
-  const int64_t col_tiles = (cols + 511) / 512;
-  const int64_t bands = rows / 16;
-  dim3 grid((unsigned)((bands + 3) / 4 * col_tiles)), block(256);
-  hipLaunchKernelGGL((nvfp4_cols_kernel<MODE, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, col_tiles);
+  const int64_t col_tiles = (cols + 127) / 128;
+  const int64_t bands = (rows + 255) / 256;
+  // 16-byte stores need 16-byte aligned output rows (and bases)
+  const int wide = rows % 32 == 0 && ((uintptr_t)q & 15) == 0 && ((uintptr_t)s & 15) == 0;
+  dim3 grid((unsigned)(bands * col_tiles)), block(256);
+  hipLaunchKernelGGL((nvfp4_cols_kernel<MODE, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s,
+                     col_tiles, wide);
 }
 
 

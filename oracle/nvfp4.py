@@ -126,6 +126,59 @@ def quantize_per_group(x: np.ndarray, row_offsets):
     return packed, S, scope_scales(amax_g)[1].astype(f32)
 
 
+def quantize_2d(x: np.ndarray, scope_rows: int | None = None):
+    """NVFP4 weights with one E4M3 scale per 16x16 block (2D block scaling).
+
+    The pages: standard NVFP4 scales 1x16 blocks along the dot-product axis; the
+    backward pass transposes the weight, so 1x16 blocks would give the forward
+    and backward passes different quantized weights and break the chain rule;
+    scaling the weights in 16x16 blocks makes both passes use one quantized
+    representation, while activations and gradients keep 1x16 blocks
+    (7minutos.es NVFP4 page, section "La metodologia de formacion de cuatro
+    partes", the 2D weight-scaling item).
+
+    Reading (the page gives no formula): the per-block steps of the 1x16
+    quantizer with the block amax taken over the 16x16 block: A = amax over the
+    scope (the tensor, or each group of `scope_rows` rows = one expert matrix);
+    s_enc, t as scope_scales; S_b = E4M3_RNE_sat(fl(fl(a_b / 6) * s_enc));
+    r_b = min(fl(s_enc / S_b), FLT_MAX) (0 if S_b = 0); q = E2M1_RNE_sat(fl(x * r_b)).
+
+    x: (R, C), float32 or BF16 bits, R % 16 == C % 16 == 0.
+    Returns (packed (R, C/2), S_rows (R, C/16), packedT (C, R/2), S_T (C, R/16),
+    t (groups,)). S_rows repeats each 16x16 block's code for its 16 rows (the
+    1x16 form a K-contiguous GEMM consumes); packedT / S_T are the transposed
+    tensor in the same form, holding the identical codes.
+    """
+    x = bf16_bits_to_f32(x) if x.dtype == np.uint16 else np.asarray(x, dtype=f32)
+    R, C = x.shape
+    if R % BLOCK or C % BLOCK:
+        raise ValueError("both axes must be multiples of 16")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input")
+    gr = R if scope_rows is None else int(scope_rows)
+    if gr <= 0 or R % gr or gr % BLOCK:
+        raise ValueError("scope rows must divide the rows and be a multiple of 16")
+    G = R // gr
+    amax_g = np.array([np.max(np.abs(x[g * gr:(g + 1) * gr])) if gr * C else 0.0 for g in range(G)], dtype=f32)
+    s_enc_g, t = scope_scales(amax_g)
+    s_enc = np.repeat(s_enc_g, gr // BLOCK)                         # per 16-row band
+    xb = x.reshape(R // BLOCK, BLOCK, C // BLOCK, BLOCK)
+    a_b = np.max(np.abs(xb), axis=(1, 3))                           # (R/16, C/16) exact
+    d_b = ((a_b / f32(6.0)).astype(f32) * s_enc[:, None]).astype(f32)
+    S = encode_e4m3(d_b.astype(np.float64))
+    S_val = decode_e4m3(S).astype(f32)
+    with np.errstate(divide="ignore", over="ignore"):
+        r_b = (s_enc[:, None] / S_val).astype(f32)
+    r_b = np.where(S_val == 0, f32(0.0), np.minimum(r_b, f32(FLT_MAX))).astype(f32)
+    prod = (xb * r_b[:, None, :, None]).astype(f32)                # rounded to FP32 first
+    q = encode_e2m1(prod.astype(np.float64)).reshape(R, C)
+    pack = lambda codes: (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    qT = np.ascontiguousarray(q.T)
+    S_rows = np.repeat(S, BLOCK, axis=0)                            # (R, C/16)
+    S_T = np.ascontiguousarray(np.repeat(S.T, BLOCK, axis=0))      # (C, R/16)
+    return pack(q), S_rows, pack(qT), S_T, t.astype(f32)
+
+
 def unpack_codes(packed: np.ndarray) -> np.ndarray:
     """uint8 (R, C/2) -> E2M1 codes (R, C): low nibble first."""
     R, Ch = packed.shape

@@ -222,3 +222,79 @@ def test_tiny_nvfp4_gemm_against_exact_rational_dot_products():
             ex *= Fraction(float(ta[i])) * Fraction(float(tb_rows[j]))
             assert abs(Fraction(float(c[i, j])) - ex) <= abs(ex) * Fraction(1, 10 ** 12)
     assert np.allclose(ah @ bh.T, c, rtol=0, atol=0)
+
+
+# --------------------- 2D (16x16) weight block scaling ---------------------
+
+def weights(r=96, c=160, seed=5, std=0.02):
+    g = np.random.default_rng(seed)
+    return bf16(g.standard_normal((r, c)) * std * g.lognormal(0, 1, (r, 1)))
+
+
+def test_2d_transposed_weight_gets_the_same_codes():
+    # The point of 2D blocks (7minutos.es "La metodologia ..."): forward and the
+    # transposed backward see one quantized weight. Quantizing W^T must give exactly
+    # the transposed outputs of quantizing W.
+    w = weights()
+    p, S, pT, ST, t = nvfp4.quantize_2d(w)
+    wt = np.ascontiguousarray(w.T)
+    p2, S2, pT2, ST2, t2 = nvfp4.quantize_2d(wt)
+    assert np.array_equal(p2, pT) and np.array_equal(S2, ST)
+    assert np.array_equal(pT2, p) and np.array_equal(ST2, S)
+    assert t2.view(np.uint32)[0] == t.view(np.uint32)[0]
+    # and the stored transposed copy holds the same codes as the row copy
+    assert np.array_equal(nvfp4.unpack_codes(pT), nvfp4.unpack_codes(p).T)
+
+
+def test_2d_block_scale_is_shared_by_its_16_rows_and_columns():
+    w = weights(64, 64, seed=6)
+    p, S, pT, ST, t = nvfp4.quantize_2d(w)
+    blocks = S.reshape(4, 16, 4)                       # (row band, row in band, col block)
+    assert np.all(blocks == blocks[:, :1, :])
+    assert np.array_equal(S[::16], ST[::16].T)
+
+
+def test_2d_block_amax_maps_to_fp4_max():
+    # As for 1x16 blocks: every block with a normal scale encodes its amax element as +-6.
+    w = weights(128, 256, seed=7)
+    p, S, pT, ST, t = nvfp4.quantize_2d(w)
+    xv = inputs.bf16_bits_to_float(w).reshape(8, 16, 16, 16)
+    codes = nvfp4.unpack_codes(p).reshape(8, 16, 16, 16)
+    Sb = S[::16]                                      # (8, 16) one code per 16x16 block
+    for i in range(8):
+        for j in range(16):
+            blk = np.abs(xv[i, :, j, :])
+            r, c = np.unravel_index(np.argmax(blk), blk.shape)
+            if F.decode_e4m3(np.array([Sb[i, j]]))[0] >= 2.0 ** -6:
+                assert codes[i, r, j, c] & 0x7 == 0x7
+
+
+def test_2d_reduces_to_1d_when_every_row_segment_holds_the_block_amax():
+    # If each 1x16 row segment of a 16x16 block reaches the block amax, the 2D block
+    # scale equals every row segment's 1x16 scale, so the 2D quantization must equal
+    # the (independently pinned) per-tensor 1x16 quantization bit for bit.
+    g = np.random.default_rng(8)
+    x = g.uniform(-1.0, 1.0, size=(64, 96)) * 0.05
+    amax = g.uniform(0.05, 0.2, size=(4, 6))
+    for bi in range(4):
+        for bj in range(6):
+            for r in range(16):
+                c = int(g.integers(0, 16))
+                x[bi * 16 + r, bj * 16 + c] = amax[bi, bj] * (1 if g.random() < 0.5 else -1)
+    xb = bf16(x)
+    xv = inputs.bf16_bits_to_float(xb)
+    seg = np.abs(xv).reshape(64, 6, 16).max(axis=2)
+    assert np.all(seg.reshape(4, 16, 6) == seg.reshape(4, 16, 6)[:, :1, :])   # construction holds
+    p, S, pT, ST, t = nvfp4.quantize_2d(xb)
+    p1, S1, t1 = nvfp4.quantize_per_tensor(xb)
+    assert np.array_equal(p, p1) and np.array_equal(S, S1)
+    assert t.view(np.uint32)[0] == t1.view(np.uint32)[0]
+
+
+def test_2d_group_scope_equals_per_tensor_on_each_group():
+    w = weights(96, 64, seed=9)
+    p, S, pT, ST, t = nvfp4.quantize_2d(w, scope_rows=32)
+    for gi in range(3):
+        pg, Sg, _, _, tg = nvfp4.quantize_2d(w[gi * 32:(gi + 1) * 32])
+        assert np.array_equal(p[gi * 32:(gi + 1) * 32], pg) and np.array_equal(S[gi * 32:(gi + 1) * 32], Sg)
+        assert t.view(np.uint32)[gi] == tg.view(np.uint32)[0]

@@ -57,6 +57,7 @@ KERNEL_SOURCES = ["microscaling_precision_quantization_amd/csrc/gemm_exact.hip",
 MX_ROWCOL = 2 + 1 + 1 + 2 / 32          # BF16 read + two E4M3 copies + two E8M0 scale sets
 NV_TOKEN = 2 + 0.5 + 1 / 16             # BF16 read + packed E2M1 + E4M3 per 16 (+ 4 B per row)
 NV_TENSOR = 2 + NV_TOKEN                # + the amax pass over the BF16 input
+NV_2D_BOTH = 2 + 2 + 2 * (0.5 + 1 / 16)  # 16x16 blocks: amax pass + quantize pass, row + transposed copies
 
 
 def source_hash(paths=KERNEL_SOURCES) -> str:
@@ -222,10 +223,13 @@ class MoeQwen3:
                 Stage("combine", m.combine, T * k * H * 4 + T * H * 4 + T * k * 12, "hbm")]
 
     def extra_components(self):
-        """Expert-weight quantization (two passes over the BF16 weights), outside the step."""
+        """Expert-weight quantization (two passes over the BF16 weights), outside the step:
+        1x16 blocks, and 16x16 blocks with the row and the transposed copy."""
         n_el = self.w_gu.numel() + self.w_d.numel()
         return [Stage("quantize_nvfp4_expert_weights", lambda: self.moe.quantize_weights(self.w_gu, self.w_d),
-                      n_el * NV_TENSOR, "hbm")]
+                      n_el * NV_TENSOR, "hbm"),
+                Stage("quantize_nvfp4_2d_expert_weights", lambda: self.moe.quantize_weights_2d(self.w_gu, self.w_d),
+                      n_el * NV_2D_BOTH, "hbm")]
 
     def cpu_baseline(self):
         from oracle import moe as omoe
@@ -313,6 +317,11 @@ class MoeDeepseek:
               Stage("shared_expert_bf16", lambda: sh.backward(self.x, d["w_sgu"], d["w_sd"], d["d_os"], d["d_gus"]),
                     self.sfl["bwd"], "mfma", "bf16")]
         return st
+
+    def extra_components(self):
+        n_el = self.d["w_gu"].numel() + self.d["w_d"].numel()
+        return [Stage("quantize_nvfp4_2d_expert_weights",
+                      lambda: self.moe.quantize_weights_2d(self.d["w_gu"], self.d["w_d"]), n_el * NV_2D_BOTH, "hbm")]
 
     def cpu_baseline(self):
         from oracle import nvfp4 as onv

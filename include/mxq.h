@@ -177,6 +177,40 @@ mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_nvfp4_2d -- NVFP4 for weights with one E4M3 scale per 16x16 block
+ * (plus the FP32 scope scale), so that the forward pass and the transposed
+ * backward pass consume the same quantized weight.
+ *   Defined by: 2D block scaling of the weights -- 1x16 blocks along the dot
+ *   product would give the forward and the transposed backward different
+ *   quantized weights; 16x16 blocks make both use one representation, while
+ *   activations and gradients keep 1x16 blocks (7minutos.es, section "La
+ *   metodologia de formacion de cuatro partes").
+ *   Arithmetic: as quantize_nvfp4 with the block amax taken over each 16x16
+ *   block: A = scope amax; s_enc = 2688 / A (1 if A = 0, FLT_MAX on overflow);
+ *   t = 1 / s_enc; S = RNE_sat_E4M3((a_b / 6) * s_enc); r = min(s_enc / S,
+ *   FLT_MAX) (0 if S = 0); q = RNE_sat_E2M1(x * r). Two passes over x.
+ *
+ *   x      : BF16 (rows, cols), row stride ld_x; rows % 16 == cols % 16 == 0,
+ *            cols <= 16384.
+ *   scope  : TENSOR, or GROUP (group_rows consecutive rows = one expert matrix,
+ *            group_rows % 16 == 0).
+ *   q_row, s_row   : packed (rows, cols/2) and E4M3 (rows, cols/16) -- the 1x16
+ *                    form a K-contiguous GEMM reads (each 16x16 block's code
+ *                    repeated on its 16 rows); both NULL = skip.
+ *   q_colT, s_colT : the transposed weight of each scope group in the same form,
+ *                    (groups, cols, group_rows/2) and (groups, cols, group_rows/16)
+ *                    (TENSOR: (cols, rows/2), (cols, rows/16)), holding the
+ *                    identical codes -- the stacked per-expert layout the grouped
+ *                    GEMM reads for dgrad; both NULL = skip.
+ *   t      : FP32 decode scale per scope; workspace: mxq_workspace_bytes(
+ *            MXQ_OP_QUANTIZE_NVFP4, rows, cols, scopes) bytes.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_nvfp4_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             mxq_scope scope, int64_t group_rows,
+                             void* q_row, void* s_row, void* q_colT, void* s_colT, float* t,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dequantize -- reconstruct BF16 or FP32 values from MXFP8 or NVFP4 data, e.g.
  * the BF16 operands of the dequantized-backward GEMMs.
  *   Defined by: the dequantized-backward mode, whose backward GEMMs run in BF16 on

@@ -33,6 +33,8 @@ _SIGS = {
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
+    "quantize_nvfp4_2d": [_c_void_p, _i64, _i64, _i64, _int, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _c_void_p, _c_void_p, _size, _c_void_p],
     "dequantize": [_int, _c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _i64, _c_void_p, _int, _c_void_p],
     "dequantize_transposed": [_int, _c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _i64, _c_void_p, _i64,
                               _c_void_p, _i64, _c_void_p],
@@ -183,6 +185,32 @@ def quantize_nvfp4(x: torch.Tensor, scope: str = "tensor", group_rows: int = 0, 
                                                   signs, _ptr(q), _ptr(s), _ptr(t), _ptr(workspace),
                                                   workspace.numel() if workspace is not None else 0, _stream(dev)))
     return q, s, t
+
+
+def quantize_nvfp4_2d(x: torch.Tensor, scope: str = "tensor", group_rows: int = 0, rowwise: bool = True,
+                      colwise: bool = True, out=None, workspace: torch.Tensor | None = None):
+    """NVFP4 with 16x16 block scales: (q_row, s_row, q_colT, s_colT, t); skipped copies are None.
+    The transposed copy is per scope group: (groups * cols, group_rows / 2)."""
+    _bf16(x)
+    R, C = x.shape
+    dev = x.device
+    n_scopes = 1 if scope == "tensor" else (R // group_rows if group_rows else 0)
+    if out is not None:
+        q_row, s_row, q_col, s_col, t = out
+    else:
+        q_row = _u8((R, C // 2), dev) if rowwise else None
+        s_row = _u8((R, C // 16), dev) if rowwise else None
+        gr = R if scope == "tensor" else group_rows
+        q_col = _u8((max(n_scopes, 1) * C, gr // 2), dev) if colwise else None
+        s_col = _u8((max(n_scopes, 1) * C, gr // 16), dev) if colwise else None
+        t = torch.empty(max(n_scopes, 1), dtype=torch.float32, device=dev)
+    ws_bytes = lib().mxq_workspace_bytes(OP_QUANTIZE_NVFP4, R, C, n_scopes)
+    if workspace is None:
+        workspace = _u8((max(ws_bytes, 4),), dev)
+    _check("quantize_nvfp4_2d", lib().quantize_nvfp4_2d(_ptr(x), R, C, x.stride(0), SCOPE[scope], group_rows,
+                                                        _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
+                                                        _ptr(t), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return q_row, s_row, q_col, s_col, t
 
 
 def dequantize(fmt: int, q: torch.Tensor, s: torch.Tensor, t: torch.Tensor | None = None, t_scope: str = "row",

@@ -14,6 +14,8 @@ hipError_t launch_quant_mxfp8_multi(int, const void* const*, const int64_t*, con
 hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
 hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
                               float*, uint32_t*, int64_t, hipStream_t);
+hipError_t launch_quant_nvfp4_2d(const void*, int64_t, int64_t, int64_t, int64_t, void*, void*, void*, void*, float*,
+                                 uint32_t*, int64_t, hipStream_t);
 hipError_t launch_dequant(int, const void*, const void*, const float*, int, int64_t, int64_t, int64_t, void*, int,
                           hipStream_t);
 hipError_t launch_dequant_t(int, const void*, const void*, const float*, int, int64_t, int64_t, int64_t,
@@ -179,6 +181,28 @@ mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
   return hip_status(mxq::launch_quant_nvfp4(x, rows, cols, ld_x, (int)scope, group_rows, transpose,
                                             rht_signs16 != nullptr, neg_mask, q, s, t, (uint32_t*)workspace,
                                             n_scopes, S(stream)));
+}
+
+mxq_status quantize_nvfp4_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,
+                             int64_t group_rows, void* q_row, void* s_row, void* q_colT, void* s_colT, float* t,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  const bool do_row = q_row || s_row, do_col = q_colT || s_colT;
+  if (!x || !t || (!do_row && !do_col)) return MXQ_ERR_NULL;
+  if ((do_row && (!q_row || !s_row)) || (do_col && (!q_colT || !s_colT))) return MXQ_ERR_NULL;
+  if (scope != MXQ_SCOPE_TENSOR && scope != MXQ_SCOPE_GROUP) return MXQ_ERR_FORMAT;
+  if (rows % 16 || cols % 16 || cols > kMaxRowCols || ld_x < cols) return MXQ_ERR_SHAPE;
+  const int64_t gr = scope == MXQ_SCOPE_TENSOR ? rows : group_rows;
+  if (scope == MXQ_SCOPE_GROUP && (group_rows <= 0 || group_rows % 16 || rows % group_rows)) return MXQ_ERR_SHAPE;
+  if (ld_x % 8 || !al16(x) || !al4(t) || (do_row && !al4(q_row)) || (do_col && !al16(q_colT))) return MXQ_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  const int64_t n_scopes = rows / gr;
+  if (!workspace || workspace_bytes < (size_t)(n_scopes * 4)) return MXQ_ERR_WORKSPACE;
+  if (!al4(workspace)) return MXQ_ERR_ALIGN;
+  if ((rows + 255) / 256 * ((cols + 127) / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_quant_nvfp4_2d(x, rows, cols, ld_x, gr, do_row ? q_row : nullptr, s_row,
+                                               do_col ? q_colT : nullptr, s_colT, t, (uint32_t*)workspace, n_scopes,
+                                               S(stream)));
 }
 
 mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float* t, mxq_scope t_scope,

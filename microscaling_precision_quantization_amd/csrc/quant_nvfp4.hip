@@ -320,6 +320,140 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2D (16x16-block) NVFP4 for weights: one E4M3 scale per 16x16 block, so the
+// forward (rows along K) and the transposed backward use the same codes
+// (7minutos.es NVFP4 page, section "La metodologia de formacion de cuatro
+// partes", 2D weight scaling). Pass 2 of a two-pass quantizer: the scope amax
+// (tensor or group of rows) comes from scope_amax. Tile as nvfp4_cols_kernel:
+// 256 rows x 128 columns per workgroup, lane = 16*m + c16 holding rows
+// 16m .. 16m+15 of its wave's 64-row slab and columns 8*c16 .. 8*c16+7; a 16x16
+// block is the lane pair (c16, c16 ^ 1). Writes the row copy (rows, cols/2) with
+// its scales repeated per row (rows, cols/16), and/or the transposed copy
+// per scope group (groups, cols, group_rows/2) with (groups, cols, group_rows/16),
+// both staged through LDS where rows of the output are short.
+// ---------------------------------------------------------------------------
+template <bool DO_ROW, bool DO_COL>
+__global__ void __launch_bounds__(256)
+nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
+                const uint32_t* __restrict__ scope_amax, uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT, int64_t col_tiles, int wide_col,
+                int dw_row) {
+  __shared__ __attribute__((aligned(16))) uint8_t lq[DO_COL ? 128 * 128 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[DO_COL ? 128 * 16 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lsr[DO_ROW ? 256 * 8 : 16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane >> 4, c16 = lane & 15;
+  const int64_t band = (int64_t)blockIdx.x / col_tiles, ct = (int64_t)blockIdx.x % col_tiles;
+  const int64_t R0 = band * 256, C0 = ct * 128;
+  const int rl0 = 64 * w + 16 * m;                  // tile row of the lane's first row
+  const int64_t r0 = R0 + rl0;
+  const int64_t c = C0 + 8 * c16;
+  const bool ok = c < cols && r0 < rows;            // cols % 16 == 0, rows % 16 == 0: whole blocks
+  uint4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    v[j] = ok ? *reinterpret_cast<const uint4*>(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
+  float s_enc = 1.0f;
+  if (ok) {
+    float tt;
+    scope_scales(__uint_as_float(scope_amax[r0 / group_rows]), s_enc, tt);   // 16 rows, one scope
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    am = pk_max_u16(am, pk_max_u16(pk_max_u16(v[j].x & 0x7FFF7FFFu, v[j].y & 0x7FFF7FFFu),
+                                   pk_max_u16(v[j].z & 0x7FFF7FFFu, v[j].w & 0x7FFF7FFFu)));
+  am = max_halves(am);
+  const uint32_t other = dpp_xor1(am);
+  am = am > other ? am : other;                     // 16x16 block amax (BF16 bits, exact)
+  float r;
+  const uint32_t code = block_scale(__uint_as_float(am << 16), s_enc, r);
+
+  if (DO_ROW) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float f[8];
+      unpack8(v[j], f);
+      const uint32_t packed = pack8_e2m1(f, r);
+      if (ok) *reinterpret_cast<uint32_t*>(q_row + (r0 + j) * (cols / 2) + c / 2) = packed;
+    }
+    if ((c16 & 1) == 0)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) lsr[(rl0 + j) * 8 + (c16 >> 1)] = (uint8_t)code;
+  }
+  if (DO_COL) {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      float f[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t wd = (cc >> 1) == 0 ? v[j].x : (cc >> 1) == 1 ? v[j].y : (cc >> 1) == 2 ? v[j].z : v[j].w;
+        f[j] = (cc & 1) ? bf16_hi(wd) : bf16_lo(wd);
+      }
+      const uint32_t lo = pack8_e2m1(f, r), hi = pack8_e2m1(f + 8, r);
+      const int cl = 8 * c16 + cc;
+      const int g = (4 * w + m) ^ ((c16 & 3) * 4);
+      *reinterpret_cast<uint2*>(lq + cl * 128 + g * 8) = make_uint2(lo, hi);
+      lsc[cl * 16 + 4 * w + m] = (uint8_t)code;
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (DO_ROW && R0 + t < rows) {
+    const int64_t sb = cols / 16;
+    const int64_t nb = min((int64_t)8, sb - ct * 8);
+    uint8_t* dst = s_row + (R0 + t) * sb + ct * 8;
+    const uint2 d = *reinterpret_cast<const uint2*>(lsr + t * 8);
+    if (dw_row && nb == 8) {
+      *reinterpret_cast<uint2*>(dst) = d;
+    } else {
+      const uint32_t wv[2] = {d.x, d.y};
+      for (int b = 0; b < nb; ++b) dst[b] = (uint8_t)(wv[b / 4] >> (8 * (b % 4)));
+    }
+  }
+  if (DO_COL) {
+    // transposed copy per scope group: (groups, cols, group_rows / 2) and (groups, cols, group_rows / 16)
+    const int64_t rb = group_rows / 2, sb = group_rows / 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = k * 256 + t;
+      const int cl = i >> 3, ch = i & 7;
+      const int64_t col = C0 + cl, rr = R0 + 32 * ch;
+      if (col >= cols || rr >= rows) continue;
+      const int g0 = (2 * ch) ^ (((cl >> 3) & 3) * 4);
+      const uint4 d = *reinterpret_cast<const uint4*>(lq + cl * 128 + g0 * 8);
+      const int64_t gi = rr / group_rows, rl = rr - gi * group_rows;
+      uint8_t* dst = q_colT + (gi * cols + col) * rb + rl / 2;
+      if (wide_col) {                                 // group_rows % 32 == 0: whole aligned chunks
+        *reinterpret_cast<uint4*>(dst) = d;
+      } else {                                        // 16-row granules, each inside one group
+        *reinterpret_cast<uint2*>(dst) = make_uint2(d.x, d.y);
+        const int64_t r2 = rr + 16;
+        if (r2 < rows) {
+          const int64_t g2 = r2 / group_rows, rl2 = r2 - g2 * group_rows;
+          *reinterpret_cast<uint2*>(q_colT + (g2 * cols + col) * rb + rl2 / 2) = make_uint2(d.z, d.w);
+        }
+      }
+    }
+    if (t < 128 && C0 + t < cols) {
+      const uint4 d = *reinterpret_cast<const uint4*>(lsc + t * 16);
+      const int64_t gi = R0 / group_rows, rl = R0 - gi * group_rows;
+      if (wide_col && group_rows % 256 == 0 && R0 + 256 <= rows) {   // 16 blocks of one group, aligned
+        *reinterpret_cast<uint4*>(s_colT + (gi * cols + C0 + t) * sb + rl / 16) = d;
+      } else {
+        const uint32_t wv[4] = {d.x, d.y, d.z, d.w};
+        for (int b = 0; b < 16; ++b) {
+          const int64_t r = R0 + 16 * b;
+          if (r >= rows) break;
+          const int64_t g2 = r / group_rows, rl2 = r - g2 * group_rows;
+          s_colT[(g2 * cols + C0 + t) * sb + rl2 / 16] = (uint8_t)(wv[b / 4] >> (8 * (b % 4)));
+        }
+      }
+    }
+  }
+}
+
 // t[g] = decode scale of scope g, from the amax in the workspace.
 __global__ void nvfp4_scope_t_kernel(const uint32_t* __restrict__ scope_amax, float* __restrict__ t, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -361,6 +495,29 @@ static void launch_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                      col_tiles, wide);
 }
 
+
+// 2D weights: scope amax pass (rows kernel, MODE 2), then the 16x16-block pass.
+hipError_t launch_quant_nvfp4_2d(const void* xv, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
+                                 void* q_row, void* s_row, void* q_colT, void* s_colT, float* t, uint32_t* ws_amax,
+                                 int64_t n_scopes, hipStream_t st) {
+  const uint16_t* x = (const uint16_t*)xv;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, 0u, n_scopes);
+  launch_rows<2, false>(x, rows, cols, ld_x, group_rows, 0u, ws_amax, nullptr, nullptr, nullptr, st);
+  const int64_t col_tiles = (cols + 127) / 128;
+  const int64_t bands = (rows + 255) / 256;
+  uint8_t *qr = (uint8_t*)q_row, *sr = (uint8_t*)s_row, *qc = (uint8_t*)q_colT, *sc = (uint8_t*)s_colT;
+  const int wide = qc && group_rows % 32 == 0 && ((uintptr_t)qc & 15) == 0 && ((uintptr_t)sc & 15) == 0;
+  const int dw_row = sr && (cols / 16) % 8 == 0 && ((uintptr_t)sr & 7) == 0;
+  dim3 grid((unsigned)(bands * col_tiles)), block(256);
+  if (qr && qc)
+    hipLaunchKernelGGL((nvfp4_2d_kernel<true, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+  else if (qr)
+    hipLaunchKernelGGL((nvfp4_2d_kernel<true, false>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+  else
+    hipLaunchKernelGGL((nvfp4_2d_kernel<false, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+  hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_nvfp4_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x,
                                     void* q, void* s, float* t, hipStream_t st) {

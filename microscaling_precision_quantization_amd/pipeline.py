@@ -122,6 +122,21 @@ class MoeNvfp4:
                 B._ptr(s), B._ptr(t), B._ptr(self.wq_ws), self.wq_ws.numel(), B._stream(dev)))
         return self.wq
 
+    def quantize_weights_2d(self, w_gu, w_d):
+        """Expert weights with 16x16 block scales (row and transposed copies hold the same
+        codes: the forward and the dgrad of one quantized weight)."""
+        G, H, I, dev = self.G, self.H, self.I, self.dev
+        if getattr(self, "wq2d", None) is None:
+            # row copies (G*N, K) and per-expert transposed copies (G*K, N) of W_gu and W_d
+            self.wq2d = {"gu": (_u8((G * 2 * I, H // 2), dev), _u8((G * 2 * I, H // 16), dev),
+                                _u8((G * H, 2 * I // 2), dev), _u8((G * H, 2 * I // 16), dev), _f32((G,), dev)),
+                         "d": (_u8((G * H, I // 2), dev), _u8((G * H, I // 16), dev),
+                               _u8((G * I, H // 2), dev), _u8((G * I, H // 16), dev), _f32((G,), dev))}
+            self.wq2d_ws = _u8((B.lib().mxq_workspace_bytes(B.OP_QUANTIZE_NVFP4, 0, 0, G),), dev)
+        for key, w, gr in (("gu", w_gu, 2 * I), ("d", w_d, H)):
+            B.quantize_nvfp4_2d(w, scope="group", group_rows=gr, out=self.wq2d[key], workspace=self.wq2d_ws)
+        return self.wq2d
+
     def quantize_tokens(self, x):                                  # A3
         B._check("quantize_nvfp4_per_token", B.lib().quantize_nvfp4_per_token(
             B._ptr(x), self.T, self.H, x.stride(0), B._ptr(self.qx), B._ptr(self.sx), B._ptr(self.tx),

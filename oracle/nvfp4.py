@@ -144,10 +144,11 @@ def quantize_2d(x: np.ndarray, scope_rows: int | None = None):
     r_b = min(fl(s_enc / S_b), FLT_MAX) (0 if S_b = 0); q = E2M1_RNE_sat(fl(x * r_b)).
 
     x: (R, C), float32 or BF16 bits, R % 16 == C % 16 == 0.
-    Returns (packed (R, C/2), S_rows (R, C/16), packedT (C, R/2), S_T (C, R/16),
-    t (groups,)). S_rows repeats each 16x16 block's code for its 16 rows (the
-    1x16 form a K-contiguous GEMM consumes); packedT / S_T are the transposed
-    tensor in the same form, holding the identical codes.
+    Returns (packed (R, C/2), S_rows (R, C/16), packedT (G*C, gr/2), S_T
+    (G*C, gr/16), t (G,)) with G = R / gr scope groups. S_rows repeats each 16x16
+    block's code for its 16 rows (the 1x16 form a K-contiguous GEMM consumes);
+    packedT / S_T hold, group after group, the transpose of each group's rows in
+    the same form (for one group: the transposed tensor), with identical codes.
     """
     x = bf16_bits_to_f32(x) if x.dtype == np.uint16 else np.asarray(x, dtype=f32)
     R, C = x.shape
@@ -173,10 +174,11 @@ def quantize_2d(x: np.ndarray, scope_rows: int | None = None):
     prod = (xb * r_b[:, None, :, None]).astype(f32)                # rounded to FP32 first
     q = encode_e2m1(prod.astype(np.float64)).reshape(R, C)
     pack = lambda codes: (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    qT = np.ascontiguousarray(q.T)
     S_rows = np.repeat(S, BLOCK, axis=0)                            # (R, C/16)
-    S_T = np.ascontiguousarray(np.repeat(S.T, BLOCK, axis=0))      # (C, R/16)
-    return pack(q), S_rows, pack(qT), S_T, t.astype(f32)
+    # transposed copy per scope group (one expert matrix each): (G, C, gr) stacked as (G*C, gr)
+    qT = np.concatenate([q[g * gr:(g + 1) * gr].T for g in range(G)], axis=0)
+    S_T = np.concatenate([np.repeat(S[g * gr // BLOCK:(g + 1) * gr // BLOCK].T, BLOCK, axis=0) for g in range(G)], axis=0)
+    return pack(q), S_rows, pack(np.ascontiguousarray(qT)), np.ascontiguousarray(S_T), t.astype(f32)
 
 
 def unpack_codes(packed: np.ndarray) -> np.ndarray:

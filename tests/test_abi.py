@@ -81,6 +81,19 @@ def test_nvfp4_validation():
     assert L.quantize_nvfp4(P, 32, 32, 32, 9, 0, 0, None, P, P, P, P, 256, None) == 4   # bad scope
 
 
+def test_quantize_nvfp4_2d_validation():
+    q2 = B.lib().quantize_nvfp4_2d
+    assert q2(P, 32, 40, 40, 1, 0, P, P, None, None, P, P, 256, None) == 2     # cols % 16
+    assert q2(P, 24, 32, 32, 1, 0, P, P, None, None, P, P, 256, None) == 2     # rows % 16
+    assert q2(P, 32, 32, 32, 0, 0, P, P, None, None, P, P, 256, None) == 4     # ROW scope
+    assert q2(P, 64, 32, 32, 2, 24, P, P, None, None, P, P, 256, None) == 2    # group rows % 16
+    assert q2(P, 32, 32, 32, 1, 0, None, None, None, None, P, P, 256, None) == 1
+    assert q2(P, 32, 32, 32, 1, 0, P, None, None, None, P, P, 256, None) == 1  # half a pair
+    assert q2(P, 32, 32, 32, 1, 0, P, P, None, None, P, None, 0, None) == 5    # no workspace
+    assert q2(P, 32, 32, 32, 1, 0, P, P, MIS, P, P, P, 256, None) == 3
+    assert q2(P, 0, 32, 32, 1, 0, P, P, None, None, P, None, 0, None) == 0     # empty
+
+
 def test_gemm_validation():
     L = B.lib()
     g = L.gemm_block_scaled

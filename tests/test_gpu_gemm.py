@@ -127,6 +127,25 @@ def test_nvfp4_wgrad_with_rht_small():
     assert_gemm_close(host(c), og.gemm_tn_fp64(ah, bh), "rht wgrad")
 
 
+def test_nvfp4_2d_weight_fprop_and_dgrad():
+    """The one 2D-quantized weight serves fprop (row form) and dgrad (transposed form)."""
+    g = inputs.rng(97, 0)
+    T, N, K = 320, 384, 512
+    x = inputs.to_bf16_bits(g.standard_normal((T, K)) * g.lognormal(0, 1, (T, 1)))
+    dy = inputs.normal_bf16(g, (T, N), 1e-3)
+    w = inputs.normal_bf16(g, (N, K), 0.02)
+    qw, sw, qwt, swt, tw = mxq.quantize_nvfp4_2d(dev_bf16(w))
+    qx, sx, tx, xh = nv_token(x)
+    y = mxq.gemm_block_scaled(mxq.NVFP4, qx, sx, qw, sw, tA=tx, tB=tw, tA_scope="row", tB_scope="tensor")
+    wh = onv.dequantize_exact(host(qw), host(sw), np.repeat(host(tw), N))
+    assert_gemm_close(host(y), og.gemm_tn_fp64(xh, wh), "2d fprop")
+    qd, sd, td, dh = nv_token(dy)
+    dx = mxq.gemm_block_scaled(mxq.NVFP4, qd, sd, qwt, swt, tA=td, tB=tw, tA_scope="row", tB_scope="tensor")
+    wth = onv.dequantize_exact(host(qwt), host(swt), np.repeat(host(tw), K))
+    assert np.array_equal(wth, wh.T)                      # the same weight values in both passes
+    assert_gemm_close(host(dx), og.gemm_tn_fp64(dh, wth), "2d dgrad")
+
+
 @pytest.mark.parametrize("mnk", [(300, 200, 96), (128, 256, 1024)])
 def test_bf16_gemm_dense(mnk):
     M, N, K = mnk
@@ -192,6 +211,31 @@ def test_grouped_nvfp4_gather_vary_m():
         lo, hi = r.offsets[e], r.offsets[e + 1]
         if hi > lo:
             assert_gemm_close(ch[lo:hi], ref[lo:hi], f"expert {e}")
+
+
+def test_grouped_nvfp4_dgrad_on_2d_expert_weights():
+    """2D-scaled expert weights give an NVFP4 dgrad: per expert dX_g = dGU_g W_g with the
+    per-expert transposed copy (G, K, N) as the stacked B operand."""
+    x, r, _ = small_moe(seed=3)
+    G, N, K = 8, 192, 256
+    g = inputs.rng(85, 30)
+    w = inputs.normal_bf16(g, (G * N, K), 0.02)
+    S = int(r.offsets[-1])
+    dgu = inputs.to_bf16_bits(g.standard_normal((S, N)) * 1e-3 * g.lognormal(0, 1, (S, 1)))
+    qw, sw, qwt, swt, tw = mxq.quantize_nvfp4_2d(dev_bf16(w), scope="group", group_rows=N)
+    qd, sd, td = mxq.quantize_nvfp4_per_token(dev_bf16(dgu))
+    dx = mxq.grouped_gemm_block_scaled(mxq.NVFP4, dev(r.offsets.astype(np.int64)), qd, qwt, N=K, K=N, sA=sd, sB=swt,
+                                       tA=td, tB=tw, tA_scope="row", tB_scope="group")
+    ah = onv.dequantize_exact(host(qd), host(sd), host(td))
+    wt = onv.dequantize_exact(host(qwt), host(swt), np.repeat(host(tw), K)).reshape(G, K, N)
+    wr = onv.dequantize_exact(host(qw), host(sw), np.repeat(host(tw), N)).reshape(G, N, K)
+    assert np.array_equal(wt, wr.transpose(0, 2, 1))          # fprop and dgrad read one weight
+    ref = omoe.grouped_gemm_ref(ah, r.offsets, wt)
+    ch = host(dx)
+    for e in range(G):
+        lo, hi = r.offsets[e], r.offsets[e + 1]
+        if hi > lo:
+            assert_gemm_close(ch[lo:hi], ref[lo:hi], f"2d dgrad expert {e}")
 
 
 def test_grouped_mxfp8_vary_m_contiguous():

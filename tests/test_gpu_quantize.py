@@ -269,6 +269,27 @@ def test_nvfp4_stress_rht_full_size_sampled():
     assert_bytes_equal(s[cols], es, "sampled RHT scales")
 
 
+@pytest.mark.parametrize("shape,group", [((96, 160), None), ((256, 512), 64), ((272, 48), None), ((512, 2048), 256),
+                                         ((1024, 7168), 512), ((144, 64), 48), ((64, 96), 16), ((768, 256), 256)])
+def test_nvfp4_2d_weights(shape, group):
+    g = inputs.rng(96, shape[0] + shape[1])
+    wb = inputs.to_bf16_bits(g.standard_normal(shape) * 0.02 * g.lognormal(0, 1, (shape[0], 1)))
+    scope = "tensor" if group is None else "group"
+    q, s, qt, st, t = mxq.quantize_nvfp4_2d(dev_bf16(wb), scope=scope, group_rows=group or 0)
+    eq, es, eqt, est, et = onv.quantize_2d(wb, scope_rows=group)
+    assert_bytes_equal(host(q), eq, "2d packed")
+    assert_bytes_equal(host(s), es, "2d scales")
+    assert_bytes_equal(host(qt), eqt, "2d transposed packed")
+    assert_bytes_equal(host(st), est, "2d transposed scales")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "2d t")
+    # one copy at a time writes the same bytes
+    q1, s1, _, _, _ = mxq.quantize_nvfp4_2d(dev_bf16(wb), scope=scope, group_rows=group or 0, colwise=False)
+    _, _, qt1, st1, _ = mxq.quantize_nvfp4_2d(dev_bf16(wb), scope=scope, group_rows=group or 0, rowwise=False)
+    assert_bytes_equal(host(q1), eq, "2d row only")
+    assert_bytes_equal(host(qt1), eqt, "2d col only")
+    assert_bytes_equal(host(st1), est, "2d col only scales")
+
+
 # ------------------------------ dequantize ---------------------------------
 
 def test_dequantize_mxfp8_and_nvfp4():

@@ -295,6 +295,7 @@ def test_2d_group_scope_equals_per_tensor_on_each_group():
     w = weights(96, 64, seed=9)
     p, S, pT, ST, t = nvfp4.quantize_2d(w, scope_rows=32)
     for gi in range(3):
-        pg, Sg, _, _, tg = nvfp4.quantize_2d(w[gi * 32:(gi + 1) * 32])
+        pg, Sg, pTg, STg, tg = nvfp4.quantize_2d(w[gi * 32:(gi + 1) * 32])
         assert np.array_equal(p[gi * 32:(gi + 1) * 32], pg) and np.array_equal(S[gi * 32:(gi + 1) * 32], Sg)
+        assert np.array_equal(pT[gi * 64:(gi + 1) * 64], pTg) and np.array_equal(ST[gi * 64:(gi + 1) * 64], STg)
         assert t.view(np.uint32)[gi] == tg.view(np.uint32)[0]

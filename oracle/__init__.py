@@ -28,4 +28,4 @@ docstring. Present ones:
   * the NVFP4 FP32 operation order and the choice to store the decode scale.
 """
 
-from . import formats, mxfp8, nvfp4, gemm, moe  # noqa: F401
+from . import formats, mxfp8, nvfp4, gemm, moe, rng  # noqa: F401

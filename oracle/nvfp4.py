@@ -44,6 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import rng
 from .formats import (E2M1_MAX, E4M3_MAX, FLT_MAX, bf16_bits_to_f32,
                       decode_e2m1, decode_e4m3, encode_e2m1, encode_e4m3,
                       f32_to_bf16_bits)
@@ -63,12 +64,45 @@ def scope_scales(amax_scope) -> tuple[np.ndarray, np.ndarray]:
     return s_enc, t
 
 
-def quantize_with_scope_amax(x: np.ndarray, amax_rows: np.ndarray):
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_stochastic(v: np.ndarray, words: np.ndarray) -> np.ndarray:
+    """Stochastic rounding of FP32 values onto the E2M1 grid: each value rounds to
+    one of its two nearest representable neighbours with probability set by its
+    distance to them, which removes the bias round-to-nearest-even introduces
+    (7minutos.es NVFP4 page, section "La metodologia de formacion de cuatro
+    partes", stochastic-rounding item: gradients only).
+
+    Reading (the page gives no procedure): m = |v|; lo = the largest grid magnitude
+    <= m, hi the next one (m >= 6 saturates to 6), d = hi - lo; f = (m - lo) / d,
+    exact; round up iff (word >> 8) < f * 2^24, i.e. with probability f for a
+    uniform 32-bit word. The sign is copied (-0 keeps it). Returns E2M1 codes.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    m = np.abs(v).astype(np.float64)
+    sat = m >= 6.0
+    lo_i = np.searchsorted(E2M1_GRID, np.minimum(m, 6.0), side="right") - 1     # index of lo
+    lo = E2M1_GRID[lo_i]
+    hi = E2M1_GRID[np.minimum(lo_i + 1, 7)]
+    d = np.where(sat, 1.0, hi - lo)
+    f = np.where(sat, 0.0, (m - lo) / d)                                         # exact
+    u = (np.asarray(words, dtype=np.uint32) >> np.uint32(8)).astype(np.float64)
+    up = u < f * 2.0 ** 24
+    code = np.where(up, lo_i + 1, lo_i).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 3)
+
+
+def quantize_with_scope_amax(x: np.ndarray, amax_rows: np.ndarray, sr_seed: int | None = None):
     """Core NVFP4 quantizer.
 
     x: float32 (R, C), C % 16 == 0; amax_rows: float32 (R,) -- the scope amax
     that applies to each row (the row's own max for per-token scaling, the
     tensor's max broadcast for per-tensor scaling).
+    sr_seed: None for round-to-nearest-even elements; else the elements are
+    rounded stochastically with the random word of element (r, c) taken from
+    rng.element_words(sr_seed, r * C + c) (its index in the (R, C) output). The
+    block and scope scales are the same either way.
     Returns (packed uint8 (R, C/2), S uint8 (R, C/16) E4M3 codes, t float32 (R,)).
     """
     x = np.asarray(x, dtype=f32)
@@ -87,23 +121,27 @@ def quantize_with_scope_amax(x: np.ndarray, amax_rows: np.ndarray):
         r_b = (s_enc[:, None] / S_val).astype(f32)
     r_b = np.where(S_val == 0, f32(0.0), np.minimum(r_b, f32(FLT_MAX))).astype(f32)
     prod = (xb * r_b[:, :, None]).astype(f32)                 # rounded to FP32 first
-    q = encode_e2m1(prod.astype(np.float64)).reshape(R, C)
+    if sr_seed is None:
+        q = encode_e2m1(prod.astype(np.float64)).reshape(R, C)
+    else:
+        words = rng.element_words(sr_seed, np.arange(R * C, dtype=np.uint64)).reshape(R, C)
+        q = e2m1_stochastic(prod.reshape(R, C), words)
     packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     return packed, S, t
 
 
-def quantize_per_token(x_bf16_bits: np.ndarray):
+def quantize_per_token(x_bf16_bits: np.ndarray, sr_seed: int | None = None):
     """Per-token NVFP4: the FP32 scale's scope is one row (token) of x (T, H)."""
     x = bf16_bits_to_f32(x_bf16_bits)
     amax = np.max(np.abs(x), axis=1).astype(f32)
-    return quantize_with_scope_amax(x, amax)
+    return quantize_with_scope_amax(x, amax, sr_seed)
 
 
-def quantize_per_tensor(x: np.ndarray):
+def quantize_per_tensor(x: np.ndarray, sr_seed: int | None = None):
     """Per-tensor NVFP4 over a float32 or BF16-bits (R, C) tensor; t is a scalar."""
     x = bf16_bits_to_f32(x) if x.dtype == np.uint16 else np.asarray(x, dtype=f32)
     A = f32(np.max(np.abs(x))) if x.size else f32(0.0)
-    packed, S, _ = quantize_with_scope_amax(x, np.full(x.shape[0], A, dtype=f32))
+    packed, S, _ = quantize_with_scope_amax(x, np.full(x.shape[0], A, dtype=f32), sr_seed)
     return packed, S, scope_scales(np.array([A], dtype=f32))[1]
 
 
@@ -241,7 +279,7 @@ def rht16_rows(x: np.ndarray, signs) -> np.ndarray:
     return (w * f32(0.25)).astype(f32).reshape(R, C)
 
 
-def rht_quantize_colwise_per_tensor(x_bf16_bits: np.ndarray, signs):
+def rht_quantize_colwise_per_tensor(x_bf16_bits: np.ndarray, signs, sr_seed: int | None = None):
     """Weight-gradient operand: RHT along the rows of x (R, C) (the reduction
     axis of dW = dY^T X), then per-tensor NVFP4 with 1x16 blocks along that
     same axis, stored transposed as (C, R).
@@ -249,4 +287,4 @@ def rht_quantize_colwise_per_tensor(x_bf16_bits: np.ndarray, signs):
     """
     x = bf16_bits_to_f32(x_bf16_bits)
     u = rht16_rows(np.ascontiguousarray(x.T), signs)         # (C, R): chunks along R
-    return quantize_per_tensor(u)
+    return quantize_per_tensor(u, sr_seed)

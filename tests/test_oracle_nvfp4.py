@@ -299,3 +299,60 @@ def test_2d_group_scope_equals_per_tensor_on_each_group():
         assert np.array_equal(p[gi * 32:(gi + 1) * 32], pg) and np.array_equal(S[gi * 32:(gi + 1) * 32], Sg)
         assert np.array_equal(pT[gi * 64:(gi + 1) * 64], pTg) and np.array_equal(ST[gi * 64:(gi + 1) * 64], STg)
         assert t.view(np.uint32)[gi] == tg.view(np.uint32)[0]
+
+
+# ---------------------- stochastic rounding (gradients) ----------------------
+
+from oracle import rng  # noqa: E402
+
+
+def test_philox_known_answer_vectors():
+    for line in read_golden("philox4x32_10_kat.txt"):
+        v = [int(w, 16) for w in line.split()]
+        out = rng.philox4x32_10(np.array(v[:4], dtype=np.uint32), np.array(v[4:6], dtype=np.uint32))
+        assert [int(o) for o in out] == v[6:]
+
+
+def test_sr_threshold_is_exact_and_picks_a_neighbour():
+    # v = 1.125 lies a quarter of the way from 1 to 1.5: up iff (word >> 8) < 2^22
+    v = np.full(4, 1.125, dtype=np.float32)
+    w = np.array([0, (2 ** 22 - 1) << 8, 2 ** 22 << 8, 0xFFFFFFFF], dtype=np.uint32)
+    assert nvfp4.e2m1_stochastic(v, w).tolist() == [3, 3, 2, 2]          # 1.5, 1.5, 1, 1
+    # grid values never move, saturation at 6, sign kept
+    g = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -3, 7.5, -0.0], dtype=np.float32)
+    for word in (0, 0x80000000, 0xFFFFFFFF):
+        codes = nvfp4.e2m1_stochastic(g, np.full(g.shape, word, dtype=np.uint32))
+        assert codes.tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 13, 7, 8]
+    x = np.random.default_rng(0).uniform(-7, 7, 4096).astype(np.float32)
+    words = rng.element_words(5, np.arange(4096, dtype=np.uint64))
+    val = F.decode_e2m1(nvfp4.e2m1_stochastic(x, words))
+    m = np.minimum(np.abs(x), 6.0)
+    grid = nvfp4.E2M1_GRID
+    lo = grid[np.searchsorted(grid, m, side="right") - 1]
+    hi = grid[np.minimum(np.searchsorted(grid, m, side="right"), 7)]
+    assert np.all((np.abs(val) == lo) | (np.abs(val) == hi))
+
+
+def test_sr_is_unbiased():
+    # E[SR(v)] = v: the mean over many independent words converges to v (4 sigma bound)
+    n = 200000
+    words = rng.element_words(11, np.arange(n, dtype=np.uint64))
+    for v in (0.1, 0.7, 1.3, 2.25, 3.9, 5.0, -4.5):
+        vals = F.decode_e2m1(nvfp4.e2m1_stochastic(np.full(n, v, dtype=np.float32), words))
+        mean = vals.mean()
+        sd = vals.std() / np.sqrt(n)
+        assert abs(mean - np.float32(v)) < 4 * sd + 1e-12, (v, mean)
+
+
+def test_sr_quantizer_keeps_the_scales_and_moves_only_rounding():
+    x = tokens(32, 256, seed=12)
+    p0, S0, t0 = nvfp4.quantize_per_token(x)
+    p1, S1, t1 = nvfp4.quantize_per_token(x, sr_seed=1234)
+    assert np.array_equal(S0, S1) and np.array_equal(t0.view(np.uint32), t1.view(np.uint32))
+    c0, c1 = nvfp4.unpack_codes(p0), nvfp4.unpack_codes(p1)
+    assert not np.array_equal(c0, c1)
+    # every SR code is a grid neighbour of the RNE code (same sign, magnitude index within 1)
+    d = np.abs((c0 & 7).astype(int) - (c1 & 7).astype(int))
+    assert np.all(d <= 1)
+    p2, _, _ = nvfp4.quantize_per_token(x, sr_seed=1234)
+    assert np.array_equal(p1, p2)                                     # deterministic per seed

@@ -383,6 +383,12 @@ class Stress:
                 Stage("gemm_block_scaled_nvfp4", st.nvfp4_wgrad, 2 * n ** 3, "mfma", "fp16")]
         return out
 
+    def extra_components(self):
+        """Stochastically rounded RHT + NVFP4 of the gradient operand A (outside the step)."""
+        n = self.N
+        return [Stage("quantize_nvfp4_rht_colwise_sr", lambda: self.st.quantize_rht_sr(self.sets[0]["a"], 1234),
+                      n * n * (2 + 2 + 0.5 + 1 / 16), "hbm")]
+
     def cpu_baseline(self):
         from oracle import gemm as og
         from oracle import mxfp8 as omx

@@ -177,6 +177,27 @@ mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_nvfp4_stochastic -- quantize_nvfp4 with the E2M1 elements rounded
+ * stochastically (for gradient tensors); scales are computed exactly as there.
+ *   Defined by: stochastic rounding of gradients -- rounding probabilistically by
+ *   the distance to the two nearest representable values removes the bias of
+ *   round-to-nearest-even; it is applied to gradients only (7minutos.es, section
+ *   "La metodologia de formacion de cuatro partes").
+ *   Rounding of p = x * r: m = |p| lies between E2M1 neighbours lo < hi (m >= 6
+ *   gives 6); f = (m - lo) / (hi - lo); the element rounds up iff
+ *   (word >> 8) < f * 2^24, where word is the 32-bit random word of the element:
+ *   element idx of the OUTPUT tensor (row-major, idx = r_out * cols_out + c_out)
+ *   takes word idx % 4 of Philox4x32-10 (Salmon et al., SC 2011) with counter
+ *   (idx / 4 low 32 bits, high 32 bits, 0, 0) and key (seed low, seed high).
+ *   Same seed and shape => same bytes. Arguments otherwise as quantize_nvfp4.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_nvfp4_stochastic(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                     mxq_scope scope, int64_t group_rows, int transpose,
+                                     const int8_t* rht_signs16, uint64_t seed,
+                                     void* q, void* s, float* t,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * quantize_nvfp4_2d -- NVFP4 for weights with one E4M3 scale per 16x16 block
  * (plus the FP32 scope scale), so that the forward pass and the transposed
  * backward pass consume the same quantized weight.

@@ -33,6 +33,8 @@ _SIGS = {
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
+    "quantize_nvfp4_stochastic": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, ctypes.c_uint64,
+                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p],
     "quantize_nvfp4_2d": [_c_void_p, _i64, _i64, _i64, _int, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _c_void_p, _size, _c_void_p],
     "dequantize": [_int, _c_void_p, _c_void_p, _c_void_p, _int, _i64, _i64, _i64, _c_void_p, _int, _c_void_p],
@@ -165,8 +167,10 @@ def quantize_nvfp4_per_token(x: torch.Tensor):
 
 
 def quantize_nvfp4(x: torch.Tensor, scope: str = "tensor", group_rows: int = 0, transpose: bool = False,
-                   rht_signs=None, workspace: torch.Tensor | None = None):
-    """General NVFP4 quantizer (see include/mxq.h). rht_signs: 16 ints in {-1, +1} or None."""
+                   rht_signs=None, workspace: torch.Tensor | None = None, sr_seed: int | None = None):
+    """General NVFP4 quantizer (see include/mxq.h). rht_signs: 16 ints in {-1, +1} or None.
+    sr_seed: None = round-to-nearest-even; an int = stochastic rounding of the elements
+    (quantize_nvfp4_stochastic) with that seed."""
     _bf16(x)
     R, C = x.shape
     dev = x.device
@@ -181,9 +185,15 @@ def quantize_nvfp4(x: torch.Tensor, scope: str = "tensor", group_rows: int = 0, 
     ws_bytes = lib().mxq_workspace_bytes(OP_QUANTIZE_NVFP4, out_rows, out_cols, n_scopes) if sc != 0 else 0
     if workspace is None and ws_bytes:
         workspace = _u8((ws_bytes,), dev)
-    _check("quantize_nvfp4", lib().quantize_nvfp4(_ptr(x), R, C, x.stride(0), sc, group_rows, int(transpose),
-                                                  signs, _ptr(q), _ptr(s), _ptr(t), _ptr(workspace),
-                                                  workspace.numel() if workspace is not None else 0, _stream(dev)))
+    wsn = workspace.numel() if workspace is not None else 0
+    if sr_seed is None:
+        _check("quantize_nvfp4", lib().quantize_nvfp4(_ptr(x), R, C, x.stride(0), sc, group_rows, int(transpose),
+                                                      signs, _ptr(q), _ptr(s), _ptr(t), _ptr(workspace), wsn,
+                                                      _stream(dev)))
+    else:
+        _check("quantize_nvfp4_stochastic", lib().quantize_nvfp4_stochastic(
+            _ptr(x), R, C, x.stride(0), sc, group_rows, int(transpose), signs, int(sr_seed), _ptr(q), _ptr(s), _ptr(t),
+            _ptr(workspace), wsn, _stream(dev)))
     return q, s, t
 
 

@@ -13,7 +13,7 @@ hipError_t launch_quant_mxfp8_multi(int, const void* const*, const int64_t*, con
                                     void* const*, void* const*, void* const*, void* const*, hipStream_t);
 hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
 hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
-                              float*, uint32_t*, int64_t, hipStream_t);
+                              float*, uint32_t*, int64_t, int, uint64_t, hipStream_t);
 hipError_t launch_quant_nvfp4_2d(const void*, int64_t, int64_t, int64_t, int64_t, void*, void*, void*, void*, float*,
                                  uint32_t*, int64_t, hipStream_t);
 hipError_t launch_dequant(int, const void*, const void*, const float*, int, int64_t, int64_t, int64_t, void*, int,
@@ -142,9 +142,10 @@ mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidde
   return hip_status(mxq::launch_quant_nvfp4_token(x, tokens, hidden, ld_x, q_packed, s_block, s_token, S(stream)));
 }
 
-mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,
-                          int64_t group_rows, int transpose, const int8_t* rht_signs16, void* q, void* s, float* t,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+mxq_status quantize_nvfp4_any(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,
+                              int64_t group_rows, int transpose, const int8_t* rht_signs16, void* q, void* s, float* t,
+                              void* workspace, size_t workspace_bytes, int sr, uint64_t seed, void* stream) {
   if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
   if (!x || !q || !s || !t) return MXQ_ERR_NULL;
   if (scope != MXQ_SCOPE_ROW && scope != MXQ_SCOPE_TENSOR && scope != MXQ_SCOPE_GROUP) return MXQ_ERR_FORMAT;
@@ -180,7 +181,23 @@ mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
   if (rows == 0 || cols == 0) return MXQ_OK;
   return hip_status(mxq::launch_quant_nvfp4(x, rows, cols, ld_x, (int)scope, group_rows, transpose,
                                             rht_signs16 != nullptr, neg_mask, q, s, t, (uint32_t*)workspace,
-                                            n_scopes, S(stream)));
+                                            n_scopes, sr, seed, S(stream)));
+}
+}  // namespace
+
+mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,
+                          int64_t group_rows, int transpose, const int8_t* rht_signs16, void* q, void* s, float* t,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_nvfp4_any(x, rows, cols, ld_x, scope, group_rows, transpose, rht_signs16, q, s, t, workspace,
+                            workspace_bytes, 0, 0, stream);
+}
+
+mxq_status quantize_nvfp4_stochastic(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,
+                                     int64_t group_rows, int transpose, const int8_t* rht_signs16, uint64_t seed,
+                                     void* q, void* s, float* t, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return quantize_nvfp4_any(x, rows, cols, ld_x, scope, group_rows, transpose, rht_signs16, q, s, t, workspace,
+                            workspace_bytes, 1, seed, stream);
 }
 
 mxq_status quantize_nvfp4_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x, mxq_scope scope,

@@ -51,6 +51,57 @@ __device__ __forceinline__ uint32_t pack8_e2m1(const float* v, float r) {
   return o;
 }
 
+// ---------------------------------------------------------------------------
+// Stochastic rounding (gradients only: 7minutos.es NVFP4 page, section "La
+// metodologia de formacion de cuatro partes"). Random words come from the
+// counter-based Philox4x32-10 generator (Salmon, Moraes, Dror, Shaw, SC 2011):
+// element idx of the output tensor (row-major) takes word idx % 4 of the block
+// for counter (idx / 4 low, high, 0, 0) and key (seed low, high).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Words of the 8 consecutive elements idx0 .. idx0 + 7 (idx0 % 8 == 0).
+__device__ __forceinline__ void philox_words8(uint64_t idx0, uint64_t seed, uint32_t* w) {
+  const uint64_t b = idx0 >> 2;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const uint4 a = philox4x32_10(make_uint4((uint32_t)b, (uint32_t)(b >> 32), 0u, 0u), k0, k1);
+  const uint4 c = philox4x32_10(make_uint4((uint32_t)(b + 1), (uint32_t)((b + 1) >> 32), 0u, 0u), k0, k1);
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+}
+
+// E2M1 code of p rounded stochastically: m = |p| between grid neighbours lo < hi
+// (spacing d), f = (m - lo) / d (exact); round up iff (word >> 8) < f * 2^24;
+// |p| >= 6 saturates to 6; the sign is copied.
+__device__ __forceinline__ uint32_t e2m1_sr_code(float p, uint32_t word) {
+  const float m = fabsf(p);
+  uint32_t lo_i;
+  float lo, inv_d;
+  if (m >= 6.0f) { lo_i = 7; lo = 6.0f; inv_d = 0.0f; }
+  else if (m >= 4.0f) { lo_i = 6; lo = 4.0f; inv_d = 0.5f; }
+  else if (m >= 2.0f) { lo = floorf(m); lo_i = lo == 2.0f ? 4u : 5u; inv_d = 1.0f; }
+  else { const float h = floorf(m * 2.0f); lo_i = (uint32_t)h; lo = h * 0.5f; inv_d = 2.0f; }
+  const float f = (m - lo) * inv_d;                        // exact: m - lo exact, 1/d a power of two
+  const bool up = (float)(word >> 8) < f * 16777216.0f;    // both sides exact integers < 2^24 (+1)
+  return (lo_i + (up ? 1u : 0u)) | ((__float_as_uint(p) >> 28) & 8u);
+}
+
+__device__ __forceinline__ uint32_t pack8_e2m1_sr(const float* v, float r, const uint32_t* w) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o |= e2m1_sr_code(v[i] * r, w[i]) << (4 * i);
+  return o;
+}
+
 __device__ __forceinline__ void unpack8(const uint4& w, float* f) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
   f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
@@ -97,12 +148,12 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 //   MODE 2: pass 1 of MODE 1 -- only the scope amax, by atomic max.
 // CH = register chunks of 512 values (the row holds at most CH * 512 values).
 // ---------------------------------------------------------------------------
-template <int MODE, int CH, bool RHT>
+template <int MODE, int CH, bool RHT, bool SR = false>
 __global__ void __launch_bounds__(256)
 nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
                   int64_t group_rows, uint32_t neg_mask,
                   uint32_t* __restrict__ scope_amax,
-                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, float* __restrict__ t_out) {
+                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, float* __restrict__ t_out, uint64_t seed) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;   // wave-uniform; with MODE 2 a partial group never syncs
@@ -175,7 +226,14 @@ nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
     a = fmaxf(a, __uint_as_float(dpp_xor1(__float_as_uint(a))));
     float r;
     const uint32_t code = block_scale(a, s_enc, r);
-    const uint32_t packed = pack8_e2m1(f, r);
+    uint32_t packed;
+    if (SR) {
+      uint32_t wd[8];
+      philox_words8((uint64_t)row * cols + e, seed, wd);
+      packed = pack8_e2m1_sr(f, r, wd);
+    } else {
+      packed = pack8_e2m1(f, r);
+    }
     if (e < cols) {
       *reinterpret_cast<uint32_t*>(q + row * (cols / 2) + e / 2) = packed;
       if (!odd) s[row * (cols / 16) + e / 16] = (uint8_t)code;
@@ -196,12 +254,13 @@ nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
 // its 16 scale bytes as one 16-byte store.
 //   MODE 1: scope amax from scope_amax[c / group_rows]; MODE 2: pass 1 (amax only).
 // ---------------------------------------------------------------------------
-template <int MODE, bool RHT>
+template <int MODE, bool RHT, bool SR = false>
 __global__ void __launch_bounds__(256)
 nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
                   int64_t group_rows, uint32_t neg_mask,
                   uint32_t* __restrict__ scope_amax,
-                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t col_tiles, int wide_stores) {
+                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t col_tiles, int wide_stores,
+                  uint64_t seed) {
   // packed tile: column cl at cl * 128, 8-byte granule g = 4w + m at (g ^ 4 * (cl / 8 % 4))
   __shared__ __attribute__((aligned(16))) uint8_t lq[MODE == 1 ? 128 * 128 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t ls[MODE == 1 ? 128 * 16 : 16];
@@ -261,7 +320,18 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
     } else {
       float r;
       const uint32_t code = block_scale(a, s_enc, r);
-      const uint32_t lo = pack8_e2m1(f, r), hi = pack8_e2m1(f + 8, r);
+      uint32_t lo, hi;
+      if (SR) {                                        // output element (col, row): index col * rows + row
+        uint32_t wd[16];
+        const uint64_t idx0 = (uint64_t)(c + cc) * rows + r0;
+        philox_words8(idx0, seed, wd);
+        philox_words8(idx0 + 8, seed, wd + 8);
+        lo = pack8_e2m1_sr(f, r, wd);
+        hi = pack8_e2m1_sr(f + 8, r, wd + 8);
+      } else {
+        lo = pack8_e2m1(f, r);
+        hi = pack8_e2m1(f + 8, r);
+      }
       const int cl = 8 * c16 + cc;
       const int g = (4 * w + m) ^ ((c16 & 3) * 4);
       *reinterpret_cast<uint2*>(lq + cl * 128 + g * 8) = make_uint2(lo, hi);
@@ -468,31 +538,32 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, int64_t n)
   if (i < n) p[i] = v;
 }
 
-template <int MODE, bool RHT>
+template <int MODE, bool RHT, bool SR = false>
 static void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
-                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, float* t, hipStream_t st) {
+                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, float* t, hipStream_t st,
+                        uint64_t seed = 0) {
   dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   const int64_t ch = (cols + 511) / 512;
   if (ch <= 4)
-    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 4, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 4, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
   else if (ch <= 8)
-    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 8, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 8, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
   else if (ch <= 16)
-    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 16, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 16, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
   else
-    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 32, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t);
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 32, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
 }
 
-template <int MODE, bool RHT>
+template <int MODE, bool RHT, bool SR = false>
 static void launch_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
-                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, hipStream_t st) {
+                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, hipStream_t st, uint64_t seed = 0) {
   const int64_t col_tiles = (cols + 127) / 128;
   const int64_t bands = (rows + 255) / 256;
   // 16-byte stores need 16-byte aligned output rows (and bases)
   const int wide = rows % 32 == 0 && ((uintptr_t)q & 15) == 0 && ((uintptr_t)s & 15) == 0;
   dim3 grid((unsigned)(bands * col_tiles)), block(256);
-  hipLaunchKernelGGL((nvfp4_cols_kernel<MODE, RHT>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s,
-                     col_tiles, wide);
+  hipLaunchKernelGGL((nvfp4_cols_kernel<MODE, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s,
+                     col_tiles, wide, seed);
 }
 
 
@@ -527,15 +598,15 @@ hipError_t launch_quant_nvfp4_token(const void* x, int64_t tokens, int64_t hidde
 
 // General entry: scope 0 = ROW, 1 = TENSOR, 2 = GROUP. RHT signs are passed as
 // a 16-bit mask (bit i set <=> sign i is -1); rht = 0 disables the transform.
-hipError_t launch_quant_nvfp4(const void* xv, int64_t rows, int64_t cols, int64_t ld_x, int scope,
-                              int64_t group_rows, int transpose, int rht, uint32_t neg_mask,
-                              void* q, void* s, float* t, uint32_t* ws_amax, int64_t n_scopes,
-                              hipStream_t st) {
-  const uint16_t* x = (const uint16_t*)xv;
-  uint8_t *qp = (uint8_t*)q, *sp = (uint8_t*)s;
+// SR = stochastic rounding of the elements with the given seed.
+template <bool SR>
+static hipError_t quant_nvfp4_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int scope,
+                                   int64_t group_rows, int transpose, int rht, uint32_t neg_mask, uint8_t* qp,
+                                   uint8_t* sp, float* t, uint32_t* ws_amax, int64_t n_scopes, uint64_t seed,
+                                   hipStream_t st) {
   if (scope == 0) {  // per row, one pass (transpose excluded by validation)
-    if (rht) launch_rows<0, true>(x, rows, cols, ld_x, 1, neg_mask, nullptr, qp, sp, t, st);
-    else launch_rows<0, false>(x, rows, cols, ld_x, 1, 0u, nullptr, qp, sp, t, st);
+    if (rht) launch_rows<0, true, SR>(x, rows, cols, ld_x, 1, neg_mask, nullptr, qp, sp, t, st, seed);
+    else launch_rows<0, false, SR>(x, rows, cols, ld_x, 1, 0u, nullptr, qp, sp, t, st, seed);
     return hipGetLastError();
   }
   const int64_t gr = scope == 1 ? (transpose ? cols : rows) : group_rows;
@@ -543,22 +614,34 @@ hipError_t launch_quant_nvfp4(const void* xv, int64_t rows, int64_t cols, int64_
   if (!transpose) {
     if (rht) {
       launch_rows<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st);
-      launch_rows<1, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st);
+      launch_rows<1, true, SR>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st, seed);
     } else {
       launch_rows<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
-      launch_rows<1, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
+      launch_rows<1, false, SR>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st, seed);
     }
   } else {
     if (rht) {
       launch_cols<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st);
-      launch_cols<1, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st);
+      launch_cols<1, true, SR>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st, seed);
     } else {
       launch_cols<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st);
-      launch_cols<1, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st);
+      launch_cols<1, false, SR>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st, seed);
     }
   }
   hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const void* xv, int64_t rows, int64_t cols, int64_t ld_x, int scope,
+                              int64_t group_rows, int transpose, int rht, uint32_t neg_mask,
+                              void* q, void* s, float* t, uint32_t* ws_amax, int64_t n_scopes,
+                              int sr, uint64_t seed, hipStream_t st) {
+  const uint16_t* x = (const uint16_t*)xv;
+  uint8_t *qp = (uint8_t*)q, *sp = (uint8_t*)s;
+  if (sr) return quant_nvfp4_impl<true>(x, rows, cols, ld_x, scope, group_rows, transpose, rht, neg_mask, qp, sp, t,
+                                        ws_amax, n_scopes, seed, st);
+  return quant_nvfp4_impl<false>(x, rows, cols, ld_x, scope, group_rows, transpose, rht, neg_mask, qp, sp, t, ws_amax,
+                                 n_scopes, seed, st);
 }
 
 }  // namespace mxq

@@ -337,6 +337,13 @@ class StressStep:
                 B._ptr(x), self.n, self.n, x.stride(0), B.SCOPE["tensor"], 0, 1, self._signs_c, B._ptr(q),
                 B._ptr(s), B._ptr(t), B._ptr(self.ws), self.ws.numel(), B._stream(self.dev)))
 
+    def quantize_rht_sr(self, a, seed: int):
+        """The gradient operand A with stochastically rounded elements (gradients only)."""
+        q, s, t = self.nv["a"]
+        B._check("quantize_nvfp4_stochastic", B.lib().quantize_nvfp4_stochastic(
+            B._ptr(a), self.n, self.n, a.stride(0), B.SCOPE["tensor"], 0, 1, self._signs_c, seed, B._ptr(q),
+            B._ptr(s), B._ptr(t), B._ptr(self.ws), self.ws.numel(), B._stream(self.dev)))
+
     def nvfp4_wgrad(self):
         qa, sa, ta = self.nv["a"]
         qb, sb, tb = self.nv["b"]

@@ -290,6 +290,44 @@ def test_nvfp4_2d_weights(shape, group):
     assert_bytes_equal(host(st1), est, "2d col only scales")
 
 
+@pytest.mark.parametrize("shape,seed", [((64, 2048), 1), ((33, 7168), 0xDEADBEEF12345678), ((128, 48), 7)])
+def test_nvfp4_stochastic_per_token(shape, seed):
+    g = inputs.rng(98, shape[1])
+    xb = inputs.to_bf16_bits(g.standard_normal(shape) * 1e-3 * g.lognormal(0, 1, (shape[0], 1)))
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="row", sr_seed=seed)
+    eq, es, et = onv.quantize_per_token(xb, sr_seed=seed)
+    assert_bytes_equal(host(q), eq, "sr packed")
+    assert_bytes_equal(host(s), es, "sr scales")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "sr t")
+
+
+def test_nvfp4_stochastic_tensor_and_group():
+    g = inputs.rng(98, 1)
+    xb = inputs.normal_bf16(g, (96, 256), 1e-3)
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="tensor", sr_seed=42)
+    eq, es, et = onv.quantize_per_tensor(xb, sr_seed=42)
+    assert_bytes_equal(host(q), eq, "sr tensor packed")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "sr tensor t")
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="group", group_rows=32, sr_seed=43)
+    x = inputs.bf16_bits_to_float(xb)
+    amax = np.repeat(np.max(np.abs(x.reshape(3, 32, 256)), axis=(1, 2)).astype(np.float32), 32)
+    eq, es, _ = onv.quantize_with_scope_amax(x, amax, sr_seed=43)
+    assert_bytes_equal(host(q), eq, "sr group packed")
+    assert_bytes_equal(host(s), es, "sr group scales")
+
+
+@pytest.mark.parametrize("shape", [(256, 520), (64, 48), (528, 256)])
+def test_nvfp4_stochastic_rht_transposed(shape):
+    g = inputs.rng(98, shape[0] * 3 + shape[1])
+    xb = inputs.to_bf16_bits(g.standard_t(3.0, size=shape) * 1e-3)
+    signs = np.where(g.random(16) < 0.5, -1, 1).astype(np.int8)
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="tensor", transpose=True, rht_signs=signs, sr_seed=99)
+    eq, es, et = onv.rht_quantize_colwise_per_tensor(xb, signs, sr_seed=99)
+    assert_bytes_equal(host(q), eq, "sr rht packed")
+    assert_bytes_equal(host(s), es, "sr rht scales")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "sr rht t")
+
+
 # ------------------------------ dequantize ---------------------------------
 
 def test_dequantize_mxfp8_and_nvfp4():

@@ -29,3 +29,4 @@ docstring. Present ones:
 """
 
 from . import formats, mxfp8, nvfp4, gemm, moe, rng  # noqa: F401
+from . import mxfp4  # noqa: F401,E402

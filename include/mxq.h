@@ -29,8 +29,8 @@
  *  correctly rounded division and no flush-to-zero (no fast math).
  *
  *  Scale layouts are canonical row-major matrices (no swizzle): the scale of the
- *  block holding element (r, c) sits at s[r * (cols / B) + c / B], B = 32 (MXFP8)
- *  or 16 (NVFP4). mxq_scale_bytes() returns that size.
+ *  block holding element (r, c) sits at s[r * (cols / B) + c / B], B = 32 (MXFP8,
+ *  MXFP4) or 16 (NVFP4). mxq_scale_bytes() returns that size.
  *
  * Sources: "Miles Blackwell RL Cambia la Uniformidad BF16 por MXFP8 y NVFP4
  * Nativos" (remio.ai); "NVIDIA presenta una metodologia de preentrenamiento de 4
@@ -59,7 +59,7 @@ typedef enum {
   MXQ_ERR_HIP = 6        /* a HIP launch failed                                */
 } mxq_status;
 
-typedef enum { MXQ_MXFP8 = 1, MXQ_NVFP4 = 2, MXQ_BF16 = 3 } mxq_format;
+typedef enum { MXQ_MXFP8 = 1, MXQ_NVFP4 = 2, MXQ_BF16 = 3, MXQ_MXFP4 = 4 } mxq_format;
 typedef enum { MXQ_OUT_BF16 = 0, MXQ_OUT_F32 = 1 } mxq_out_dtype;
 
 /* Scope of an NVFP4 FP32 (second-level) scale.
@@ -118,6 +118,28 @@ typedef struct {
   void* s_colT;
 } mxq_mxfp8_tensor;
 mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * quantize_mxfp4 -- MXFP4 quantization (E2M1 elements, one E8M0 scale per 32) of a
+ * BF16 (rows, cols) tensor into a rowwise 1x32 and/or a columnwise 32x1 copy, in
+ * one pass over HBM.
+ *   Defined by: MXFP4 blocks of 32 E2M1 values sharing a power-of-two UE8M0 scale,
+ *   the format NVFP4 is compared with (7minutos.es, sections "Que es realmente
+ *   NVFP4" and "NVFP4 frente a MXFP4").
+ *   Scale rule (as for MXFP8, with the E2M1 maximum 6): s = clamp(e + 127, 0, 254),
+ *   e the smallest integer with amax <= 6 * 2^e (s = 0 for an all-zero block);
+ *   q = RNE_sat_E2M1(x * 2^(127-s)).
+ *
+ *   x      : BF16, element (r, c) at x[r * ld_x + c]; ld_x >= cols, ld_x % 8 == 0.
+ *   q_row  : packed E2M1 (rows, cols/2);  s_row : E8M0 (rows, cols/32).
+ *   q_colT : packed E2M1 (cols, rows/2), the columnwise copy stored transposed
+ *            (element (r, c) of x is element r of row c);  s_colT : E8M0 (cols, rows/32).
+ *   Either output pair may be NULL to skip that copy (not both). Requires
+ *   cols % 32 == 0, and rows % 32 == 0 when the columnwise copy is requested.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          void* q_row, void* s_row, void* q_colT, void* s_colT,
+                          void* stream);
 
 /* ---------------------------------------------------------------------------
  * quantize_nvfp4_per_token -- NVFP4 with one FP32 scale per token (row),
@@ -232,17 +254,19 @@ mxq_status quantize_nvfp4_2d(const void* x, int64_t rows, int64_t cols, int64_t 
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * dequantize -- reconstruct BF16 or FP32 values from MXFP8 or NVFP4 data, e.g.
+ * dequantize -- reconstruct BF16 or FP32 values from MXFP8, NVFP4 or MXFP4 data, e.g.
  * the BF16 operands of the dequantized-backward GEMMs.
  *   Defined by: the dequantized-backward mode, whose backward GEMMs run in BF16 on
  *   dequantizations of the exact low-precision forward operands ("Miles Blackwell
  *   RL", remio.ai, section "La Compatibilidad ..."; aib.vote, backward-modes
  *   paragraph).
- *   FP32 output: v = (q * S) * t, one binary32 rounding (q * S is exact; MXFP8 has
- *   no t). BF16 output: that FP32 value rounded to BF16 (RNE). Overflow gives Inf.
+ *   FP32 output: v = (q * S) * t, one binary32 rounding (q * S is exact; MXFP8 and
+ *   MXFP4 have no t). BF16 output: that FP32 value rounded to BF16 (RNE). Overflow
+ *   gives Inf.
  *
- *   fmt   : MXQ_MXFP8 (q (rows, cols) E4M3, s (rows, cols/32) E8M0, t unused) or
- *           MXQ_NVFP4 (q (rows, cols/2), s (rows, cols/16) E4M3, t per t_scope).
+ *   fmt   : MXQ_MXFP8 (q (rows, cols) E4M3, s (rows, cols/32) E8M0, t unused),
+ *           MXQ_NVFP4 (q (rows, cols/2), s (rows, cols/16) E4M3, t per t_scope) or
+ *           MXQ_MXFP4 (q (rows, cols/2), s (rows, cols/32) E8M0, t unused).
  *   out   : (rows, cols) row-major, BF16 or FP32.
  * ------------------------------------------------------------------------- */
 mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float* t,
@@ -291,10 +315,13 @@ mxq_status dequantize_transposed(mxq_format fmt, const void* q, const void* s, c
  *              B likewise with tB (ROW: N, TENSOR: 1);
  *              C = tA[m] tB[n] * sum_k (qA SA)(qB SB) -- the E4M3-per-16 block
  *              products are formed exactly, then accumulated in FP32.
+ *   MXQ_MXFP4: A (M, K/2) packed E2M1 + sA (M, K/32) E8M0; B (N, K/2) + sB (N, K/32);
+ *              tA/tB unused. Operand values E2M1 * 2^(s-127) formed exactly (scale
+ *              codes s <= 252), products accumulated at FP32 precision.
  *   MXQ_BF16 : A (M, K) BF16, B (N, K) BF16; scales unused.
  *   C[m * ldc + n], ldc >= N, C 4-byte aligned. Accuracy: normwise relative error
  *   <= 2e-5 against the FP64 product of the exact dequantized operands.
- *   Requires K % 32 == 0 (MXFP8), K % 32 == 0 (NVFP4), K % 8 == 0 (BF16), and
+ *   Requires K % 32 == 0 (MXFP8, NVFP4, MXFP4), K % 8 == 0 (BF16), and
  *   K <= 2^22 (32-bit operand offsets); MXQ_ERR_SHAPE otherwise.
  * ------------------------------------------------------------------------- */
 mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K,
@@ -339,11 +366,11 @@ mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K,
  *   vary_k = 1 (wgrad): for every group g:  C_g = sum over k in [offsets[g],
  *       offsets[g+1]) of A[:, k] B[:, k]^T
  *     A : (M, total_k) K-contiguous; B : (N, total_k); C : (groups, M, N).
- *     Group boundaries must be multiples of 32 (MXFP8) or 8 (BF16); only MXQ_MXFP8
- *     and MXQ_BF16 are supported with vary_k = 1 in ABI version 1.
+ *     Group boundaries must be multiples of 32 (MXFP8, MXFP4) or 8 (BF16); MXQ_NVFP4
+ *     is not supported with vary_k = 1 in ABI version 1.
  *   offsets  : DEVICE int64 (groups + 1), non-decreasing, offsets[0] = 0,
  *              offsets[groups] = total (total_slots or total_k, passed as `total`);
- *              with vary_k = 1 every offset is a multiple of 32 (MXFP8) or 8 (BF16).
+ *              with vary_k = 1 every offset is a multiple of 32 (MXFP8, MXFP4) or 8 (BF16).
  *              The device checks this before any tile runs; offsets that break it
  *              make the call a no-op that leaves C unwritten.
  *   Limits     : K <= 2^22 (vary_k = 1: total <= 2^22); with a_row_index, a_rows times
@@ -390,7 +417,7 @@ mxq_status moe_combine(const float* o_slots, int64_t total_slots, int64_t tokens
  * Queries.
  * ------------------------------------------------------------------------- */
 /* Bytes of the scale matrix for a (rows, cols) tensor blocked along cols
- * (MXFP8: rows * cols/32, NVFP4: rows * cols/16); 0 for BF16 or bad shapes. */
+ * (MXFP8, MXFP4: rows * cols/32, NVFP4: rows * cols/16); 0 for BF16 or bad shapes. */
 size_t mxq_scale_bytes(mxq_format fmt, int64_t rows, int64_t cols);
 
 enum { MXQ_OP_QUANTIZE_NVFP4 = 1, MXQ_OP_GROUPED_GEMM = 2 };

@@ -17,7 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
-MXFP8, NVFP4, BF16 = 1, 2, 3
+MXFP8, NVFP4, BF16, MXFP4 = 1, 2, 3, 4
+_PACKED4 = (NVFP4, MXFP4)          # formats with two elements per byte
 OUT_BF16, OUT_F32 = 0, 1
 SCOPE = {"row": 0, "token": 0, "tensor": 1, "group": 2}
 OP_QUANTIZE_NVFP4, OP_GROUPED_GEMM = 1, 2
@@ -30,6 +31,7 @@ _size = ctypes.c_size_t
 _SIGS = {
     "quantize_mxfp8": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_mxfp8_multi": [_c_void_p, _int, _c_void_p],
+    "quantize_mxfp4": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
@@ -135,6 +137,26 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, 
     return q_row, s_row, q_col, s_col
 
 
+def quantize_mxfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out=None):
+    """MXFP4 rowwise (R, C/2) + columnwise-transposed (C, R/2) packed copies of BF16 x.
+
+    Returns (q_row, s_row, q_colT, s_colT); skipped copies are None.
+    """
+    _bf16(x)
+    R, C = x.shape
+    dev = x.device
+    if out is not None:
+        q_row, s_row, q_col, s_col = out
+    else:
+        q_row = _u8((R, C // 2), dev) if rowwise else None
+        s_row = _u8((R, C // 32), dev) if rowwise else None
+        q_col = _u8((C, R // 2), dev) if colwise else None
+        s_col = _u8((C, R // 32), dev) if colwise else None
+    _check("quantize_mxfp4", lib().quantize_mxfp4(_ptr(x), R, C, x.stride(0), _ptr(q_row), _ptr(s_row),
+                                                  _ptr(q_col), _ptr(s_col), _stream(dev)))
+    return q_row, s_row, q_col, s_col
+
+
 class _Mxfp8Tensor(ctypes.Structure):
     _fields_ = [("x", _c_void_p), ("rows", _i64), ("cols", _i64), ("ld_x", _i64), ("q_row", _c_void_p),
                 ("s_row", _c_void_p), ("q_colT", _c_void_p), ("s_colT", _c_void_p)]
@@ -226,7 +248,7 @@ def quantize_nvfp4_2d(x: torch.Tensor, scope: str = "tensor", group_rows: int = 
 def dequantize(fmt: int, q: torch.Tensor, s: torch.Tensor, t: torch.Tensor | None = None, t_scope: str = "row",
                group_rows: int = 0, out_dtype: torch.dtype = torch.bfloat16):
     rows = q.shape[0]
-    cols = q.shape[1] * (2 if fmt == NVFP4 else 1)
+    cols = q.shape[1] * (2 if fmt in _PACKED4 else 1)
     out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
     od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
     _check("dequantize", lib().dequantize(fmt, _ptr(q), _ptr(s), _ptr(t), SCOPE[t_scope], group_rows, rows, cols,
@@ -261,7 +283,7 @@ def gemm_block_scaled(fmt: int, A, sA, B, sB, tA=None, tB=None, tA_scope="row", 
     """C = A_hat B_hat^T in FP32; A (M, K-bytes) and B (N, K-bytes) K-contiguous."""
     M = A.shape[0]
     N = B.shape[0]
-    K = A.shape[1] * (2 if fmt == NVFP4 else 1)
+    K = A.shape[1] * (2 if fmt in _PACKED4 else 1)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _check("gemm_block_scaled", lib().gemm_block_scaled(fmt, M, N, K, _ptr(A), _ptr(sA), _ptr(tA), SCOPE[tA_scope],

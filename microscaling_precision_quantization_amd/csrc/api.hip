@@ -11,6 +11,7 @@ namespace mxq {
 hipError_t launch_quant_mxfp8(const void*, int64_t, int64_t, int64_t, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_quant_mxfp8_multi(int, const void* const*, const int64_t*, const int64_t*, const int64_t*,
                                     void* const*, void* const*, void* const*, void* const*, hipStream_t);
+hipError_t launch_quant_mxfp4(const void*, int64_t, int64_t, int64_t, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
 hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
                               float*, uint32_t*, int64_t, int, uint64_t, hipStream_t);
@@ -43,7 +44,7 @@ constexpr int64_t kMaxGridBlocks = 0x7FFFFFFF;
 // or (gather) the whole gathered operand, must span less than 2^31 bytes.
 constexpr int64_t kMaxGemmK = int64_t(1) << 22;
 inline int64_t gemm_row_bytes(mxq_format fmt, int64_t k) {
-  return fmt == MXQ_BF16 ? 2 * k : fmt == MXQ_MXFP8 ? k : k / 2;
+  return fmt == MXQ_BF16 ? 2 * k : fmt == MXQ_MXFP8 ? k : k / 2;   // NVFP4, MXFP4: two per byte
 }
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -72,7 +73,7 @@ const char* mxq_status_string(mxq_status s) {
 
 size_t mxq_scale_bytes(mxq_format fmt, int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0) return 0;
-  if (fmt == MXQ_MXFP8 && cols % 32 == 0) return (size_t)(rows * (cols / 32));
+  if ((fmt == MXQ_MXFP8 || fmt == MXQ_MXFP4) && cols % 32 == 0) return (size_t)(rows * (cols / 32));
   if (fmt == MXQ_NVFP4 && cols % 16 == 0) return (size_t)(rows * (cols / 16));
   return 0;
 }
@@ -97,6 +98,22 @@ mxq_status quantize_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_
   if (rows == 0 || cols == 0) return MXQ_OK;
   if (((rows + 127) / 128) * ((cols + 127) / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
   return hip_status(mxq::launch_quant_mxfp8(x, rows, cols, ld_x, do_row ? q_row : nullptr, s_row,
+                                            do_col ? q_colT : nullptr, s_colT, S(stream)));
+}
+
+mxq_status quantize_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q_row, void* s_row,
+                          void* q_colT, void* s_colT, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  const bool do_row = q_row || s_row, do_col = q_colT || s_colT;
+  if (!x || (!do_row && !do_col)) return MXQ_ERR_NULL;
+  if ((do_row && (!q_row || !s_row)) || (do_col && (!q_colT || !s_colT))) return MXQ_ERR_NULL;
+  if (cols % 32) return MXQ_ERR_SHAPE;
+  if (do_col && rows % 32) return MXQ_ERR_SHAPE;
+  if (ld_x < cols) return MXQ_ERR_SHAPE;
+  if (ld_x % 8 || !al16(x) || (do_row && !al16(q_row)) || (do_col && !al16(q_colT))) return MXQ_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if (((rows + 127) / 128) * ((cols + 127) / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_quant_mxfp4(x, rows, cols, ld_x, do_row ? q_row : nullptr, s_row,
                                             do_col ? q_colT : nullptr, s_colT, S(stream)));
 }
 
@@ -226,10 +243,10 @@ mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float*
                       int64_t group_rows, int64_t rows, int64_t cols, void* out, mxq_out_dtype out_dtype,
                       void* stream) {
   if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
-  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4) return MXQ_ERR_FORMAT;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_MXFP4) return MXQ_ERR_FORMAT;
   if (out_dtype != MXQ_OUT_BF16 && out_dtype != MXQ_OUT_F32) return MXQ_ERR_FORMAT;
   if (!q || !s || !out || (fmt == MXQ_NVFP4 && !t)) return MXQ_ERR_NULL;
-  if (fmt == MXQ_MXFP8 && cols % 32) return MXQ_ERR_SHAPE;
+  if ((fmt == MXQ_MXFP8 || fmt == MXQ_MXFP4) && cols % 32) return MXQ_ERR_SHAPE;
   if (fmt == MXQ_NVFP4 && cols % 16) return MXQ_ERR_SHAPE;
   int tm = 0;
   if (fmt == MXQ_NVFP4) {
@@ -242,7 +259,7 @@ mxq_status dequantize(mxq_format fmt, const void* q, const void* s, const float*
   }
   if (!al16(q) || !al16(out)) return MXQ_ERR_ALIGN;
   if (rows == 0 || cols == 0) return MXQ_OK;
-  return hip_status(mxq::launch_dequant(fmt == MXQ_NVFP4, q, s, t, tm, group_rows, rows, cols, out,
+  return hip_status(mxq::launch_dequant((int)fmt, q, s, t, tm, group_rows, rows, cols, out,
                                         out_dtype == MXQ_OUT_F32, S(stream)));
 }
 
@@ -277,7 +294,7 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K, co
                              const float* tA, mxq_scope tA_scope, const void* B, const void* sB, const float* tB,
                              mxq_scope tB_scope, float* C, int64_t ldc, void* stream) {
   if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16) return MXQ_ERR_FORMAT;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4) return MXQ_ERR_FORMAT;
   if (!A || !B || !C) return MXQ_ERR_NULL;
   if (fmt != MXQ_BF16 && (!sA || !sB)) return MXQ_ERR_NULL;
   int ta = -1, tb = -1;
@@ -288,8 +305,7 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K, co
     if (ta != 0 && ta != 1) return MXQ_ERR_FORMAT;
     if (tb != 0 && tb != 1) return MXQ_ERR_FORMAT;
   }
-  if (fmt == MXQ_MXFP8 && K % 32) return MXQ_ERR_SHAPE;
-  if (fmt == MXQ_NVFP4 && K % 32) return MXQ_ERR_SHAPE;
+  if (fmt != MXQ_BF16 && K % 32) return MXQ_ERR_SHAPE;
   if (fmt == MXQ_BF16 && K % 8) return MXQ_ERR_SHAPE;
   if (K > kMaxGemmK || ldc < N) return MXQ_ERR_SHAPE;
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
@@ -313,7 +329,7 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
                                      const void* B, const void* sB, const float* tB, mxq_scope tB_scope, float* C,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   if (groups < 0 || total < 0 || M < 0 || N < 0 || K < 0 || a_rows < 0) return MXQ_ERR_SHAPE;
-  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16) return MXQ_ERR_FORMAT;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4) return MXQ_ERR_FORMAT;
   if (vary_k != 0 && vary_k != 1) return MXQ_ERR_FORMAT;
   if (vary_k && fmt == MXQ_NVFP4) return MXQ_ERR_FORMAT;
   if (vary_k && a_row_index) return MXQ_ERR_FORMAT;
@@ -328,13 +344,12 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
     if (tb != 0 && tb != 2) return MXQ_ERR_FORMAT;    // per B row, or per group (expert)
   }
   if (!vary_k) {
-    if (fmt == MXQ_MXFP8 && K % 32) return MXQ_ERR_SHAPE;
-    if (fmt == MXQ_NVFP4 && K % 32) return MXQ_ERR_SHAPE;
+    if (fmt != MXQ_BF16 && K % 32) return MXQ_ERR_SHAPE;
     if (fmt == MXQ_BF16 && K % 8) return MXQ_ERR_SHAPE;
     if (K > kMaxGemmK) return MXQ_ERR_SHAPE;
     if (a_row_index && a_rows * gemm_row_bytes(fmt, K) > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   } else {
-    if (total % (fmt == MXQ_MXFP8 ? 32 : 8)) return MXQ_ERR_SHAPE;
+    if (total % ((fmt == MXQ_MXFP8 || fmt == MXQ_MXFP4) ? 32 : 8)) return MXQ_ERR_SHAPE;
     if (total > kMaxGemmK) return MXQ_ERR_SHAPE;
   }
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;

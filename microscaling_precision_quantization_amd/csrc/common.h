@@ -76,6 +76,19 @@ __device__ __forceinline__ uint32_t e8m0_from_bf16_amax(uint32_t amax_bits) {
   int s = E - 8 + (M > 96 ? 1 : 0);
   return (uint32_t)(s < 0 ? 0 : s);
 }
+// The same rule for MXFP4 blocks (E2M1 maximum 6 = 1.5 * 2^2): the smallest 2^e with
+// amax <= 6 * 2^e, s = clamp(e + 127, 0, 254): e = E - 127 - 2 when M <= 64
+// (mantissa <= 1.5), else E - 127 - 1.
+__device__ __forceinline__ uint32_t e8m0_from_bf16_amax_e2m1(uint32_t amax_bits) {
+  int E = (int)((amax_bits >> 7) & 0xFF);
+  int M = (int)(amax_bits & 0x7F);
+  int s = E - 2 + (M > 64 ? 1 : 0);
+  return (uint32_t)(s < 0 ? 0 : s);
+}
+// 2^(127-s) as a float (exact); s = 254 gives the subnormal 2^-127.
+__device__ __forceinline__ float e8m0_inverse(uint32_t s) {
+  return __uint_as_float(s <= 253 ? (254u - s) << 23 : 0x00400000u);
+}
 // 2^(s-127) as a float; s = 0 gives the subnormal 2^-127.
 __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   return __uint_as_float(s == 0 ? 0x00400000u : (s << 23));

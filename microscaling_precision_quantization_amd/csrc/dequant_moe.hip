@@ -5,18 +5,21 @@
 // BF16 on dequantizations of the exact low-precision forward operands
 // ("Miles Blackwell RL", remio.ai, section "La Compatibilidad de Miles
 // Blackwell Ahora Abarca Todo el Ciclo de RL"; aib.vote, backward paragraph).
-//   v = fl(fl(q * S) * t)  (q * S exact; MXFP8 has no t), BF16 = RNE(v).
+//   v = fl(fl(q * S) * t)  (q * S exact; MXFP8 and MXFP4 have no t), BF16 = RNE(v).
 // SwiGLU experts with gate and up in one fused GEMM, and per-token NVFP4 on the
 // expert activations: remio.ai, sections "Un Cuantizador Compartido Es el
 // Mecanismo Real" and "La Compatibilidad ...".
+#include <type_traits>
+
 #include "common.h"
 
 namespace mxq {
 
 // ---------------------------------------------------------------------------
 // Dequantize: one thread per 16 consecutive elements of a row.
+// FMT: 1 MXFP8, 2 NVFP4, 4 MXFP4.
 // ---------------------------------------------------------------------------
-template <bool NV, bool OUT_F32>
+template <int FMT, bool OUT_F32>
 __global__ void __launch_bounds__(256)
 dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, const float* __restrict__ t,
                int t_mode, int64_t group_rows, int64_t rows, int64_t cols, void* __restrict__ out) {
@@ -25,12 +28,18 @@ dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, con
   if (idx >= rows * per_row) return;
   const int64_t r = idx / per_row, c0 = (idx % per_row) * 16;
   float v[16];
-  if (!NV) {
+  if (FMT == 1) {
     const uint4 b = *reinterpret_cast<const uint4*>(q + r * cols + c0);
     const float sc = e8m0_to_float(s[r * (cols / 32) + c0 / 32]);
     const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFF) * sc;
+  } else if (FMT == 4) {
+    const uint2 b = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c0 / 2);
+    const float sc = e8m0_to_float(s[r * (cols / 32) + c0 / 32]);
+    const uint32_t w[2] = {b.x, b.y};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = e2m1_to_f32((w[i / 8] >> (4 * (i % 8))) & 0xF) * sc;   // exact
   } else {
     const uint2 b = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c0 / 2);
     const float S = e4m3_to_f32(s[r * (cols / 16) + c0 / 16]);
@@ -56,15 +65,19 @@ dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, con
   }
 }
 
-hipError_t launch_dequant(int nv, const void* q, const void* s, const float* t, int t_mode, int64_t group_rows,
+// fmt: 1 MXFP8, 2 NVFP4, 4 MXFP4
+hipError_t launch_dequant(int fmt, const void* q, const void* s, const float* t, int t_mode, int64_t group_rows,
                           int64_t rows, int64_t cols, void* out, int out_f32, hipStream_t st) {
   const int64_t n = rows * (cols / 16);
   dim3 grid((unsigned)((n + 255) / 256)), block(256);
   const uint8_t *qp = (const uint8_t*)q, *sp = (const uint8_t*)s;
-  if (nv && out_f32) hipLaunchKernelGGL((dequant_kernel<true, true>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
-  else if (nv) hipLaunchKernelGGL((dequant_kernel<true, false>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
-  else if (out_f32) hipLaunchKernelGGL((dequant_kernel<false, true>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
-  else hipLaunchKernelGGL((dequant_kernel<false, false>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+  auto go = [&](auto K) {
+    if (out_f32) hipLaunchKernelGGL((dequant_kernel<decltype(K)::value, true>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+    else hipLaunchKernelGGL((dequant_kernel<decltype(K)::value, false>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, rows, cols, out);
+  };
+  if (fmt == 2) go(std::integral_constant<int, 2>{});
+  else if (fmt == 4) go(std::integral_constant<int, 4>{});
+  else go(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

@@ -11,6 +11,10 @@
 //     at most 6 significant bits and lies in [2^-10, 2688], inside FP16's normal
 //     range. S = 2^e * m (m = 1..1.875): the scaled convert applies 2^e, a packed
 //     FP16 multiply applies m (exact) -> FP16 MFMA; tA tB in the epilogue.
+//   * MXFP4 (E2M1, E8M0 per 32 along K): q * 2^(s-127) has 2 significant bits and
+//     lies in [2^-128, 6 * 2^125] for s <= 252, where BF16 holds it exactly (the
+//     smallest values as BF16 subnormals) -> the scaled convert yields it in BF16
+//     -> BF16 MFMA. (s = 253 arises only for blocks whose amax exceeds 1.5 * 2^127.)
 //   * BF16 operands as they are -> BF16 MFMA.
 // Definitions: microscaling blocks along the reduction dimension ("Miles
 // Blackwell RL", remio.ai, section "Un Cuantizador Compartido Es el Mecanismo
@@ -52,19 +56,21 @@ template <int LD> struct RowBytes;
 template <> struct RowBytes<0> { static constexpr int v = 128; };   // BF16
 template <> struct RowBytes<1> { static constexpr int v = 64; };    // MXFP8
 template <> struct RowBytes<2> { static constexpr int v = 32; };    // NVFP4
+template <> struct RowBytes<3> { static constexpr int v = 32; };    // MXFP4
 
 // Scale modes (SM):
 //   0  general: K tiles may end early; per stage, one direct load per row and scale
-//      unit (MXFP8: 1 byte = one 32-block per unit, NVFP4: 2 bytes = two 16-blocks).
+//      unit (MXFP8 / MXFP4: 1 byte = one 32-block per unit, NVFP4: 2 bytes = two
+//      16-blocks).
 //   1  K % 64 == 0: per stage, one load per row of all the stage's blocks (2 / 4 bytes).
 //   2  K % 64 == 0 and 16-byte aligned scale rows: 16 bytes per row (8 MXFP8 / 4 NVFP4
-//      stages) in one load, double-buffered in a separate LDS area; cuts the scale
-//      cache-line requests by 8 / 4.
+//      / 8 MXFP4 narrow stages) in one load, double-buffered in a separate LDS area;
+//      cuts the scale cache-line requests by that factor.
 // Each per-stage load lands in a 4-byte LDS slot per row (gfx950 places 1/2/4-byte
 // direct loads at base + 4 lane); chunked scales in a 16-byte slot per row.
 template <int LD, int SM> struct ScaleDma {
   static constexpr int SU = (LD == 0 || SM == 2) ? 0 : (SM == 1 ? 1 : 2);
-  static constexpr int SZ = LD == 1 ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
+  static constexpr int SZ = (LD == 1 || LD == 3) ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
 };
 
 // OCC = workgroups meant to share one CU: the LDS budget of a workgroup is 1 / OCC of it.
@@ -80,7 +86,7 @@ struct Cfg {
   static constexpr int SU = ScaleDma<LD, SM>::SU, SZ = ScaleDma<LD, SM>::SZ;
   static constexpr bool CH = SM == 2 && LD != 0;                 // chunked scales
   // stages per 16-byte scale chunk (16 blocks)
-  static constexpr int SPC = LD == 1 ? 16 / (BK / 32) : LD == 2 ? 16 / (BK / 16) : 4;
+  static constexpr int SPC = (LD == 1 || LD == 3) ? 16 / (BK / 32) : LD == 2 ? 16 / (BK / 16) : 4;
   static constexpr int CH_HALF = CH ? (BM + BN) * 16 : 0;         // one chunk buffer
   static constexpr int S_BYTES = SU * (BM + BN) * 4;              // scale slots of one stage
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
@@ -99,8 +105,8 @@ struct Cfg {
 }  // namespace gx
 
 struct ExactProblem {
-  const uint8_t* A;        // MXFP8: (rows, lda) bytes; NVFP4: (rows, lda/2); BF16: (rows, lda) x 2 bytes
-  const uint8_t* sA;       // MXFP8 (rows, lda/32) E8M0; NVFP4 (rows, lda/16) E4M3
+  const uint8_t* A;        // MXFP8: (rows, lda) bytes; NVFP4 / MXFP4: (rows, lda/2); BF16: (rows, lda) x 2 bytes
+  const uint8_t* sA;       // MXFP8 / MXFP4 (rows, lda/32) E8M0; NVFP4 (rows, lda/16) E4M3
   const float* tA;         // NVFP4 decode scales (tA_mode 0 per A row, 1 tensor)
   int tA_mode;
   const int32_t* a_idx;    // optional gather of A rows
@@ -219,6 +225,17 @@ __device__ __forceinline__ v8bf mx_to_bf16(uint32_t w0, uint32_t w1, float sc) {
   return r;
 }
 
+// 8 E2M1 values (one dword, low nibble first) -> 8 BF16, each exactly q * 2^(s-127).
+__device__ __forceinline__ v8bf mx4_to_bf16(uint32_t w, float sc) {
+  v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  v8bf r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1]; r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // 8 E2M1 values (one dword, low nibble first) times the E4M3 block scale S -> 8
 // FP16, exactly: convert with the power-of-two part of S, multiply by its mantissa.
 __device__ __forceinline__ v8h nv_to_f16(uint32_t w, float p2, v2h m2) {
@@ -253,6 +270,9 @@ __device__ __forceinline__ void e4m3_split(uint32_t codes, float& p2, v2h& m2) {
 
 template <int I> using ic = std::integral_constant<int, I>;
 
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+constexpr int lcm_int(int a, int b) { return a / gcd_int(a, b) * b; }
+
 // Compile-time loop: f(ic<0>), ..., f(ic<N-1>).
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -282,10 +302,10 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   constexpr int RB = C::RB, NS = C::NS, TI = C::TI, TJ = C::TJ, IA = C::IA, IB = C::IB, IS = C::IS;
   constexpr int SBS = C::SBS;                             // sub-blocks per stage
   constexpr int NF = TI + TJ;                             // fragments per lane and sub-block
-  constexpr int BS = LD == 1 ? 32 : 16;                   // elements per scale block
+  constexpr int BS = (LD == 1 || LD == 3) ? 32 : 16;      // elements per scale block
   constexpr int EPC = LD == 0 ? 8 : LD == 1 ? 16 : 32;    // elements per 16-byte chunk
   constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave (chunks aside)
-  constexpr int R = CH ? (SPC > NS ? SPC : NS) : NS;      // stages per unrolled round
+  constexpr int R = CH ? lcm_int(SPC, NS) : NS;           // stages per unrolled round
   static_assert(R % NS == 0 && (!CH || R % SPC == 0), "round must cover whole slot and chunk cycles");
   static_assert((R * SBS) % 2 == 0, "fragment double buffer needs an even sub-block count per round");
   const int lane = threadIdx.x & 63;
@@ -325,7 +345,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   }
   // Scales: load q of IS per wave covers 64 consecutive items of the [A rows | B rows]
   // list of unit u (SU units per stage); each lands in a 4-byte LDS slot per row.
-  constexpr int BPU = (LD == 1 ? 2 : 4) / (C::SU > 0 ? C::SU : 1);   // blocks per unit
+  constexpr int BPU = ((LD == 1 || LD == 3) ? 2 : 4) / (C::SU > 0 ? C::SU : 1);   // blocks per unit
   v4i rsS[IS > 0 ? IS : 1];
   uint32_t voS[IS > 0 ? IS : 1];
 #pragma unroll
@@ -467,8 +487,8 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 
   // Chunked scales: the 16-byte chunk row of each fragment row (one per lane) is read into
   // registers once per chunk (SPC stages), at its first stage, and the stage's bytes are
-  // taken from there: row r's byte (MXFP8 block b) or byte pair (NVFP4 blocks 2h, 2h+1)
-  // of stage t sits at chunk + 16 r + (t % SPC) * bytes per stage. (Byte-wise LDS reads of
+  // taken from there: row r's byte (MXFP8 block b, MXFP4 block 2b + h) or byte pair (NVFP4
+  // blocks 2h, 2h+1) of stage t sits at chunk + 16 r + (t % SPC) * bytes per stage. (Byte-wise LDS reads of
   // 16-byte-strided rows would each take several conflicting passes.)
   const uint32_t wcA = (uint32_t)(wm * (BM / 2) * 16), wcB = (uint32_t)((BM + wn * (BN / 2)) * 16);
   u32x4 chr[CH ? NF : 1];
@@ -493,18 +513,23 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         if constexpr (LD == 1) {                      // one block per sub-block
           constexpr int idx = tp * SBS + b;
           fr.sc[f] = (chr[f][idx / 4] >> (8 * (idx % 4))) & 0xFFu;
+        } else if constexpr (LD == 3) {               // two blocks per sub-block, one per lane half
+          constexpr int idx = tp * 2 * SBS + 2 * b;    // even: idx % 4 + h stays in its dword
+          fr.sc[f] = (chr[f][idx / 4] >> (8 * (idx % 4 + h))) & 0xFFu;
         } else {                                      // four blocks per sub-block, two per lane
           fr.sc[f] = (chr[f][tp * SBS + b] >> (16 * h)) & 0xFFFFu;
         }
       }
     } else if constexpr (LD != 0) {
       const lds_cptr sa = as_lds(lbase[S] + wsA + xs), sb = as_lds(lbase[S] + wsB + xs);
-      // MXFP8: the byte of block b; NVFP4: the two bytes of blocks 2h, 2h+1
-      const int so = LD == 1 ? (C::SU == 1 ? b : b * SC_UNIT) : (C::SU == 1 ? 2 * h : h * SC_UNIT);
+      // MXFP8: the byte of block b; NVFP4: the two bytes of blocks 2h, 2h+1; MXFP4 (one
+      // sub-block per stage): the byte of block h
+      const int so = LD == 1 ? (C::SU == 1 ? b : b * SC_UNIT)
+                   : LD == 2 ? (C::SU == 1 ? 2 * h : h * SC_UNIT) : (C::SU == 1 ? h : h * SC_UNIT);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const lds_cptr q = (f < TI ? sa + f * 128 : sb + (f - TI) * 128) + so;
-        fr.sc[f] = LD == 1 ? (uint32_t)*q : (uint32_t)*(const __attribute__((address_space(3))) uint16_t*)q;
+        fr.sc[f] = LD != 2 ? (uint32_t)*q : (uint32_t)*(const __attribute__((address_space(3))) uint16_t*)q;
       }
     }
   };
@@ -548,6 +573,28 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, acc[i][j], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, acc[i][j], 0, 0, 0);
+        hook(JJ);
+      });
+    } else if constexpr (LD == 3) {
+      v8bf fa[4][TI];          // [dword][i]: 8 consecutive K each
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const float s = mx_cvt_scale(fr.sc[i]);
+        fa[0][i] = mx4_to_bf16(fr.raw[i].x, s);
+        fa[1][i] = mx4_to_bf16(fr.raw[i].y, s);
+        fa[2][i] = mx4_to_bf16(fr.raw[i].z, s);
+        fa[3][i] = mx4_to_bf16(fr.raw[i].w, s);
+      }
+      static_for<0, TJ>([&](auto JJ) {
+        constexpr int j = decltype(JJ)::value;
+        const float s = mx_cvt_scale(fr.sc[TI + j]);
+        static_for<0, 4>([&](auto DW) {
+          constexpr int d = decltype(DW)::value;
+          const uint32_t w = d == 0 ? fr.raw[TI + j].x : d == 1 ? fr.raw[TI + j].y : d == 2 ? fr.raw[TI + j].z : fr.raw[TI + j].w;
+          const v8bf fb = mx4_to_bf16(w, s);
+#pragma unroll
+          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[d][i], fb, acc[i][j], 0, 0, 0);
+        });
         hook(JJ);
       });
     } else {
@@ -755,7 +802,7 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.m_valid = offsets[g + 1] - offsets[g];
     const int64_t b_elems = g * N * base.ldb;
     p.B = base.B + k_bytes<LD>(b_elems);
-    if (LD == 1) p.sB = base.sB + b_elems / 32;
+    if (LD == 1 || LD == 3) p.sB = base.sB + b_elems / 32;
     if (LD == 2) {
       p.sB = base.sB + b_elems / 16;
       if (base.tB_mode == 2) { p.tB = base.tB + g; p.tB_mode = 1; }
@@ -789,10 +836,10 @@ static void launch_dense_t(const ExactProblem& p, int64_t M, int64_t N, hipStrea
 }
 
 // Scale mode: 2 when K % 64 == 0 and every scale row starts 16-byte aligned
-// (K % 512 == 0 for MXFP8, K % 256 == 0 for NVFP4), 1 when K % 64 == 0, else 0.
+// (K % 512 == 0 for MXFP8 / MXFP4, K % 256 == 0 for NVFP4), 1 when K % 64 == 0, else 0.
 static int scale_mode(int ld, int64_t K, bool vary_k) {
   if (vary_k || K % 64) return 0;
-  if (ld == 1 && K % 512 == 0) return 2;
+  if ((ld == 1 || ld == 3) && K % 512 == 0) return 2;
   if (ld == 2 && K % 256 == 0) return 2;
   return 1;
 }
@@ -822,8 +869,10 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, 
   p.a_idx = nullptr; p.a_rows = M; p.a_base = 0; p.m_valid = M; p.lda = K;
   p.B = (const uint8_t*)B; p.sB = (const uint8_t*)sB; p.tB = tB; p.tB_mode = tB_mode; p.n_valid = N; p.ldb = K;
   p.k_begin = 0; p.k_end = K; p.C = C; p.ldc = ldc;
+  // fmt: 1 MXFP8, 2 NVFP4, 3 BF16, 4 MXFP4
   if (fmt == 1) launch_dense_ld<1>(p, M, N, K, st);
   else if (fmt == 2) launch_dense_ld<2>(p, M, N, K, st);
+  else if (fmt == 4) launch_dense_ld<3>(p, M, N, K, st);
   else launch_dense_ld<0>(p, M, N, K, st);
   return hipGetLastError();
 }
@@ -885,7 +934,7 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   constexpr int BT = 128;
   const int64_t tiles_n = (N + BT - 1) / BT;
   const int64_t tiles_m_fixed = vary_k ? (M + BT - 1) / BT : 0;
-  const int64_t align = fmt == 1 ? 32 : fmt == 2 ? 16 : 8;
+  const int64_t align = (fmt == 1 || fmt == 4) ? 32 : fmt == 2 ? 16 : 8;
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, st, offsets, groups, total, vary_k, align, (int64_t)BT,
                      tiles_m_fixed, tiles_n, prefix);
   const int64_t max_tiles = vary_k ? groups * tiles_m_fixed * tiles_n : ((total + BT - 1) / BT + groups) * tiles_n;
@@ -899,7 +948,8 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   } else {
     p.m_valid = M; p.lda = total; p.n_valid = N; p.ldb = total; p.k_begin = 0; p.k_end = 0;
   }
-  const int sm = scale_mode(fmt == 1 ? 1 : fmt == 2 ? 2 : 0, p.lda, vary_k != 0);
+  const int ld = fmt == 1 ? 1 : fmt == 2 ? 2 : fmt == 4 ? 3 : 0;
+  const int sm = scale_mode(ld, p.lda, vary_k != 0);
   auto go = [&](auto LDC, auto SMC) {
     launch_grouped_t<decltype(LDC)::value, BT, decltype(SMC)::value>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
   };
@@ -911,8 +961,9 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
     else if (sm == 1) go(LDC, ic<1>{});
     else go(LDC, ic<0>{});
   };
-  if (fmt == 1) by_sm(ic<1>{});
-  else if (fmt == 2) by_sm(ic<2>{});
+  if (ld == 1) by_sm(ic<1>{});
+  else if (ld == 2) by_sm(ic<2>{});
+  else if (ld == 3) by_sm(ic<3>{});
   else by_sm(ic<0>{});
   return hipGetLastError();
 }

@@ -27,6 +27,17 @@
 
 namespace mxq {
 
+// Eight BF16 values (one uint4, element 0 first) times 2^(127 - s) (exact) -> eight E2M1
+// nibbles, RNE, element 0 in the low nibble.
+__device__ __forceinline__ uint32_t fp4x8_scaled(const uint4& v, float inv) {
+  uint32_t o = 0;
+  o = cvt_fp4x2_f32<0>(o, bf16_lo(v.x) * inv, bf16_hi(v.x) * inv);
+  o = cvt_fp4x2_f32<1>(o, bf16_lo(v.y) * inv, bf16_hi(v.y) * inv);
+  o = cvt_fp4x2_f32<2>(o, bf16_lo(v.z) * inv, bf16_hi(v.z) * inv);
+  o = cvt_fp4x2_f32<3>(o, bf16_lo(v.w) * inv, bf16_hi(v.w) * inv);
+  return o;
+}
+
 // Up to kMaxQJobs tensors per launch (e.g. the input, weight and gradient of a linear
 // layer): workgroups [block0, block0 + blocks) of the grid belong to job j.
 constexpr int kMaxQJobs = 8;
@@ -42,7 +53,8 @@ struct QJobs {
   int n;
 };
 
-template <bool DO_ROW, bool DO_COL>
+// FP4 = MXFP4 (E2M1 elements, same E8M0 blocks of 32, packed two per byte, low nibble first).
+template <bool DO_ROW, bool DO_COL, bool FP4 = false>
 __global__ void __launch_bounds__(256)
 quant_mxfp8_kernel(const QJobs jobs) {
   // job of this workgroup (static indices only: the table stays in kernel arguments)
@@ -58,9 +70,11 @@ quant_mxfp8_kernel(const QJobs jobs) {
   uint8_t* __restrict__ s_colT = jb.s_colT;
   const int row_scale_dw = jb.row_scale_dw, col_scale_dw = jb.col_scale_dw;
   const int64_t blk = (int64_t)blockIdx.x - jb.block0;
-  // Transposed FP8 tile: column cl at cl * 128; its 8-byte granule g (rows 8g .. 8g+7)
-  // sits at granule g ^ 4 * (cl / 8 % 4), which spreads one wave's writes over more banks.
-  __shared__ __attribute__((aligned(16))) uint8_t lcol[DO_COL ? 128 * 128 : 16];
+  // Transposed tile: column cl at cl * CP (128 bytes FP8, 64 FP4); its granule g (rows
+  // 8g .. 8g+7: 8 bytes FP8, 4 FP4) sits at granule g ^ 4 * (cl / 8 % 4), which spreads one
+  // wave's writes over more banks.
+  constexpr int CP = FP4 ? 64 : 128, GB = FP4 ? 4 : 8;
+  __shared__ __attribute__((aligned(16))) uint8_t lcol[DO_COL ? 128 * CP : 16];
   __shared__ uint32_t lsrow[DO_ROW ? 128 : 1];     // 4 row-scale bytes per tile row
   __shared__ uint32_t lscol[DO_COL ? 128 : 1];     // 4 column-scale bytes per tile column
   const int lane = threadIdx.x & 63;
@@ -91,14 +105,21 @@ quant_mxfp8_kernel(const QJobs jobs) {
       a = a > b ? a : b;
       b = dpp_xor2(a);
       a = a > b ? a : b;
-      const uint32_t s = e8m0_from_bf16_amax(a);
-      const float sc = e8m0_to_float(s);
-      uint32_t lo = cvt_fp8x2_bf16(0u, v[j].x, sc, false);
-      lo = cvt_fp8x2_bf16(lo, v[j].y, sc, true);
-      uint32_t hi = cvt_fp8x2_bf16(0u, v[j].z, sc, false);
-      hi = cvt_fp8x2_bf16(hi, v[j].w, sc, true);
       const int64_t r = R0 + rl0 + j;
-      if (col_ok && r < rows) *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(lo, hi);
+      uint32_t s;
+      if constexpr (FP4) {
+        s = e8m0_from_bf16_amax_e2m1(a);
+        const uint32_t packed = fp4x8_scaled(v[j], e8m0_inverse(s));
+        if (col_ok && r < rows) *reinterpret_cast<uint32_t*>(q_row + r * (cols / 2) + c / 2) = packed;
+      } else {
+        s = e8m0_from_bf16_amax(a);
+        const float sc = e8m0_to_float(s);
+        uint32_t lo = cvt_fp8x2_bf16(0u, v[j].x, sc, false);
+        lo = cvt_fp8x2_bf16(lo, v[j].y, sc, true);
+        uint32_t hi = cvt_fp8x2_bf16(0u, v[j].z, sc, false);
+        hi = cvt_fp8x2_bf16(hi, v[j].w, sc, true);
+        if (col_ok && r < rows) *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(lo, hi);
+      }
       if ((c16 & 3) == 0) reinterpret_cast<uint8_t*>(lsrow)[(rl0 + j) * 4 + (c16 >> 2)] = (uint8_t)s;
     }
   }
@@ -121,7 +142,7 @@ quant_mxfp8_kernel(const QJobs jobs) {
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       const uint32_t amax = (cc & 1) ? (cm[cc >> 1] >> 16) : (cm[cc >> 1] & 0xFFFFu);
-      const uint32_t s = e8m0_from_bf16_amax(amax);
+      const uint32_t s = FP4 ? e8m0_from_bf16_amax_e2m1(amax) : e8m0_from_bf16_amax(amax);
       const float sc = e8m0_to_float(s);
       const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
       uint32_t wd[8];
@@ -130,14 +151,21 @@ quant_mxfp8_kernel(const QJobs jobs) {
         const uint32_t p = cc >> 1;
         wd[j] = p == 0 ? v[j].x : p == 1 ? v[j].y : p == 2 ? v[j].z : v[j].w;
       }
-      // pair (row j, row j+1) of column cc -> one packed BF16x2 dword
-      uint32_t out0 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(wd[1], wd[0], sel), sc, false);
-      out0 = cvt_fp8x2_bf16(out0, __builtin_amdgcn_perm(wd[3], wd[2], sel), sc, true);
-      uint32_t out1 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(wd[5], wd[4], sel), sc, false);
-      out1 = cvt_fp8x2_bf16(out1, __builtin_amdgcn_perm(wd[7], wd[6], sel), sc, true);
       const int cl = 8 * c16 + cc;
       const int g = (4 * w + m) ^ ((c16 & 3) * 4);
-      *reinterpret_cast<uint2*>(lcol + cl * 128 + g * 8) = make_uint2(out0, out1);
+      if constexpr (FP4) {
+        // rows j of column cc -> 8 nibbles, row order
+        const uint4 col8 = make_uint4(__builtin_amdgcn_perm(wd[1], wd[0], sel), __builtin_amdgcn_perm(wd[3], wd[2], sel),
+                                      __builtin_amdgcn_perm(wd[5], wd[4], sel), __builtin_amdgcn_perm(wd[7], wd[6], sel));
+        *reinterpret_cast<uint32_t*>(lcol + cl * CP + g * GB) = fp4x8_scaled(col8, e8m0_inverse(s));
+      } else {
+        // pair (row j, row j+1) of column cc -> one packed BF16x2 dword
+        uint32_t out0 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(wd[1], wd[0], sel), sc, false);
+        out0 = cvt_fp8x2_bf16(out0, __builtin_amdgcn_perm(wd[3], wd[2], sel), sc, true);
+        uint32_t out1 = cvt_fp8x2_bf16(0u, __builtin_amdgcn_perm(wd[5], wd[4], sel), sc, false);
+        out1 = cvt_fp8x2_bf16(out1, __builtin_amdgcn_perm(wd[7], wd[6], sel), sc, true);
+        *reinterpret_cast<uint2*>(lcol + cl * CP + g * GB) = make_uint2(out0, out1);
+      }
       if (m == 0) reinterpret_cast<uint8_t*>(lscol)[cl * 4 + w] = (uint8_t)s;
     }
   }
@@ -145,16 +173,19 @@ quant_mxfp8_kernel(const QJobs jobs) {
 
   const int t = threadIdx.x;
   if (DO_COL) {
-    // 16-byte chunk i = k * 256 + t of the tile's transposed copy: column i / 8, rows 16 (i % 8) ..
+    // 16-byte chunk i = k * 256 + t of the tile's transposed copy: column i / NCH, rows
+    // (128 / NCH) (i % NCH) .. (FP8: 8 chunks of 16 rows; FP4: 4 chunks of 32 rows).
     // rows % 32 == 0, so a chunk is either wholly inside the tensor or wholly outside.
+    constexpr int NCH = CP / 16, RPC = 128 / NCH;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NCH / 2; ++k) {
       const int i = k * 256 + t;
-      const int cl = i >> 3, ch = i & 7;
-      const int g0 = (2 * ch) ^ (((cl >> 3) & 3) * 4);   // granules 2ch, 2ch+1 stay adjacent
-      const int64_t col = C0 + cl, r = R0 + 16 * ch;
+      const int cl = i / NCH, ch = i % NCH;
+      const int g0 = (ch * (16 / GB)) ^ (((cl >> 3) & 3) * 4);   // the chunk's granules stay adjacent
+      const int64_t col = C0 + cl, r = R0 + RPC * ch;
       if (col < cols && r < rows)
-        *reinterpret_cast<uint4*>(q_colT + col * rows + r) = *reinterpret_cast<const uint4*>(lcol + cl * 128 + g0 * 8);
+        *reinterpret_cast<uint4*>(q_colT + col * (FP4 ? rows / 2 : rows) + (FP4 ? r / 2 : r)) =
+            *reinterpret_cast<const uint4*>(lcol + cl * CP + g0 * GB);
     }
     if (t < 128 && C0 + t < cols) {
       const int64_t sb = rows / 32;
@@ -180,9 +211,10 @@ quant_mxfp8_kernel(const QJobs jobs) {
 }
 
 // Tensors of one launch must request the same copies (row, column or both).
-hipError_t launch_quant_mxfp8_multi(int n, const void* const* x, const int64_t* rows, const int64_t* cols,
-                                    const int64_t* ld_x, void* const* q_row, void* const* s_row,
-                                    void* const* q_colT, void* const* s_colT, hipStream_t stream) {
+template <bool FP4>
+static hipError_t launch_quant_mx_multi(int n, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                        const int64_t* ld_x, void* const* q_row, void* const* s_row,
+                                        void* const* q_colT, void* const* s_colT, hipStream_t stream) {
   QJobs jobs;
   jobs.n = n;
   int64_t blocks = 0;
@@ -201,10 +233,21 @@ hipError_t launch_quant_mxfp8_multi(int n, const void* const* x, const int64_t* 
   if (blocks == 0) return hipSuccess;
   dim3 grid((unsigned)blocks), block(256);
   const bool do_row = q_row[0] != nullptr, do_col = q_colT[0] != nullptr;
-  if (do_row && do_col) hipLaunchKernelGGL((quant_mxfp8_kernel<true, true>), grid, block, 0, stream, jobs);
-  else if (do_row) hipLaunchKernelGGL((quant_mxfp8_kernel<true, false>), grid, block, 0, stream, jobs);
-  else hipLaunchKernelGGL((quant_mxfp8_kernel<false, true>), grid, block, 0, stream, jobs);
+  if (do_row && do_col) hipLaunchKernelGGL((quant_mxfp8_kernel<true, true, FP4>), grid, block, 0, stream, jobs);
+  else if (do_row) hipLaunchKernelGGL((quant_mxfp8_kernel<true, false, FP4>), grid, block, 0, stream, jobs);
+  else hipLaunchKernelGGL((quant_mxfp8_kernel<false, true, FP4>), grid, block, 0, stream, jobs);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp8_multi(int n, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                    const int64_t* ld_x, void* const* q_row, void* const* s_row,
+                                    void* const* q_colT, void* const* s_colT, hipStream_t stream) {
+  return launch_quant_mx_multi<false>(n, x, rows, cols, ld_x, q_row, s_row, q_colT, s_colT, stream);
+}
+
+hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q_row, void* s_row,
+                              void* q_colT, void* s_colT, hipStream_t stream) {
+  return launch_quant_mx_multi<true>(1, &x, &rows, &cols, &ld_x, &q_row, &s_row, &q_colT, &s_colT, stream);
 }
 
 hipError_t launch_quant_mxfp8(const void* x, int64_t rows, int64_t cols, int64_t ld_x,

@@ -51,6 +51,19 @@ def test_quantize_mxfp8_validation():
     assert q8(P, 0, 32, 32, P, P, P, P, None) == 0                     # empty: no-op
 
 
+def test_quantize_mxfp4_validation():
+    q4 = B.lib().quantize_mxfp4
+    assert q4(None, 32, 32, 32, P, P, None, None, None) == 1           # x NULL
+    assert q4(P, 32, 32, 32, None, None, None, None, None) == 1        # no output
+    assert q4(P, 32, 32, 32, None, None, P, None, None) == 1           # half a pair
+    assert q4(P, 32, 48, 48, P, P, None, None, None) == 2              # cols % 32
+    assert q4(P, 48, 32, 32, None, None, P, P, None) == 2              # rows % 32 with colwise
+    assert q4(P, 32, 64, 32, P, P, None, None, None) == 2              # ld_x < cols
+    assert q4(P, 32, 32, 32, MIS, P, None, None, None) == 3            # misaligned q_row
+    assert q4(P, 32, 32, 36, P, P, None, None, None) == 3              # ld_x % 8
+    assert q4(P, 0, 32, 32, P, P, P, P, None) == 0                     # empty: no-op
+
+
 def multi(descs):
     arr = (B._Mxfp8Tensor * max(len(descs), 1))(*[B._Mxfp8Tensor(*d) for d in descs])
     return B.lib().quantize_mxfp8_multi(ctypes.cast(arr, ctypes.c_void_p), len(descs), None)
@@ -105,11 +118,15 @@ def test_gemm_validation():
     assert g(1, 32, 32, 64, P, P, None, 0, P, P, None, 0, P, 16, None) == 2      # ldc < N
     assert g(1, 32, 32, 64, MIS, P, None, 0, P, P, None, 0, P, 32, None) == 3
     assert g(1, 0, 32, 64, P, P, None, 0, P, P, None, 0, P, 32, None) == 0       # empty
+    assert g(4, 32, 32, 48, P, P, None, 0, P, P, None, 0, P, 32, None) == 2      # MXFP4 K % 32
+    assert g(4, 32, 32, 64, P, P, None, 0, P, None, None, 0, P, 32, None) == 1   # MXFP4 scales missing
+    assert g(4, 32, 32, 64, P, P, None, 0, MIS, P, None, 0, P, 32, None) == 3
     gg = L.grouped_gemm_block_scaled
     assert gg(1, 4, P, 0, 64, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, None, 0, None) == 5
     assert gg(2, 4, P, 1, 64, 32, 32, 64, None, 0, P, P, P, 0, P, P, P, 2, P, P, 4096, None) == 4   # NVFP4 vary_k
     assert gg(1, 4, None, 0, 64, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, P, 4096, None) == 1
     assert gg(1, 0, P, 0, 0, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, None, 0, None) == 0
+    assert gg(4, 4, P, 1, 48, 32, 32, 0, None, 0, P, P, None, 0, P, P, None, 0, P, P, 4096, None) == 2   # MXFP4 total % 32
 
 
 def test_dequant_and_moe_validation():
@@ -117,6 +134,8 @@ def test_dequant_and_moe_validation():
     assert L.dequantize(2, P, P, None, 0, 0, 4, 32, P, 0, None) == 1      # NVFP4 without t
     assert L.dequantize(1, P, P, None, 0, 0, 4, 48, P, 0, None) == 2
     assert L.dequantize(3, P, P, None, 0, 0, 4, 32, P, 0, None) == 4
+    assert L.dequantize(4, P, P, None, 0, 0, 4, 48, P, 0, None) == 2      # MXFP4 cols % 32
+    assert L.dequantize(4, P, None, None, 0, 0, 4, 32, P, 0, None) == 1
     dt = L.dequantize_transposed
     assert dt(2, P, P, None, 0, 1, 64, 32, None, 64, P, 64, None) == 1       # NVFP4 without t
     assert dt(1, P, P, None, 0, 1, 64, 48, None, 64, P, 64, None) == 2       # cols % 32 (MXFP8)
@@ -136,6 +155,7 @@ def test_scale_and_workspace_sizes():
     assert B.scale_bytes(B.MXFP8, 256, 512) == 256 * 16
     assert B.scale_bytes(B.NVFP4, 4096, 2048) == 4096 * 128
     assert B.scale_bytes(B.MXFP8, 4, 48) == 0
+    assert B.scale_bytes(B.MXFP4, 128, 1024) == 128 * 32
     L = B.lib()
     assert L.mxq_workspace_bytes(B.OP_QUANTIZE_NVFP4, 0, 0, 3) >= 12
     assert L.mxq_workspace_bytes(B.OP_GROUPED_GEMM, 128, 0, 0) >= 129 * 8

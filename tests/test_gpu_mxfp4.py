@@ -1,0 +1,198 @@
+"""GPU parity for MXFP4 (E2M1 elements, one E8M0 scale per 32): the quantizer's
+rowwise and transposed columnwise copies byte for byte against the oracle,
+dequantize bit for bit, and the dense and grouped GEMMs against the FP64 product
+of the oracle's exact dequantized operands (normwise 2e-5; exactly, where every
+partial sum is representable)."""
+
+import numpy as np
+import pytest
+import torch
+
+import microscaling_precision_quantization_amd as mxq
+from microscaling_precision_quantization_amd import inputs
+from oracle import formats as F
+from oracle import gemm as og
+from oracle import moe as omoe
+from oracle import mxfp4 as om4
+from tests.gpu_util import assert_bytes_equal, assert_gemm_close, dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(v):
+    return inputs.to_bf16_bits(np.asarray(v, dtype=np.float64))
+
+
+def check_mxfp4(xb, rowwise=True, colwise=True, what="", x_dev=None):
+    x = dev_bf16(xb) if x_dev is None else x_dev
+    qr, sr, qc, sc = mxq.quantize_mxfp4(x, rowwise, colwise)
+    if rowwise:
+        eq, es = om4.quantize_rowwise(xb)
+        assert_bytes_equal(host(qr), eq, f"{what} q_row")
+        assert_bytes_equal(host(sr), es, f"{what} s_row")
+    if colwise:
+        eq, es = om4.quantize_colwise(xb)
+        assert_bytes_equal(host(qc), eq, f"{what} q_colT")
+        assert_bytes_equal(host(sc), es, f"{what} s_colT")
+    return qr, sr, qc, sc
+
+
+def edge_case_tensor(rows=64, cols=256, seed=0):
+    """Zero blocks with -0, the largest BF16, exact E2M1 grids at several binades,
+    amax at the 3 / 4 / 6 boundaries, BF16 subnormals and random data."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, cols)) * 3
+    x[0:32, 0:32] = 0.0
+    xb = bf16(x)
+    xb[0:32, 0:32][::3, ::5] = 0x8000
+    xb[32, 32:64] = 0x7F7F
+    xb[33, 32:64] = 0xFF7F
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    xb[34, 64:96] = bf16(grid[g.integers(0, 8, 32)] * g.choice([-1, 1], 32) * 2.0 ** 5)
+    xb[35, 96:128] = bf16(np.r_[3.0, 3.03125, 4.0, 6.0, 6.0625, np.zeros(27)] * 2.0 ** -3)
+    xb[36:68 if rows >= 68 else rows, 128:160] = bf16(g.integers(-127, 128, (min(32, rows - 36), 32)) * 2.0 ** -133)
+    xb[37, 160:192] = bf16(g.standard_normal(32) * 1e-30)
+    return xb
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (128, 128), (96, 160), (160, 96), (4128, 96), (64, 416), (256, 1024)])
+def test_mxfp4_quantize_ragged_tiles(shape):
+    g = inputs.rng(120, shape[0] * 7 + shape[1])
+    xb = inputs.to_bf16_bits(g.standard_normal(shape) * g.lognormal(0, 1, (shape[0], 1)))
+    check_mxfp4(xb, what=str(shape))
+
+
+@pytest.mark.parametrize("shape", [(37, 64), (1, 32), (129, 160)])
+def test_mxfp4_rowwise_only_any_rows(shape):
+    xb = inputs.normal_bf16(inputs.rng(121, shape[0]), shape, 1.0)
+    check_mxfp4(xb, rowwise=True, colwise=False, what=f"rowwise {shape}")
+
+
+def test_mxfp4_colwise_only_strided_and_edge_blocks():
+    xb = inputs.normal_bf16(inputs.rng(122, 0), (64, 320), 1.0)
+    wide = dev_bf16(xb)
+    check_mxfp4(np.ascontiguousarray(xb[:, :256]), what="strided", x_dev=wide[:, :256])
+    check_mxfp4(xb, rowwise=False, colwise=True, what="colwise only")
+    check_mxfp4(edge_case_tensor(), what="edge cases")
+    check_mxfp4(edge_case_tensor(rows=160, cols=288, seed=3), what="edge cases 160x288")
+
+
+def test_mxfp4_dequantize_exact():
+    xb = edge_case_tensor(rows=64, cols=256, seed=5)
+    qr, sr, _, _ = mxq.quantize_mxfp4(dev_bf16(xb), True, False)
+    ref = om4.dequantize_exact(host(qr), host(sr))            # FP64; exact in FP32 below 2^128
+    with np.errstate(over="ignore"):                          # 4 * 2^126 (largest-BF16 block) -> Inf
+        ref32 = ref.astype(np.float32)
+    f32 = host(mxq.dequantize(mxq.MXFP4, qr, sr, out_dtype=torch.float32))
+    assert_bytes_equal(f32.view(np.uint32), ref32.view(np.uint32), "mxfp4 -> f32")
+    b16 = host(mxq.dequantize(mxq.MXFP4, qr, sr))
+    assert_bytes_equal(b16, F.f32_to_bf16_bits(ref32), "mxfp4 -> bf16")
+
+
+def m4_operands(xb, col=False):
+    qr, sr, qc, sc = mxq.quantize_mxfp4(dev_bf16(xb), rowwise=not col, colwise=col)
+    q, s = (qc, sc) if col else (qr, sr)
+    return q, s, om4.dequantize_exact(host(q), host(s))
+
+
+@pytest.mark.parametrize("mnk", [(300, 200, 96), (32, 32, 32), (257, 513, 160), (64, 1000, 1024), (128, 256, 576)])
+def test_mxfp4_gemm_dense(mnk):
+    """K = 96 / 160: partial K stages and one-byte scale loads; 576: per-stage scale
+    loads; 1024: 16-byte scale chunks with 256-K stages."""
+    M, N, K = mnk
+    g = inputs.rng(123, M + N + K)
+    a = inputs.to_bf16_bits(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))
+    b = inputs.normal_bf16(g, (N, K), 0.5)
+    qa, sa, ah = m4_operands(a)
+    qb, sb, bh = m4_operands(b)
+    c = mxq.gemm_block_scaled(mxq.MXFP4, qa, sa, qb, sb)
+    assert_gemm_close(host(c), og.gemm_tn_fp64(ah, bh), f"mxfp4 {mnk}")
+
+
+@pytest.mark.parametrize("K", [512, 544, 576])
+def test_mxfp4_gemm_256_tiles_ragged(K):
+    M, N = 4196, 3112
+    g = inputs.rng(124, K)
+    a = inputs.to_bf16_bits(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))
+    b = inputs.normal_bf16(g, (N, K), 0.05)
+    qa, sa, ah = m4_operands(a)
+    qb, sb, bh = m4_operands(b)
+    c = host(mxq.gemm_block_scaled(mxq.MXFP4, qa, sa, qb, sb))
+    rows = np.r_[0:64, M - 100:M]
+    assert_gemm_close(c[rows], og.gemm_tn_fp64(ah[rows], bh), f"mxfp4 256 tiles K={K}")
+
+
+def test_mxfp4_gemm_integer_sums_are_exact():
+    """Operands whose every partial sum is an integer below 2^24: the FP32 result
+    must equal the exact product bit for bit (no accumulation may lose a bit)."""
+    g = inputs.rng(125, 0)
+    M, N, K = 192, 160, 1024
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    a = grid[g.integers(0, 8, (M, K))] * g.choice([-1, 1], (M, K))
+    b = grid[g.integers(0, 8, (N, K))] * g.choice([-1, 1], (N, K))
+    a[:, ::32] = 6.0                                  # every block's amax is 6: scale 2^0
+    b[:, ::32] = -6.0
+    a *= 2.0                                           # multiples of 1 ...
+    b *= 4.0                                           # ... and of 2: products are integers
+    qa, sa, ah = m4_operands(bf16(a))
+    qb, sb, bh = m4_operands(bf16(b))
+    assert np.array_equal(ah, a) and np.array_equal(bh, b)
+    c = host(mxq.gemm_block_scaled(mxq.MXFP4, qa, sa, qb, sb))
+    ref = og.gemm_tn_fp64(ah, bh)
+    assert np.max(np.abs(ref)) < 2 ** 24
+    assert np.array_equal(c.astype(np.float64), ref)
+
+
+def test_mxfp4_linear_fprop_dgrad_wgrad():
+    """One quantize per tensor serves the three GEMMs of a linear layer."""
+    g = inputs.rng(126, 0)
+    T, N, K = 512, 384, 640
+    x = inputs.to_bf16_bits(g.standard_normal((T, K)) * g.lognormal(0, 1, (T, 1)))
+    w = inputs.normal_bf16(g, (N, K), 0.02)
+    dy = inputs.normal_bf16(g, (T, N), 1e-3)
+    xq, wq, dq = (mxq.quantize_mxfp4(dev_bf16(v)) for v in (x, w, dy))
+    deq = lambda q, s: om4.dequantize_exact(host(q), host(s))
+    y = mxq.gemm_block_scaled(mxq.MXFP4, xq[0], xq[1], wq[0], wq[1])
+    assert_gemm_close(host(y), og.gemm_tn_fp64(deq(xq[0], xq[1]), deq(wq[0], wq[1])), "fprop")
+    dx = mxq.gemm_block_scaled(mxq.MXFP4, dq[0], dq[1], wq[2], wq[3])
+    assert_gemm_close(host(dx), og.gemm_tn_fp64(deq(dq[0], dq[1]), deq(wq[2], wq[3])), "dgrad")
+    dw = mxq.gemm_block_scaled(mxq.MXFP4, dq[2], dq[3], xq[2], xq[3])
+    assert_gemm_close(host(dw), og.gemm_tn_fp64(deq(dq[2], dq[3]), deq(xq[2], xq[3])), "wgrad")
+
+
+def test_mxfp4_grouped_vary_m_gather():
+    g = inputs.rng(127, 0)
+    T, H, G, k, N = 96, 256, 8, 2, 192
+    x = inputs.to_bf16_bits(g.standard_normal((T, H)) * g.lognormal(0, 1, (T, 1)))
+    w = inputs.normal_bf16(g, (G * N, H), 0.02)
+    logits = g.standard_normal((T, G)).astype(np.float32)
+    logits[:, 5] = -50.0                                   # expert 5 receives no tokens
+    r = inputs.route_topk(logits, k)
+    qx, sx, _, _ = mxq.quantize_mxfp4(dev_bf16(x), True, False)
+    qw, sw, _, _ = mxq.quantize_mxfp4(dev_bf16(w), True, False)
+    idx = dev(r.row_index.astype(np.int32))
+    c = mxq.grouped_gemm_block_scaled(mxq.MXFP4, dev(r.offsets.astype(np.int64)), qx, qw, N=N, K=H, sA=sx, sB=sw,
+                                      a_row_index=idx, a_rows=T)
+    xh = om4.dequantize_exact(host(qx), host(sx))
+    rows = np.where(r.row_index[:, None] >= 0, xh[np.clip(r.row_index, 0, T - 1)], 0.0)
+    ref = omoe.grouped_gemm_ref(rows, r.offsets, om4.dequantize_exact(host(qw), host(sw)).reshape(G, N, H))
+    assert_gemm_close(host(c), ref, "mxfp4 grouped gather")
+
+
+def test_mxfp4_grouped_vary_k_wgrad():
+    g = inputs.rng(128, 0)
+    G, M, N = 5, 96, 160
+    sizes = np.array([64, 0, 160, 32, 256])
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    S = int(off[-1])
+    a = inputs.normal_bf16(g, (M, S), 1.0)
+    b = inputs.normal_bf16(g, (N, S), 1.0)
+    qa, sa, _, _ = mxq.quantize_mxfp4(dev_bf16(a), True, False)
+    qb, sb, _, _ = mxq.quantize_mxfp4(dev_bf16(b), True, False)
+    c = host(mxq.grouped_gemm_block_scaled(mxq.MXFP4, dev(off), qa, qb, N=N, K=0, sA=sa, sB=sb, vary_k=True, M=M))
+    ah, bh = om4.dequantize_exact(host(qa), host(sa)), om4.dequantize_exact(host(qb), host(sb))
+    for e in range(G):
+        if sizes[e] == 0:
+            assert np.all(c[e] == 0.0)
+        else:
+            assert_gemm_close(c[e], ah[:, off[e]:off[e + 1]] @ bh[:, off[e]:off[e + 1]].T, f"group {e}")

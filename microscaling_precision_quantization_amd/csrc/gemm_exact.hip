@@ -1,9 +1,10 @@
-// Exact-operand GEMMs on the gfx950 16-bit MFMAs (v_mfma_f32_32x32x16_bf16/f16):
+// Block-scaled GEMMs with FP32-grade accumulation:
 //   C[m, n] = tA tB * sum_k A_hat[m, k] B_hat[n, k]   ("TN", FP32 output)
 //
-// Every operand value is formed EXACTLY in a 16-bit format right before the
-// matrix core consumes it, and the matrix core accumulates at FP32 precision
-// (measured on MI355X: 2^20 + 2^-3 sums exactly at every operand position):
+// MXFP8, NVFP4 and BF16 run on the gfx950 16-bit MFMAs (v_mfma_f32_32x32x16_bf16/f16):
+// every operand value is formed EXACTLY in a 16-bit format right before the matrix
+// core consumes it, and the matrix core accumulates at FP32 precision (measured on
+// MI355X: 2^20 + 2^-3 sums exactly at every operand position):
 //   * MXFP8 (E4M3, E8M0 per 32 along K): q * 2^(s-127) has 4 significant bits and
 //     stays in BF16 range, so the gfx950 scaled convert (which applies the
 //     power-of-two scale exactly) yields it in BF16 -> BF16 MFMA.
@@ -11,10 +12,13 @@
 //     at most 6 significant bits and lies in [2^-10, 2688], inside FP16's normal
 //     range. S = 2^e * m (m = 1..1.875): the scaled convert applies 2^e, a packed
 //     FP16 multiply applies m (exact) -> FP16 MFMA; tA tB in the epilogue.
-//   * MXFP4 (E2M1, E8M0 per 32 along K): q * 2^(s-127) has 2 significant bits and
-//     lies in [2^-128, 6 * 2^125] for s <= 252, where BF16 holds it exactly (the
-//     smallest values as BF16 subnormals) -> the scaled convert yields it in BF16
-//     -> BF16 MFMA. (s = 253 arises only for blocks whose amax exceeds 1.5 * 2^127.)
+//   * MXFP4 (E2M1, E8M0 per 32 along K) runs on the native FP4 form of the scaled
+//     MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), which applies the E8M0 scales itself.
+//     Measured on MI355X: lane l supplies row l % 32 and the whole 32-K block h = l / 32
+//     of the instruction's 64 K (16 bytes, low nibble first), with that block's scale;
+//     products of one block sum exactly, and a result differs from the exact value by
+//     at most 2^-23.6 of the sum of the magnitudes of its terms (FP32-grade, unlike the
+//     FP8 form's ~2^-13 window), so this path meets the same accuracy bound.
 //   * BF16 operands as they are -> BF16 MFMA.
 // Definitions: microscaling blocks along the reduction dimension ("Miles
 // Blackwell RL", remio.ai, section "Un Cuantizador Compartido Es el Mecanismo
@@ -29,9 +33,9 @@
 // (buffer_load_dwordx4 ... lds: lane l of a wave instruction lands at LDS base +
 // 16 l), through a 16-byte XOR swizzle chosen so that each 16-lane fragment read
 // (ds_read_b128) covers all 64 banks (measured conflict-free). A stage holds 64 K
-// (128 B/row BF16, 64 B/row MXFP8, 32 B/row NVFP4), or 128 B/row for every format
-// in the dense kernels when K allows chunked scales (128 K MXFP8, 256 K NVFP4:
-// fewer barriers, larger loads). NS stages keep NS - 1 tiles in flight; explicit
+// (128 B/row BF16, 64 B/row MXFP8, 32 B/row NVFP4 / MXFP4), or 128 B/row for every
+// format in the dense kernels when K allows chunked scales (128 K MXFP8, 256 K NVFP4
+// and MXFP4: fewer barriers, larger loads). NS stages keep NS - 1 tiles in flight; explicit
 // vmcnt waits + one barrier per stage. Scales travel either per stage into
 // 4-byte LDS slots, or as 16-byte chunks per row (16 blocks) double-buffered in
 // LDS and read into registers once per chunk. Out-of-range rows and K chunks
@@ -225,15 +229,13 @@ __device__ __forceinline__ v8bf mx_to_bf16(uint32_t w0, uint32_t w1, float sc) {
   return r;
 }
 
-// 8 E2M1 values (one dword, low nibble first) -> 8 BF16, each exactly q * 2^(s-127).
-__device__ __forceinline__ v8bf mx4_to_bf16(uint32_t w, float sc) {
-  v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
-  v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
-  v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
-  v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
-  v8bf r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1]; r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
+// 32 E2M1 values (16 bytes) as the A/B operand of the FP4 form of the scaled MFMA, which
+// reads the low four dwords.
+__device__ __forceinline__ v8i fp4_operand(const u32x4& r) {
+  v8i v;
+  v[0] = (int)r.x; v[1] = (int)r.y; v[2] = (int)r.z; v[3] = (int)r.w;
+  v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
+  return v;
 }
 
 // 8 E2M1 values (one dword, low nibble first) times the E4M3 block scale S -> 8
@@ -576,25 +578,19 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         hook(JJ);
       });
     } else if constexpr (LD == 3) {
-      v8bf fa[4][TI];          // [dword][i]: 8 consecutive K each
+      // Native E2M1 x E2M1 scaled MFMA, 64 K per instruction: lane half h supplies the
+      // whole 32-K block of its chunk and that block's E8M0 byte (the operand layout the
+      // sub-block reads already have).
+      v8i fa[TI];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const float s = mx_cvt_scale(fr.sc[i]);
-        fa[0][i] = mx4_to_bf16(fr.raw[i].x, s);
-        fa[1][i] = mx4_to_bf16(fr.raw[i].y, s);
-        fa[2][i] = mx4_to_bf16(fr.raw[i].z, s);
-        fa[3][i] = mx4_to_bf16(fr.raw[i].w, s);
-      }
+      for (int i = 0; i < TI; ++i) fa[i] = fp4_operand(fr.raw[i]);
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
-        const float s = mx_cvt_scale(fr.sc[TI + j]);
-        static_for<0, 4>([&](auto DW) {
-          constexpr int d = decltype(DW)::value;
-          const uint32_t w = d == 0 ? fr.raw[TI + j].x : d == 1 ? fr.raw[TI + j].y : d == 2 ? fr.raw[TI + j].z : fr.raw[TI + j].w;
-          const v8bf fb = mx4_to_bf16(w, s);
+        const v8i fb = fp4_operand(fr.raw[TI + j]);
 #pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[d][i], fb, acc[i][j], 0, 0, 0);
-        });
+        for (int i = 0; i < TI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb, acc[i][j], 4, 4, 0, (int)fr.sc[i], 0,
+                                                                     (int)fr.sc[TI + j]);
         hook(JJ);
       });
     } else {

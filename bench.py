@@ -55,6 +55,7 @@ KERNEL_SOURCES = ["microscaling_precision_quantization_amd/csrc/gemm_exact.hip",
 
 # algorithmic bytes per element
 MX_ROWCOL = 2 + 1 + 1 + 2 / 32          # BF16 read + two E4M3 copies + two E8M0 scale sets
+MX4_ROWCOL = 2 + 0.5 + 0.5 + 2 / 32      # BF16 read + two packed E2M1 copies + two E8M0 scale sets
 NV_TOKEN = 2 + 0.5 + 1 / 16             # BF16 read + packed E2M1 + E4M3 per 16 (+ 4 B per row)
 NV_TENSOR = 2 + NV_TOKEN                # + the amax pass over the BF16 input
 NV_2D_BOTH = 2 + 2 + 2 * (0.5 + 1 / 16)  # 16x16 blocks: amax pass + quantize pass, row + transposed copies
@@ -114,6 +115,7 @@ class Linear:
         base = {k: to_dev(torch, dev, v) for k, v in self.host.items()}
         self.sets = [{k: v.clone() for k, v in base.items()} for _ in range(self.N_SETS)]
         self.layer = pipeline.LinearMxfp8(self.T, self.DIN, self.DOUT, dev)
+        self.layer4 = pipeline.LinearMxfp4(self.T, self.DIN, self.DOUT, dev)
         self.gemm_flop = 2 * self.T * self.DOUT * self.DIN            # each of fprop, dgrad, wgrad
         self.step_flop = 3 * self.gemm_flop
         self.config = {"workload": "MXFP8 linear layer: X (2048,2048) N(0,1), W (8192,2048) N(0,0.02), "
@@ -129,6 +131,16 @@ class Linear:
         n_el = self.T * self.DIN + self.DOUT * self.DIN + self.T * self.DOUT
         out = [Stage("quantize_mxfp8_rowcol", lambda: L.quantize(s["x"], s["w"], s["dy"]), n_el * MX_ROWCOL, "hbm")]
         out += [Stage("gemm_block_scaled_mxfp8", (lambda g=g: L.gemm(g)), self.gemm_flop, "mfma", "bf16")
+                for g in ("fprop", "dgrad", "wgrad")]
+        return out
+
+    def extra_components(self):
+        """The same layer in MXFP4 (E2M1 + E8M0 per 32) on the native FP4 scaled MFMA,
+        outside the step: one row+col quantize launch of X, W, dY and the three GEMMs."""
+        s, L4 = self.sets[0], self.layer4
+        n_el = self.T * self.DIN + self.DOUT * self.DIN + self.T * self.DOUT
+        out = [Stage("quantize_mxfp4_rowcol", lambda: L4.quantize(s["x"], s["w"], s["dy"]), n_el * MX4_ROWCOL, "hbm")]
+        out += [Stage("gemm_block_scaled_mxfp4_" + g, (lambda g=g: L4.gemm(g)), self.gemm_flop, "mfma", "fp4")
                 for g in ("fprop", "dgrad", "wgrad")]
         return out
 
@@ -384,10 +396,16 @@ class Stress:
         return out
 
     def extra_components(self):
-        """Stochastically rounded RHT + NVFP4 of the gradient operand A (outside the step)."""
+        """Outside the step: stochastically rounded RHT + NVFP4 of the gradient operand A;
+        MXFP4 row+col quantization of A and B and the MXFP4 GEMM at 8192^3 (native FP4
+        scaled MFMA) beside the step's NVFP4 GEMM (exact FP16-MFMA path)."""
         n = self.N
-        return [Stage("quantize_nvfp4_rht_colwise_sr", lambda: self.st.quantize_rht_sr(self.sets[0]["a"], 1234),
-                      n * n * (2 + 2 + 0.5 + 1 / 16), "hbm")]
+        s = self.sets[0]
+        return [Stage("quantize_nvfp4_rht_colwise_sr", lambda: self.st.quantize_rht_sr(s["a"], 1234),
+                      n * n * (2 + 2 + 0.5 + 1 / 16), "hbm"),
+                Stage("quantize_mxfp4_rowcol", lambda: self.st.quantize_mxfp4(s["a"], s["b"]), 2 * n * n * MX4_ROWCOL,
+                      "hbm"),
+                Stage("gemm_block_scaled_mxfp4", self.st.mxfp4_gemm, 2 * n ** 3, "mfma", "fp4")]
 
     def cpu_baseline(self):
         from oracle import gemm as og
@@ -511,7 +529,7 @@ def main():
                       "flop_per_step": int(c["work"] / K)})
             if c["peak"] in ("bf16", "fp16") and name.find("mxfp8") >= 0:
                 d["frac_mfma_fp8"] = round(tf / MFMA_PEAK_TFLOPS["fp8"], 4)
-            if name.find("nvfp4") >= 0:
+            if name.find("nvfp4") >= 0 or name.find("mxfp4") >= 0:
                 d["frac_mfma_fp4"] = round(tf / MFMA_PEAK_TFLOPS["fp4"], 4)
         if c.get("outside_step"):
             d["outside_step"] = True

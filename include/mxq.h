@@ -142,6 +142,18 @@ mxq_status quantize_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
                           void* stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_mxfp4_multi -- quantize_mxfp4 over several tensors in one launch (the
+ * same bytes as `count` calls of quantize_mxfp4).
+ *   Defined by: as quantize_mxfp4 (7minutos.es, sections "Que es realmente NVFP4" and
+ *   "NVFP4 frente a MXFP4").
+ *   tensors : HOST array of `count` mxq_mxfp8_tensor descriptors (the descriptor of
+ *             quantize_mxfp8_multi; q_row and q_colT receive packed E2M1), with the
+ *             same rules: 1 <= count <= MXQ_MXFP8_MULTI_MAX, one set of copies for
+ *             all tensors, validation before any launch, empty tensors skipped.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_mxfp4_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream);
+
+/* ---------------------------------------------------------------------------
  * quantize_nvfp4_per_token -- NVFP4 with one FP32 scale per token (row),
  * computed online in the same kernel that emits the packed E2M1 values and the
  * E4M3 block scales.

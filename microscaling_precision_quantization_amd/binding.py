@@ -32,6 +32,7 @@ _SIGS = {
     "quantize_mxfp8": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_mxfp8_multi": [_c_void_p, _int, _c_void_p],
     "quantize_mxfp4": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "quantize_mxfp4_multi": [_c_void_p, _int, _c_void_p],
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
@@ -162,9 +163,7 @@ class _Mxfp8Tensor(ctypes.Structure):
                 ("s_row", _c_void_p), ("q_colT", _c_void_p), ("s_colT", _c_void_p)]
 
 
-def quantize_mxfp8_multi(xs, outs):
-    """quantize_mxfp8 of several BF16 tensors in one launch; outs[i] = (q_row, s_row,
-    q_colT, s_colT) preallocated (a skipped copy is (None, None) in its slots)."""
+def _mx_multi(fn: str, xs, outs):
     n = len(xs)
     arr = (_Mxfp8Tensor * n)()
     for i, (x, o) in enumerate(zip(xs, outs)):
@@ -172,8 +171,20 @@ def quantize_mxfp8_multi(xs, outs):
         q_row, s_row, q_col, s_col = o
         arr[i] = _Mxfp8Tensor(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0),
                               *(None if t is None else t.data_ptr() for t in (q_row, s_row, q_col, s_col)))
-    _check("quantize_mxfp8_multi", lib().quantize_mxfp8_multi(ctypes.cast(arr, _c_void_p), n, _stream(xs[0].device)))
+    _check(fn, getattr(lib(), fn)(ctypes.cast(arr, _c_void_p), n, _stream(xs[0].device)))
     return outs
+
+
+def quantize_mxfp8_multi(xs, outs):
+    """quantize_mxfp8 of several BF16 tensors in one launch; outs[i] = (q_row, s_row,
+    q_colT, s_colT) preallocated (a skipped copy is (None, None) in its slots)."""
+    return _mx_multi("quantize_mxfp8_multi", xs, outs)
+
+
+def quantize_mxfp4_multi(xs, outs):
+    """quantize_mxfp4 of several BF16 tensors in one launch; outs as quantize_mxfp8_multi
+    with packed (R, C/2) / (C, R/2) element buffers."""
+    return _mx_multi("quantize_mxfp4_multi", xs, outs)
 
 
 def quantize_nvfp4_per_token(x: torch.Tensor):

@@ -12,6 +12,8 @@ hipError_t launch_quant_mxfp8(const void*, int64_t, int64_t, int64_t, void*, voi
 hipError_t launch_quant_mxfp8_multi(int, const void* const*, const int64_t*, const int64_t*, const int64_t*,
                                     void* const*, void* const*, void* const*, void* const*, hipStream_t);
 hipError_t launch_quant_mxfp4(const void*, int64_t, int64_t, int64_t, void*, void*, void*, void*, hipStream_t);
+hipError_t launch_quant_mxfp4_multi(int, const void* const*, const int64_t*, const int64_t*, const int64_t*,
+                                    void* const*, void* const*, void* const*, void* const*, hipStream_t);
 hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
 hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
                               float*, uint32_t*, int64_t, int, uint64_t, hipStream_t);
@@ -117,7 +119,10 @@ mxq_status quantize_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
                                             do_col ? q_colT : nullptr, s_colT, S(stream)));
 }
 
-mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream) {
+}  // extern "C"
+
+namespace {
+mxq_status quantize_mx_multi(const mxq_mxfp8_tensor* tensors, int count, bool fp4, void* stream) {
   if (count < 1 || count > MXQ_MXFP8_MULTI_MAX) return MXQ_ERR_SHAPE;
   if (!tensors) return MXQ_ERR_NULL;
   const void* x[MXQ_MXFP8_MULTI_MAX];
@@ -146,7 +151,19 @@ mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void
   }
   if (blocks > kMaxGridBlocks) return MXQ_ERR_SHAPE;
   if (n == 0) return MXQ_OK;
-  return hip_status(mxq::launch_quant_mxfp8_multi(n, x, rows, cols, ld, qr, sr, qc, sc, S(stream)));
+  return hip_status(fp4 ? mxq::launch_quant_mxfp4_multi(n, x, rows, cols, ld, qr, sr, qc, sc, S(stream))
+                        : mxq::launch_quant_mxfp8_multi(n, x, rows, cols, ld, qr, sr, qc, sc, S(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream) {
+  return quantize_mx_multi(tensors, count, false, stream);
+}
+
+mxq_status quantize_mxfp4_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream) {
+  return quantize_mx_multi(tensors, count, true, stream);
 }
 
 mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x, void* q_packed,

@@ -1,4 +1,4 @@
-// MXFP8 quantizer: rowwise 1x32 and columnwise 32x1 copies from one HBM read.
+// MXFP8 / MXFP4 quantizer: rowwise 1x32 and columnwise 32x1 copies from one HBM read.
 //
 // Operation (restated from the pages): 32 consecutive E4M3 values share one
 // E8M0 scale ("Miles Blackwell RL", remio.ai, section "La Compatibilidad de
@@ -243,6 +243,12 @@ hipError_t launch_quant_mxfp8_multi(int n, const void* const* x, const int64_t* 
                                     const int64_t* ld_x, void* const* q_row, void* const* s_row,
                                     void* const* q_colT, void* const* s_colT, hipStream_t stream) {
   return launch_quant_mx_multi<false>(n, x, rows, cols, ld_x, q_row, s_row, q_colT, s_colT, stream);
+}
+
+hipError_t launch_quant_mxfp4_multi(int n, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                    const int64_t* ld_x, void* const* q_row, void* const* s_row,
+                                    void* const* q_colT, void* const* s_colT, hipStream_t stream) {
+  return launch_quant_mx_multi<true>(n, x, rows, cols, ld_x, q_row, s_row, q_colT, s_colT, stream);
 }
 
 hipError_t launch_quant_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q_row, void* s_row,

@@ -70,6 +70,24 @@ class LinearMxfp8:
             self.gemm(n)
 
 
+class LinearMxfp4(LinearMxfp8):
+    """The same three GEMMs with MXFP4 operands (E2M1 + E8M0 per 32), on the native
+    FP4 scaled MFMA."""
+
+    def __init__(self, tokens: int, d_in: int, d_out: int, dev):
+        T, Di, Do = tokens, d_in, d_out
+        self.q = {n: (_u8((r, c // 2), dev), _u8((r, c // 32), dev), _u8((c, r // 2), dev), _u8((c, r // 32), dev))
+                  for n, (r, c) in {"x": (T, Di), "w": (Do, Di), "dy": (T, Do)}.items()}
+        self.y, self.dx, self.dw = _f32((T, Do), dev), _f32((T, Di), dev), _f32((Do, Di), dev)
+
+    def quantize(self, x, w, dy):
+        B.quantize_mxfp4_multi([x, w, dy], [self.q["x"], self.q["w"], self.q["dy"]])
+
+    def gemm(self, name: str):
+        A, sA, Bq, sB, out = self.gemm_args()[name]
+        B.gemm_block_scaled(B.MXFP4, A, sA, Bq, sB, out=out)
+
+
 # ---------------------------------------------------------------------------
 # Routed-expert MoE layer with per-token NVFP4 activations and NVFP4 expert weights
 # ---------------------------------------------------------------------------
@@ -312,7 +330,7 @@ class StressStep:
         self.signs = [int(v) for v in signs]
         self.qa = (_u8((n, n), dev), _u8((n, n // 32), dev), _u8((n, n), dev), _u8((n, n // 32), dev))
         self.qb = (_u8((n, n), dev), _u8((n, n // 32), dev), _u8((n, n), dev), _u8((n, n // 32), dev))
-        self.c = {k: _f32((n, n), dev) for k in ("fprop", "dgrad", "wgrad", "wgrad_nvfp4")}
+        self.c = {k: _f32((n, n), dev) for k in ("fprop", "dgrad", "wgrad", "wgrad_nvfp4", "fprop_mxfp4")}
         self.nv = {k: (_u8((n, n // 2), dev), _u8((n, n // 16), dev), _f32((1,), dev)) for k in ("a", "b")}
         ws = B.lib().mxq_workspace_bytes(B.OP_QUANTIZE_NVFP4, n, n, 1)
         self.ws = _u8((ws,), dev)
@@ -343,6 +361,20 @@ class StressStep:
         B._check("quantize_nvfp4_stochastic", B.lib().quantize_nvfp4_stochastic(
             B._ptr(a), self.n, self.n, a.stride(0), B.SCOPE["tensor"], 0, 1, self._signs_c, seed, B._ptr(q),
             B._ptr(s), B._ptr(t), B._ptr(self.ws), self.ws.numel(), B._stream(self.dev)))
+
+    def quantize_mxfp4(self, a, b):
+        """MXFP4 rowwise + columnwise copies of A and B (one launch)."""
+        if not hasattr(self, "q4"):
+            n, dev = self.n, self.dev
+            mk = lambda: (_u8((n, n // 2), dev), _u8((n, n // 32), dev), _u8((n, n // 2), dev), _u8((n, n // 32), dev))
+            self.q4 = {"a": mk(), "b": mk()}
+        B.quantize_mxfp4_multi([a, b], [self.q4["a"], self.q4["b"]])
+
+    def mxfp4_gemm(self):
+        """C = A B^T on the MXFP4 rowwise copies (native FP4 scaled MFMA)."""
+        ar, ars, _, _ = self.q4["a"]
+        br, brs, _, _ = self.q4["b"]
+        B.gemm_block_scaled(B.MXFP4, ar, ars, br, brs, out=self.c["fprop_mxfp4"])
 
     def nvfp4_wgrad(self):
         qa, sa, ta = self.nv["a"]

@@ -79,6 +79,9 @@ def test_quantize_mxfp8_multi_validation():
     assert multi([ok, (None, 64, 64, 64, P, P, P, P)]) == 1
     assert multi([(P, 0, 64, 64, P, P, P, P)]) == 0                     # all empty: no-op
     assert B.lib().quantize_mxfp8_multi(None, 1, None) == 1
+    arr = (B._Mxfp8Tensor * 2)(B._Mxfp8Tensor(*ok), B._Mxfp8Tensor(P, 64, 48, 48, P, P, P, P))
+    assert B.lib().quantize_mxfp4_multi(ctypes.cast(arr, ctypes.c_void_p), 2, None) == 2       # MXFP4: cols % 32
+    assert B.lib().quantize_mxfp4_multi(ctypes.cast(arr, ctypes.c_void_p), 0, None) == 2
 
 
 def test_nvfp4_validation():

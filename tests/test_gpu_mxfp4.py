@@ -77,6 +77,25 @@ def test_mxfp4_colwise_only_strided_and_edge_blocks():
     check_mxfp4(edge_case_tensor(rows=160, cols=288, seed=3), what="edge cases 160x288")
 
 
+def test_mxfp4_multi_matches_single_calls():
+    g = inputs.rng(129, 0)
+    shapes = [(4128, 96), (32, 32), (0, 64), (256, 544), (96, 160)]
+    xs = [inputs.to_bf16_bits(g.standard_normal(sh) * g.lognormal(0, 2, (sh[0], 1))) for sh in shapes]
+    dx = [dev_bf16(x) for x in xs]
+    outs = [tuple(torch.empty(s, dtype=torch.uint8, device="cuda")
+                  for s in ((r, c // 2), (r, c // 32), (c, r // 2), (c, r // 32))) for r, c in shapes]
+    mxq.quantize_mxfp4_multi(dx, outs)
+    for x, o, sh in zip(xs, outs, shapes):
+        if sh[0] == 0:
+            continue
+        eq, es = om4.quantize_rowwise(x)
+        assert_bytes_equal(host(o[0]), eq, f"multi {sh} q_row")
+        assert_bytes_equal(host(o[1]), es, f"multi {sh} s_row")
+        eq, es = om4.quantize_colwise(x)
+        assert_bytes_equal(host(o[2]), eq, f"multi {sh} q_colT")
+        assert_bytes_equal(host(o[3]), es, f"multi {sh} s_colT")
+
+
 def test_mxfp4_dequantize_exact():
     xb = edge_case_tensor(rows=64, cols=256, seed=5)
     qr, sr, _, _ = mxq.quantize_mxfp4(dev_bf16(xb), True, False)
@@ -141,6 +160,32 @@ def test_mxfp4_gemm_integer_sums_are_exact():
     ref = og.gemm_tn_fp64(ah, bh)
     assert np.max(np.abs(ref)) < 2 ** 24
     assert np.array_equal(c.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("case", ["student_t", "block_outliers"])
+def test_mxfp4_gemm_error_model(case):
+    """The native FP4 scaled MFMA sums the exact products of each 64-K instruction with
+    FP32-grade error (measured: <= 2^-23.6 of the sum of the term magnitudes). Checked
+    elementwise over K / 64 chained instructions on heavy-tailed data, whose blocks
+    span the whole E2M1 range and whose block scales differ widely."""
+    g = inputs.rng(130, len(case))
+    M, N, K = 256, 320, 2048
+    if case == "student_t":
+        a = inputs.to_bf16_bits(g.standard_t(3.0, (M, K)))
+        b = inputs.to_bf16_bits(g.standard_t(3.0, (N, K)))
+    else:
+        a = g.standard_normal((M, K)) * np.exp2(g.integers(-20, 21, (M, K // 32))).repeat(32, axis=1)
+        b = g.standard_normal((N, K)) * np.exp2(g.integers(-20, 21, (N, K // 32))).repeat(32, axis=1)
+        a[g.random((M, K)) < 1e-3] *= 1e4
+        a, b = inputs.to_bf16_bits(a), inputs.to_bf16_bits(b)
+    qa, sa, ah = m4_operands(a)
+    qb, sb, bh = m4_operands(b)
+    c = host(mxq.gemm_block_scaled(mxq.MXFP4, qa, sa, qb, sb)).astype(np.float64)
+    ref = og.gemm_tn_fp64(ah, bh)
+    mag = og.gemm_tn_fp64(np.abs(ah), np.abs(bh))
+    bound = (K / 64 + 2) * 2.0 ** -23 * mag
+    assert np.all(np.abs(c - ref) <= bound), f"{case}: max err / bound {np.max(np.abs(c - ref) / bound):.3f}"
+    assert_gemm_close(c.astype(np.float32), ref, case)
 
 
 def test_mxfp4_linear_fprop_dgrad_wgrad():

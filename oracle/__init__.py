@@ -25,8 +25,10 @@ Functions with no pin against the pages are marked "parity unpinned" in their
 docstring. Present ones:
   * the E8M0 exponent-selection rule (round-up reading) is held in place only by
     invariants and hand-worked closed forms, not by a value printed on a page;
-  * the NVFP4 FP32 operation order and the choice to store the decode scale.
+  * the NVFP4 FP32 operation order and the choice to store the decode scale;
+  * the blockwise-FP8 scale choice s = amax / 448 and its zero-block scale.
 """
 
 from . import formats, mxfp8, nvfp4, gemm, moe, rng  # noqa: F401
 from . import mxfp4  # noqa: F401,E402
+from . import fp8_block  # noqa: F401,E402

@@ -49,6 +49,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0, "fp4": 10100.
 METRIC = "quantize GB/s (% HBM peak) + block-scaled GEMM TFLOPS (% MFMA peak), 1 GPU"
 KERNEL_SOURCES = ["microscaling_precision_quantization_amd/csrc/gemm_exact.hip",
                   "microscaling_precision_quantization_amd/csrc/quant_mxfp8.hip",
+                  "microscaling_precision_quantization_amd/csrc/quant_fp8_block.hip",
                   "microscaling_precision_quantization_amd/csrc/quant_nvfp4.hip",
                   "microscaling_precision_quantization_amd/csrc/dequant_moe.hip",
                   "microscaling_precision_quantization_amd/csrc/common.h"]
@@ -56,6 +57,8 @@ KERNEL_SOURCES = ["microscaling_precision_quantization_amd/csrc/gemm_exact.hip",
 # algorithmic bytes per element
 MX_ROWCOL = 2 + 1 + 1 + 2 / 32          # BF16 read + two E4M3 copies + two E8M0 scale sets
 MX4_ROWCOL = 2 + 0.5 + 0.5 + 2 / 32      # BF16 read + two packed E2M1 copies + two E8M0 scale sets
+FP8B_ACT = 2 + 1 + 1 + 2 * 4 / 128       # BF16 read + 1x128 and 128x1 E4M3 copies + their FP32 scales
+FP8B_W = 2 + 1 + 1 + 2 * 4 / 128 ** 2    # BF16 read + row and transposed E4M3 copies + block scales
 NV_TOKEN = 2 + 0.5 + 1 / 16             # BF16 read + packed E2M1 + E4M3 per 16 (+ 4 B per row)
 NV_TENSOR = 2 + NV_TOKEN                # + the amax pass over the BF16 input
 NV_2D_BOTH = 2 + 2 + 2 * (0.5 + 1 / 16)  # 16x16 blocks: amax pass + quantize pass, row + transposed copies
@@ -116,6 +119,7 @@ class Linear:
         self.sets = [{k: v.clone() for k, v in base.items()} for _ in range(self.N_SETS)]
         self.layer = pipeline.LinearMxfp8(self.T, self.DIN, self.DOUT, dev)
         self.layer4 = pipeline.LinearMxfp4(self.T, self.DIN, self.DOUT, dev)
+        self.layer8b = pipeline.LinearFp8Block(self.T, self.DIN, self.DOUT, dev)
         self.gemm_flop = 2 * self.T * self.DOUT * self.DIN            # each of fprop, dgrad, wgrad
         self.step_flop = 3 * self.gemm_flop
         self.config = {"workload": "MXFP8 linear layer: X (2048,2048) N(0,1), W (8192,2048) N(0,0.02), "
@@ -135,12 +139,21 @@ class Linear:
         return out
 
     def extra_components(self):
-        """The same layer in MXFP4 (E2M1 + E8M0 per 32) on the native FP4 scaled MFMA,
-        outside the step: one row+col quantize launch of X, W, dY and the three GEMMs."""
+        """Outside the step: the same layer in MXFP4 (E2M1 + E8M0 per 32) on the native FP4
+        scaled MFMA (one row+col quantize launch of X, W, dY, then the three GEMMs), and in
+        DeepSeek-V3-style blockwise FP8 (three quantize launches, three GEMMs on the BF16
+        datapath with the FP32 block scales applied in software)."""
         s, L4 = self.sets[0], self.layer4
         n_el = self.T * self.DIN + self.DOUT * self.DIN + self.T * self.DOUT
         out = [Stage("quantize_mxfp4_rowcol", lambda: L4.quantize(s["x"], s["w"], s["dy"]), n_el * MX4_ROWCOL, "hbm")]
         out += [Stage("gemm_block_scaled_mxfp4_" + g, (lambda g=g: L4.gemm(g)), self.gemm_flop, "mfma", "fp4")
+                for g in ("fprop", "dgrad", "wgrad")]
+        # DeepSeek-V3-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks)
+        L8 = self.layer8b
+        w_el = self.DOUT * self.DIN
+        out += [Stage("quantize_fp8_block", lambda: L8.quantize(s["x"], s["w"], s["dy"]),
+                      (n_el - w_el) * FP8B_ACT + w_el * FP8B_W, "hbm")]
+        out += [Stage("gemm_fp8_blockwise_" + g, (lambda g=g: L8.gemm(g)), self.gemm_flop, "mfma", "bf16")
                 for g in ("fprop", "dgrad", "wgrad")]
         return out
 

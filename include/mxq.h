@@ -154,6 +154,44 @@ mxq_status quantize_mxfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_
 mxq_status quantize_mxfp4_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_fp8_block_act -- blockwise FP8 (DeepSeek-V3 style) of an activation or
+ * gradient: E4M3 elements with one FP32 scale per 1 x 128 tile.
+ *   Defined by: E4M3 elements, 1 x 128 activation tiles and 128 x 128 weight blocks
+ *   with FP32 scales applied in software around the matrix product ("Miles Blackwell
+ *   MXFP8/NVFP4 RL recipes", aib.vote, second paragraph; "Miles Blackwell RL",
+ *   remio.ai, section "NVFP4 por token cuestiona ..."); gradients in the same 1 x 128
+ *   tiles (7minutos.es NVFP4 page, the 12B results paragraph).
+ *   Arithmetic (binary32): s = amax / 448 over the tile (s = 0 for an all-zero tile);
+ *   q = RNE_sat_E4M3(x / s) (a signed zero when s = 0). Dequantized value q * s.
+ *
+ *   x      : BF16 (rows, cols), row stride ld_x (ld_x % 8 == 0, cols % 8 == 0).
+ *   q_row  : E4M3 (rows, cols), s_row : FP32 (rows, cols/128) -- 1 x 128 tiles along each
+ *            row (the operand of fprop / dgrad); requires cols % 128 == 0.
+ *   q_colT : E4M3 (cols, rows), s_colT : FP32 (cols, rows/128) -- tiles of 128 down each
+ *            column, stored transposed (the operand of a GEMM that reduces over rows,
+ *            e.g. wgrad); requires rows % 128 == 0.
+ *   Either pair may be NULL (not both); both copies come from one read of x.
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_fp8_block_act(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  void* q_row, float* s_row, void* q_colT, float* s_colT, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * quantize_fp8_block_weight -- blockwise FP8 of a weight: E4M3 elements with one FP32
+ * scale per 128 x 128 block, as a row copy and/or a transposed copy with the same
+ * codes (the forward GEMM and the transposed backward GEMM read one quantized weight).
+ *   Defined by: as quantize_fp8_block_act (aib.vote, second paragraph; remio.ai,
+ *   section "NVFP4 por token cuestiona ...").
+ *   Arithmetic as quantize_fp8_block_act with the amax over the 128 x 128 block.
+ *
+ *   x      : BF16 (rows, cols), row stride ld_x; rows % 128 == cols % 128 == 0.
+ *   q_row  : E4M3 (rows, cols);  s_row : FP32 (rows/128, cols/128).
+ *   q_colT : E4M3 (cols, rows) = the transpose;  s_colT : FP32 (cols/128, rows/128).
+ *   Either pair may be NULL (not both).
+ * ------------------------------------------------------------------------- */
+mxq_status quantize_fp8_block_weight(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                     void* q_row, float* s_row, void* q_colT, float* s_colT, void* stream);
+
+/* ---------------------------------------------------------------------------
  * quantize_nvfp4_per_token -- NVFP4 with one FP32 scale per token (row),
  * computed online in the same kernel that emits the packed E2M1 values and the
  * E4M3 block scales.
@@ -340,6 +378,27 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                              const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
                              const void* B, const void* sB, const float* tB, mxq_scope tB_scope,
                              float* C, int64_t ldc, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gemm_fp8_blockwise -- C = A_hat B_hat^T (FP32 output, "TN") for blockwise FP8
+ * operands, the FP32 scales applied in software around the matrix product.
+ *   Defined by: DeepSeek-V3-style FP8 with 128 x 128 weight blocks, 1 x 128 activation
+ *   tiles and FP32 scales applied outside the matrix hardware (aib.vote, second
+ *   paragraph; remio.ai, section "NVFP4 por token cuestiona ...").
+ *   C[m, n] = sum over 128-K blocks kb of sA[m, kb] sB(n, kb) sum_{k in kb} qA[m, k] qB[n, k]:
+ *   each block's code products are summed at FP32 precision, scaled by the two FP32
+ *   scales and accumulated in FP32.
+ *   A  : E4M3 (M, K) + sA FP32 (M, K/128)        (quantize_fp8_block_act layout)
+ *   B  : E4M3 (N, K) + sB FP32:
+ *          b_blocks = 1: (ceil(N/128), K/128), one per 128 x 128 block (a weight, or the
+ *                        transposed copy of one);
+ *          b_blocks = 0: (N, K/128), one per row and 128-K tile (an activation).
+ *   C[m * ldc + n], ldc >= N. Accuracy: normwise relative error <= 2e-5 against the
+ *   FP64 product of the dequantized operands. Requires K % 128 == 0 and K <= 2^22.
+ * ------------------------------------------------------------------------- */
+mxq_status gemm_fp8_blockwise(int64_t M, int64_t N, int64_t K, const void* A, const float* sA,
+                              const void* B, const float* sB, int b_blocks, float* C, int64_t ldc,
+                              void* stream);
 
 /* ---------------------------------------------------------------------------
  * gemm_mxfp8_matrix_core -- MXFP8 GEMM C = A_hat B_hat^T on the gfx950 scaled FP8

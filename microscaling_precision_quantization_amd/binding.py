@@ -33,6 +33,10 @@ _SIGS = {
     "quantize_mxfp8_multi": [_c_void_p, _int, _c_void_p],
     "quantize_mxfp4": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_mxfp4_multi": [_c_void_p, _int, _c_void_p],
+    "quantize_fp8_block_act": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "quantize_fp8_block_weight": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "gemm_fp8_blockwise": [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _i64,
+                           _c_void_p],
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
@@ -155,6 +159,43 @@ def quantize_mxfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, 
         s_col = _u8((C, R // 32), dev) if colwise else None
     _check("quantize_mxfp4", lib().quantize_mxfp4(_ptr(x), R, C, x.stride(0), _ptr(q_row), _ptr(s_row),
                                                   _ptr(q_col), _ptr(s_col), _stream(dev)))
+    return q_row, s_row, q_col, s_col
+
+
+def quantize_fp8_block_act(x: torch.Tensor, rowwise: bool = True, colwise: bool = False, out=None):
+    """Blockwise FP8 of an activation / gradient: (q_row (R, C), s_row (R, C/128)) with 1 x 128
+    tiles along rows and (q_colT (C, R), s_colT (C, R/128)) with tiles of 128 down columns,
+    stored transposed; skipped copies are None."""
+    _bf16(x)
+    R, C = x.shape
+    dev = x.device
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    if out is not None:
+        q_row, s_row, q_col, s_col = out
+    else:
+        q_row, s_row = (_u8((R, C), dev), f32(R, C // 128)) if rowwise else (None, None)
+        q_col, s_col = (_u8((C, R), dev), f32(C, R // 128)) if colwise else (None, None)
+    _check("quantize_fp8_block_act", lib().quantize_fp8_block_act(
+        _ptr(x), R, C, x.stride(0), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(dev)))
+    return q_row, s_row, q_col, s_col
+
+
+def quantize_fp8_block_weight(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out=None):
+    """Blockwise FP8 of a weight (128 x 128 blocks): (q_row (R, C), s_row (R/128, C/128),
+    q_colT (C, R), s_colT (C/128, R/128)); skipped copies are None."""
+    _bf16(x)
+    R, C = x.shape
+    dev = x.device
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    if out is not None:
+        q_row, s_row, q_col, s_col = out
+    else:
+        q_row = _u8((R, C), dev) if rowwise else None
+        s_row = f32(R // 128, C // 128) if rowwise else None
+        q_col = _u8((C, R), dev) if colwise else None
+        s_col = f32(C // 128, R // 128) if colwise else None
+    _check("quantize_fp8_block_weight", lib().quantize_fp8_block_weight(
+        _ptr(x), R, C, x.stride(0), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(dev)))
     return q_row, s_row, q_col, s_col
 
 
@@ -300,6 +341,17 @@ def gemm_block_scaled(fmt: int, A, sA, B, sB, tA=None, tB=None, tA_scope="row", 
     _check("gemm_block_scaled", lib().gemm_block_scaled(fmt, M, N, K, _ptr(A), _ptr(sA), _ptr(tA), SCOPE[tA_scope],
                                                         _ptr(B), _ptr(sB), _ptr(tB), SCOPE[tB_scope], _ptr(out),
                                                         out.stride(0), _stream(A.device)))
+    return out
+
+
+def gemm_fp8_blockwise(A, sA, B, sB, b_blocks: bool = True, out=None):
+    """Blockwise FP8 GEMM C = A_hat B_hat^T (FP32); sB per 128 x 128 block (b_blocks) or per row."""
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _check("gemm_fp8_blockwise", lib().gemm_fp8_blockwise(M, N, K, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), int(b_blocks),
+                                                          _ptr(out), out.stride(0), _stream(A.device)))
     return out
 
 

@@ -14,6 +14,8 @@ hipError_t launch_quant_mxfp8_multi(int, const void* const*, const int64_t*, con
 hipError_t launch_quant_mxfp4(const void*, int64_t, int64_t, int64_t, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_quant_mxfp4_multi(int, const void* const*, const int64_t*, const int64_t*, const int64_t*,
                                     void* const*, void* const*, void* const*, void* const*, hipStream_t);
+hipError_t launch_quant_fp8_block(int, const void*, int64_t, int64_t, int64_t, void*, float*, void*, float*,
+                                  hipStream_t);
 hipError_t launch_quant_nvfp4_token(const void*, int64_t, int64_t, int64_t, void*, void*, float*, hipStream_t);
 hipError_t launch_quant_nvfp4(const void*, int64_t, int64_t, int64_t, int, int64_t, int, int, uint32_t, void*, void*,
                               float*, uint32_t*, int64_t, int, uint64_t, hipStream_t);
@@ -164,6 +166,38 @@ mxq_status quantize_mxfp8_multi(const mxq_mxfp8_tensor* tensors, int count, void
 
 mxq_status quantize_mxfp4_multi(const mxq_mxfp8_tensor* tensors, int count, void* stream) {
   return quantize_mx_multi(tensors, count, true, stream);
+}
+
+mxq_status quantize_fp8_block_act(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q_row, float* s_row,
+                                  void* q_colT, float* s_colT, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  const bool do_row = q_row || s_row, do_col = q_colT || s_colT;
+  if (!x || (!do_row && !do_col)) return MXQ_ERR_NULL;
+  if ((do_row && (!q_row || !s_row)) || (do_col && (!q_colT || !s_colT))) return MXQ_ERR_NULL;
+  if (ld_x < cols || cols % 8) return MXQ_ERR_SHAPE;
+  if (do_row && cols % 128) return MXQ_ERR_SHAPE;
+  if (do_col && rows % 128) return MXQ_ERR_SHAPE;
+  if (ld_x % 8 || !al16(x) || (do_row && (!al16(q_row) || !al4(s_row))) || (do_col && (!al16(q_colT) || !al4(s_colT))))
+    return MXQ_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if (((rows + 127) / 128) * ((cols + 127) / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_quant_fp8_block(0, x, rows, cols, ld_x, do_row ? q_row : nullptr, s_row,
+                                                do_col ? q_colT : nullptr, s_colT, S(stream)));
+}
+
+mxq_status quantize_fp8_block_weight(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q_row, float* s_row,
+                                     void* q_colT, float* s_colT, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+  const bool do_row = q_row || s_row, do_col = q_colT || s_colT;
+  if (!x || (!do_row && !do_col)) return MXQ_ERR_NULL;
+  if ((do_row && (!q_row || !s_row)) || (do_col && (!q_colT || !s_colT))) return MXQ_ERR_NULL;
+  if (rows % 128 || cols % 128 || ld_x < cols) return MXQ_ERR_SHAPE;
+  if (ld_x % 8 || !al16(x) || (do_row && (!al16(q_row) || !al4(s_row))) || (do_col && (!al16(q_colT) || !al4(s_colT))))
+    return MXQ_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if ((rows / 128) * (cols / 128) > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_quant_fp8_block(1, x, rows, cols, ld_x, do_row ? q_row : nullptr, s_row,
+                                                do_col ? q_colT : nullptr, s_colT, S(stream)));
 }
 
 mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x, void* q_packed,
@@ -328,6 +362,17 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K, co
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   if (M == 0 || N == 0) return MXQ_OK;
   return hip_status(mxq::launch_gemm((int)fmt, M, N, K, A, sA, tA, ta, B, sB, tB, tb, C, ldc, S(stream)));
+}
+
+mxq_status gemm_fp8_blockwise(int64_t M, int64_t N, int64_t K, const void* A, const float* sA, const void* B,
+                              const float* sB, int b_blocks, float* C, int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (!A || !sA || !B || !sB || !C) return MXQ_ERR_NULL;
+  if (b_blocks != 0 && b_blocks != 1) return MXQ_ERR_FORMAT;
+  if (K % 128 || K > kMaxGemmK || ldc < N) return MXQ_ERR_SHAPE;
+  if (!al16(A) || !al16(B) || !al4(sA) || !al4(sB) || !al4(C)) return MXQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return MXQ_OK;
+  return hip_status(mxq::launch_gemm(5, M, N, K, A, sA, nullptr, 0, B, sB, nullptr, b_blocks, C, ldc, S(stream)));
 }
 
 mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const void* B,

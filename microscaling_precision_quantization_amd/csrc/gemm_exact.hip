@@ -19,6 +19,10 @@
 //     products of one block sum exactly, and a result differs from the exact value by
 //     at most 2^-23.6 of the sum of the magnitudes of its terms (FP32-grade, unlike the
 //     FP8 form's ~2^-13 window), so this path meets the same accuracy bound.
+//   * Blockwise FP8 (E4M3, FP32 scale per row and 128-K block of A, per row or per
+//     128 x 128 block of B): the E4M3 values are exact in BF16 -> BF16 MFMA into a
+//     per-block partial sum; at the end of each 128-K stage the FP32 scales are applied
+//     in software (acc += partial * sA sB, one FMA per accumulator).
 //   * BF16 operands as they are -> BF16 MFMA.
 // Definitions: microscaling blocks along the reduction dimension ("Miles
 // Blackwell RL", remio.ai, section "Un Cuantizador Compartido Es el Mecanismo
@@ -54,13 +58,13 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 namespace gx {
-constexpr int BK = 64;                          // K elements per stage
 constexpr int kLdsBytes = 160 * 1024;           // gfx950 LDS per workgroup
 template <int LD> struct RowBytes;
 template <> struct RowBytes<0> { static constexpr int v = 128; };   // BF16
 template <> struct RowBytes<1> { static constexpr int v = 64; };    // MXFP8
 template <> struct RowBytes<2> { static constexpr int v = 32; };    // NVFP4
 template <> struct RowBytes<3> { static constexpr int v = 32; };    // MXFP4
+template <> struct RowBytes<4> { static constexpr int v = 128; };   // blockwise FP8: one 128-K block per stage
 
 // Scale modes (SM):
 //   0  general: K tiles may end early; per stage, one direct load per row and scale
@@ -72,9 +76,11 @@ template <> struct RowBytes<3> { static constexpr int v = 32; };    // MXFP4
 //      cuts the scale cache-line requests by that factor.
 // Each per-stage load lands in a 4-byte LDS slot per row (gfx950 places 1/2/4-byte
 // direct loads at base + 4 lane); chunked scales in a 16-byte slot per row.
+// Blockwise FP8 (LD 4): one FP32 scale per row and 128-K block, one dword load per row
+// and stage (SU 1, SZ 4) whatever SM is.
 template <int LD, int SM> struct ScaleDma {
-  static constexpr int SU = (LD == 0 || SM == 2) ? 0 : (SM == 1 ? 1 : 2);
-  static constexpr int SZ = (LD == 1 || LD == 3) ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
+  static constexpr int SU = LD == 4 ? 1 : (LD == 0 || SM == 2) ? 0 : (SM == 1 ? 1 : 2);
+  static constexpr int SZ = LD == 4 ? 4 : (LD == 1 || LD == 3) ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
 };
 
 // OCC = workgroups meant to share one CU: the LDS budget of a workgroup is 1 / OCC of it.
@@ -83,12 +89,12 @@ template <int LD, int SM> struct ScaleDma {
 template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false>
 struct Cfg {
   static constexpr int RB = (WIDE && LD != 0) ? 128 : RowBytes<LD>::v;
-  static constexpr int BK = LD == 0 ? RB / 2 : LD == 1 ? RB : 2 * RB;   // K elements per stage
+  static constexpr int BK = LD == 0 ? RB / 2 : (LD == 1 || LD == 4) ? RB : 2 * RB;   // K elements per stage
   static constexpr int SBS = RB / 32;                                     // sub-blocks per stage
   static_assert(!WIDE || SM == 2, "wide stages need chunked scales");
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int SU = ScaleDma<LD, SM>::SU, SZ = ScaleDma<LD, SM>::SZ;
-  static constexpr bool CH = SM == 2 && LD != 0;                 // chunked scales
+  static constexpr bool CH = SM == 2 && LD != 0 && LD != 4;      // chunked scales
   // stages per 16-byte scale chunk (16 blocks)
   static constexpr int SPC = (LD == 1 || LD == 3) ? 16 / (BK / 32) : LD == 2 ? 16 / (BK / 16) : 4;
   static constexpr int CH_HALF = CH ? (BM + BN) * 16 : 0;         // one chunk buffer
@@ -204,7 +210,7 @@ __device__ __forceinline__ void buf_dma16_group(v4i rs, const uint32_t* vo, uint
 
 template <int LD>
 __device__ __forceinline__ int64_t k_bytes(int64_t k) {
-  return LD == 0 ? k * 2 : LD == 1 ? k : k / 2;
+  return LD == 0 ? k * 2 : (LD == 1 || LD == 4) ? k : k / 2;
 }
 
 typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
@@ -304,8 +310,9 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   constexpr int RB = C::RB, NS = C::NS, TI = C::TI, TJ = C::TJ, IA = C::IA, IB = C::IB, IS = C::IS;
   constexpr int SBS = C::SBS;                             // sub-blocks per stage
   constexpr int NF = TI + TJ;                             // fragments per lane and sub-block
-  constexpr int BS = (LD == 1 || LD == 3) ? 32 : 16;      // elements per scale block
-  constexpr int EPC = LD == 0 ? 8 : LD == 1 ? 16 : 32;    // elements per 16-byte chunk
+  constexpr int BS = LD == 4 ? 128 : (LD == 1 || LD == 3) ? 32 : 16;   // elements per scale block
+  constexpr int SEB = LD == 4 ? 4 : 1;                    // bytes per scale entry
+  constexpr int EPC = LD == 0 ? 8 : (LD == 1 || LD == 4) ? 16 : 32;   // elements per 16-byte chunk
   constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave (chunks aside)
   constexpr int R = CH ? lcm_int(SPC, NS) : NS;           // stages per unrolled round
   static_assert(R % NS == 0 && (!CH || R % SPC == 0), "round must cover whole slot and chunk cycles");
@@ -357,7 +364,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     const int r0 = item0 % (BM + BN);
     const int row = r0 + lane;
     if (r0 < BM) {
-      const int64_t lds_ = p.lda / BS;
+      const int64_t lds_ = p.lda / BS * SEB;
       if (p.a_idx) {
         rsS[q] = make_rsrc(p.sA, (uint32_t)min(p.a_rows * lds_, (int64_t)0x7FFFFFFF));
         const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
@@ -366,8 +373,14 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         rsS[q] = make_rsrc(p.sA + (p.a_base + m0) * lds_, (uint32_t)(a_rows_tile * lds_));
         voS[q] = (uint32_t)(row * lds_ + u * BPU);
       }
+    } else if (LD == 4 && p.tB_mode == 1) {
+      // one scale per 128 x 128 block of B: every row of a 128-row block reads its block's
+      // entry (n0 is a multiple of 128)
+      const int64_t lds_ = p.ldb / BS * SEB;
+      rsS[q] = make_rsrc(p.sB + (n0 / 128) * lds_, (uint32_t)((b_rows_tile + 127) / 128 * lds_));
+      voS[q] = (uint32_t)(((row - BM) / 128) * lds_);
     } else {
-      const int64_t lds_ = p.ldb / BS;
+      const int64_t lds_ = p.ldb / BS * SEB;
       rsS[q] = make_rsrc(p.sB + n0 * lds_, (uint32_t)(b_rows_tile * lds_));
       voS[q] = (uint32_t)((row - BM) * lds_ + u * BPU);
     }
@@ -413,8 +426,8 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     TileK r;
     r.k0 = kb + t * C::BK;
     const bool past = t >= nk;
-    r.sod = past ? kOutOfRange : (uint32_t)(LD == 0 ? 2 * r.k0 : LD == 1 ? r.k0 : r.k0 / 2);
-    r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS);
+    r.sod = past ? kOutOfRange : (uint32_t)(LD == 0 ? 2 * r.k0 : (LD == 1 || LD == 4) ? r.k0 : r.k0 / 2);
+    r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS * SEB);
     r.tail = !AL && !past && r.k0 + C::BK > ke;
     return r;
   };
@@ -522,7 +535,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           fr.sc[f] = (chr[f][tp * SBS + b] >> (16 * h)) & 0xFFFFu;
         }
       }
-    } else if constexpr (LD != 0) {
+    } else if constexpr (LD != 0 && LD != 4) {
       const lds_cptr sa = as_lds(lbase[S] + wsA + xs), sb = as_lds(lbase[S] + wsB + xs);
       // MXFP8: the byte of block b; NVFP4: the two bytes of blocks 2h, 2h+1; MXFP4 (one
       // sub-block per stage): the byte of block h
@@ -543,6 +556,57 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // Blockwise FP8: the matrix core sums one 128-K block into `part`; at the end of the
+  // stage the block's FP32 scales are applied in software, acc += part * (sA[row] sB[col]),
+  // and part restarts from zero.
+  constexpr int TI4 = LD == 4 ? TI : 1, TJ4 = LD == 4 ? TJ : 1;
+  v16f part[TI4][TJ4];
+  float sa4[TI4][16], sb4[TJ4];
+#pragma unroll
+  for (int i = 0; i < TI4; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+  auto dst = [&](int i, int j) -> v16f& {
+    if constexpr (LD == 4) return part[i][j];
+    else return acc[i][j];
+  };
+  // the stage's scales (slot S, published by the barrier that ended the previous stage)
+  auto read_scales4 = [&](auto SLOT) {
+    if constexpr (LD == 4) {
+      constexpr int S = decltype(SLOT)::value;
+      const uint32_t base = lbase[S] + C::A_BYTES + C::B_BYTES;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {        // accumulator rows 8 g + 4 h + 0..3 of MFMA tile i
+          const int row = wm * (BM / 2) + i * 32 + g * 8 + h * 4;
+          const u32x4 v4 = lds_ld16(as_lds(base + (uint32_t)(row * 4)));
+          sa4[i][4 * g + 0] = __uint_as_float(v4.x);
+          sa4[i][4 * g + 1] = __uint_as_float(v4.y);
+          sa4[i][4 * g + 2] = __uint_as_float(v4.z);
+          sa4[i][4 * g + 3] = __uint_as_float(v4.w);
+        }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        sb4[j] = *(const __attribute__((address_space(3))) float*)as_lds(
+            base + (uint32_t)((BM + wn * (BN / 2) + j * 32 + lr) * 4));
+    }
+  };
+  auto promote4 = [&]() {
+    if constexpr (LD == 4) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[i][j][r] = __builtin_fmaf(part[i][j][r], sa4[i][r] * sb4[j], acc[i][j][r]);
+            part[i][j][r] = 0.0f;
+          }
+    }
+  };
 
   // Convert + MFMA one sub-block; hook(jj) runs after the MFMAs of B fragment jj.
   auto mma_sub = [&](const Frag& fr, auto&& hook) {
@@ -558,23 +622,24 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][j], 0, 0, 0);
         hook(JJ);
       });
-    } else if constexpr (LD == 1) {
+    } else if constexpr (LD == 1 || LD == 4) {
+      // MXFP8: E4M3 * 2^(s-127); blockwise FP8: the E4M3 values themselves (scale 2^0)
       v8bf fa0[TI], fa1[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const float s = mx_cvt_scale(fr.sc[i]);
+        const float s = LD == 4 ? 1.0f : mx_cvt_scale(fr.sc[i]);
         fa0[i] = mx_to_bf16(fr.raw[i].x, fr.raw[i].y, s);
         fa1[i] = mx_to_bf16(fr.raw[i].z, fr.raw[i].w, s);
       }
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
-        const float s = mx_cvt_scale(fr.sc[TI + j]);
+        const float s = LD == 4 ? 1.0f : mx_cvt_scale(fr.sc[TI + j]);
         const v8bf fb0 = mx_to_bf16(fr.raw[TI + j].x, fr.raw[TI + j].y, s);
         const v8bf fb1 = mx_to_bf16(fr.raw[TI + j].z, fr.raw[TI + j].w, s);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TI; ++i) dst(i, j) = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, dst(i, j), 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TI; ++i) dst(i, j) = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, dst(i, j), 0, 0, 0);
         hook(JJ);
       });
     } else if constexpr (LD == 3) {
@@ -652,6 +717,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     constexpr int WAIT = allowed(RI);
     static_assert(WAIT < 64, "vmcnt range");
     const TileK tk = tile_k(kt + NS - 1);
+    read_scales4(ic<S>{});
     static_for<0, SBS>([&](auto SB) {
       constexpr int b = decltype(SB)::value;
       constexpr int cur = (ri * SBS + b) & 1;
@@ -681,6 +747,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         }
       });
     });
+    promote4();
   };
 
   // prologue: scale chunk 0, tiles 0 .. NS-2 in flight, then the first sub-block's fragments
@@ -865,8 +932,10 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, 
   p.a_idx = nullptr; p.a_rows = M; p.a_base = 0; p.m_valid = M; p.lda = K;
   p.B = (const uint8_t*)B; p.sB = (const uint8_t*)sB; p.tB = tB; p.tB_mode = tB_mode; p.n_valid = N; p.ldb = K;
   p.k_begin = 0; p.k_end = K; p.C = C; p.ldc = ldc;
-  // fmt: 1 MXFP8, 2 NVFP4, 3 BF16, 4 MXFP4
-  if (fmt == 1) launch_dense_ld<1>(p, M, N, K, st);
+  // fmt: 1 MXFP8, 2 NVFP4, 3 BF16, 4 MXFP4, 5 blockwise FP8 (tB_mode: 0 per B row, 1 per
+  // 128 x 128 block; 128 x 128 tiles, K % 128 == 0)
+  if (fmt == 5) launch_dense_t<4, 128, 1>(p, M, N, st);
+  else if (fmt == 1) launch_dense_ld<1>(p, M, N, K, st);
   else if (fmt == 2) launch_dense_ld<2>(p, M, N, K, st);
   else if (fmt == 4) launch_dense_ld<3>(p, M, N, K, st);
   else launch_dense_ld<0>(p, M, N, K, st);

@@ -88,6 +88,42 @@ class LinearMxfp4(LinearMxfp8):
         B.gemm_block_scaled(B.MXFP4, A, sA, Bq, sB, out=out)
 
 
+class LinearFp8Block:
+    """The linear layer in DeepSeek-V3-style blockwise FP8: X and dY in 1 x 128 tiles (row
+    copy for fprop / dgrad, 128 x 1 transposed copy for wgrad, both from one read), W in
+    128 x 128 blocks (row copy for fprop, transposed copy for dgrad); FP32 scales applied
+    around the matrix product."""
+
+    def __init__(self, tokens: int, d_in: int, d_out: int, dev):
+        T, Di, Do = tokens, d_in, d_out
+        f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+        act = lambda r, c: (_u8((r, c), dev), f32(r, c // 128), _u8((c, r), dev), f32(c, r // 128))
+        self.qx, self.qdy = act(T, Di), act(T, Do)
+        self.qw = (_u8((Do, Di), dev), f32(Do // 128, Di // 128), _u8((Di, Do), dev), f32(Di // 128, Do // 128))
+        self.y, self.dx, self.dw = _f32((T, Do), dev), _f32((T, Di), dev), _f32((Do, Di), dev)
+
+    def quantize(self, x, w, dy):
+        B.quantize_fp8_block_act(x, True, True, out=self.qx)
+        B.quantize_fp8_block_weight(w, out=self.qw)
+        B.quantize_fp8_block_act(dy, True, True, out=self.qdy)
+
+    def gemm(self, name: str):
+        xr, xs, xc, xcs = self.qx
+        wr, ws, wc, wcs = self.qw
+        dr, ds, dc, dcs = self.qdy
+        if name == "fprop":
+            B.gemm_fp8_blockwise(xr, xs, wr, ws, b_blocks=True, out=self.y)
+        elif name == "dgrad":
+            B.gemm_fp8_blockwise(dr, ds, wc, wcs, b_blocks=True, out=self.dx)
+        else:
+            B.gemm_fp8_blockwise(dc, dcs, xc, xcs, b_blocks=False, out=self.dw)
+
+    def step(self, x, w, dy):
+        self.quantize(x, w, dy)
+        for n in ("fprop", "dgrad", "wgrad"):
+            self.gemm(n)
+
+
 # ---------------------------------------------------------------------------
 # Routed-expert MoE layer with per-token NVFP4 activations and NVFP4 expert weights
 # ---------------------------------------------------------------------------

@@ -64,6 +64,30 @@ def test_quantize_mxfp4_validation():
     assert q4(P, 0, 32, 32, P, P, P, P, None) == 0                     # empty: no-op
 
 
+def test_fp8_block_validation():
+    L = B.lib()
+    qa = L.quantize_fp8_block_act
+    assert qa(P, 4, 96, 96, P, P, None, None, None) == 2        # row copy: cols % 128
+    assert qa(P, 96, 128, 128, None, None, P, P, None) == 2     # transposed copy: rows % 128
+    assert qa(P, 128, 12, 12, None, None, P, P, None) == 2      # cols % 8
+    assert qa(P, 4, 128, 128, P, MIS + 1, None, None, None) == 3   # misaligned scales
+    assert qa(P, 4, 128, 128, None, None, None, None, None) == 1
+    assert qa(P, 4, 128, 128, P, None, None, None, None) == 1
+    assert qa(P, 0, 128, 128, P, P, None, None, None) == 0
+    qw = L.quantize_fp8_block_weight
+    assert qw(P, 128, 96, 96, P, P, None, None, None) == 2   # cols % 128
+    assert qw(P, 64, 128, 128, P, P, None, None, None) == 2  # rows % 128
+    assert qw(P, 128, 128, 128, None, None, None, None, None) == 1
+    assert qw(P, 128, 128, 128, P, None, None, None, None) == 1
+    assert qw(P, 128, 128, 128, P, P, MIS, P, None) == 3
+    g = L.gemm_fp8_blockwise
+    assert g(32, 32, 96, P, P, P, P, 1, P, 32, None) == 2    # K % 128
+    assert g(32, 32, 128, P, P, P, P, 2, P, 32, None) == 4
+    assert g(32, 32, 128, P, None, P, P, 1, P, 32, None) == 1
+    assert g(32, 32, 128, P, P, P, P, 1, P, 16, None) == 2   # ldc < N
+    assert g(0, 32, 128, P, P, P, P, 1, P, 32, None) == 0
+
+
 def multi(descs):
     arr = (B._Mxfp8Tensor * max(len(descs), 1))(*[B._Mxfp8Tensor(*d) for d in descs])
     return B.lib().quantize_mxfp8_multi(ctypes.cast(arr, ctypes.c_void_p), len(descs), None)

@@ -342,3 +342,22 @@ def test_linear_mxfp4_layer_matches_direct_calls():
         ah = om4.dequantize_exact(host(A), host(sA))
         bh = om4.dequantize_exact(host(Bq), host(sB))
         assert_gemm_close(host(got), ah @ bh.T, "linear mxfp4")
+
+
+def test_linear_fp8_block_layer_matches_direct_calls():
+    g = inputs.rng(123, 0)
+    T, Di, Do = 256, 384, 640
+    x = dev_bf16(inputs.normal_bf16(g, (T, Di), 1.0))
+    w = dev_bf16(inputs.normal_bf16(g, (Do, Di), 0.02))
+    dy = dev_bf16(inputs.normal_bf16(g, (T, Do), 1e-3))
+    L = pipeline.LinearFp8Block(T, Di, Do, torch.device("cuda:0"))
+    L.step(x, w, dy)
+    for got, ref in ((L.qx, mxq.quantize_fp8_block_act(x, True, True)), (L.qw, mxq.quantize_fp8_block_weight(w)),
+                     (L.qdy, mxq.quantize_fp8_block_act(dy, True, True))):
+        for a, b in zip(got, ref):
+            assert_bytes_equal(host(a).view(np.uint8), host(b).view(np.uint8), "fp8 block copy")
+    for got, args, blocks in ((L.y, (L.qx[0], L.qx[1], L.qw[0], L.qw[1]), True),
+                              (L.dx, (L.qdy[0], L.qdy[1], L.qw[2], L.qw[3]), True),
+                              (L.dw, (L.qdy[2], L.qdy[3], L.qx[2], L.qx[3]), False)):
+        ref = mxq.gemm_fp8_blockwise(*args, b_blocks=blocks)
+        assert_bytes_equal(host(got).view(np.uint32), host(ref).view(np.uint32), "fp8 block gemm")

@@ -133,21 +133,20 @@ class Linear:
         s = self.sets[i % self.N_SETS]
         L = self.layer
         n_el = self.T * self.DIN + self.DOUT * self.DIN + self.T * self.DOUT
-        out = [Stage("quantize_mxfp8_rowcol", lambda: L.quantize(s["x"], s["w"], s["dy"]), n_el * MX_ROWCOL, "hbm")]
-        out += [Stage("gemm_block_scaled_mxfp8", (lambda g=g: L.gemm(g)), self.gemm_flop, "mfma", "bf16")
-                for g in ("fprop", "dgrad", "wgrad")]
-        return out
+        # one quantize launch (six copies), one batched launch of fprop, dgrad and wgrad
+        return [Stage("quantize_mxfp8_rowcol", lambda: L.quantize(s["x"], s["w"], s["dy"]), n_el * MX_ROWCOL, "hbm"),
+                Stage("gemm_block_scaled_mxfp8", L.gemm_all, 3 * self.gemm_flop, "mfma", "bf16")]
 
     def extra_components(self):
         """Outside the step: the same layer in MXFP4 (E2M1 + E8M0 per 32) on the native FP4
-        scaled MFMA (one row+col quantize launch of X, W, dY, then the three GEMMs), and in
+        scaled MFMA (one row+col quantize launch of X, W, dY, one batched launch of the three
+        GEMMs), and in
         DeepSeek-V3-style blockwise FP8 (three quantize launches, three GEMMs on the BF16
         datapath with the FP32 block scales applied in software)."""
         s, L4 = self.sets[0], self.layer4
         n_el = self.T * self.DIN + self.DOUT * self.DIN + self.T * self.DOUT
         out = [Stage("quantize_mxfp4_rowcol", lambda: L4.quantize(s["x"], s["w"], s["dy"]), n_el * MX4_ROWCOL, "hbm")]
-        out += [Stage("gemm_block_scaled_mxfp4_" + g, (lambda g=g: L4.gemm(g)), self.gemm_flop, "mfma", "fp4")
-                for g in ("fprop", "dgrad", "wgrad")]
+        out += [Stage("gemm_block_scaled_mxfp4", L4.gemm_all, 3 * self.gemm_flop, "mfma", "fp4")]
         # DeepSeek-V3-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks)
         L8 = self.layer8b
         w_el = self.DOUT * self.DIN
@@ -400,9 +399,8 @@ class Stress:
         s = self.sets[i % self.N_SETS]
         st, n = self.st, self.N
         import microscaling_precision_quantization_amd as mxq
-        out = [Stage("quantize_mxfp8_rowcol", lambda: st.quantize_mxfp8(s["a"], s["b"]), 2 * n * n * MX_ROWCOL, "hbm")]
-        out += [Stage("gemm_block_scaled_mxfp8", (lambda g=g: st.mxfp8_gemm(g)), 2 * n ** 3, "mfma", "bf16")
-                for g in ("fprop", "dgrad", "wgrad")]
+        out = [Stage("quantize_mxfp8_rowcol", lambda: st.quantize_mxfp8(s["a"], s["b"]), 2 * n * n * MX_ROWCOL, "hbm"),
+               Stage("gemm_block_scaled_mxfp8", st.mxfp8_gemm_all, 3 * 2 * n ** 3, "mfma", "bf16")]
         out += [Stage("quantize_nvfp4_rht_colwise", lambda: st.quantize_rht(s["a"], s["b"]),
                       2 * n * n * (2 + 2 + 0.5 + 1 / 16), "hbm"),
                 Stage("gemm_block_scaled_nvfp4", st.nvfp4_wgrad, 2 * n ** 3, "mfma", "fp16")]

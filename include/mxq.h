@@ -380,6 +380,39 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K,
                              float* C, int64_t ldc, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gemm_block_scaled_batch -- up to MXQ_GEMM_BATCH_MAX independent gemm_block_scaled
+ * problems of one format in one launch (e.g. the fprop, dgrad and wgrad GEMMs of a
+ * linear layer, which all read the quantized copies made once by the quantizer).
+ *   Defined by: as gemm_block_scaled (remio.ai, sections "Un Cuantizador Compartido ..."
+ *   and "La Compatibilidad ..."; 7minutos.es, section "Que esta cuantificado y que no").
+ *   Each problem's C is bit-identical to what gemm_block_scaled writes for it (same
+ *   accumulation order). The problems share one launch, longest K first, so one
+ *   problem's output stores overlap another's main loop; a problem too small for the
+ *   batch's 256 x 256 tiles (fewer than 128 of them) runs as its own launch on the same
+ *   stream instead.
+ *   problems : HOST array of `count` descriptors (1 <= count <= MXQ_GEMM_BATCH_MAX); each
+ *              field follows gemm_block_scaled's argument of the same name (tA/tB and
+ *              their scopes are used for MXQ_NVFP4 only, scopes ROW or TENSOR). Problems
+ *              with M or N = 0 are skipped; any invalid descriptor fails the whole call
+ *              before anything is launched. Output buffers must not overlap.
+ * ------------------------------------------------------------------------- */
+#define MXQ_GEMM_BATCH_MAX 8
+typedef struct {
+  int64_t M, N, K;
+  const void* A;
+  const void* sA;
+  const float* tA;
+  mxq_scope tA_scope;
+  const void* B;
+  const void* sB;
+  const float* tB;
+  mxq_scope tB_scope;
+  float* C;
+  int64_t ldc;
+} mxq_gemm_problem;
+mxq_status gemm_block_scaled_batch(mxq_format fmt, const mxq_gemm_problem* problems, int count, void* stream);
+
+/* ---------------------------------------------------------------------------
  * gemm_fp8_blockwise -- C = A_hat B_hat^T (FP32 output, "TN") for blockwise FP8
  * operands, the FP32 scales applied in software around the matrix product.
  *   Defined by: DeepSeek-V3-style FP8 with 128 x 128 weight blocks, 1 x 128 activation

@@ -35,6 +35,7 @@ _SIGS = {
     "quantize_mxfp4_multi": [_c_void_p, _int, _c_void_p],
     "quantize_fp8_block_act": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_fp8_block_weight": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "gemm_block_scaled_batch": [_int, _c_void_p, _int, _c_void_p],
     "gemm_fp8_blockwise": [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _i64,
                            _c_void_p],
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
@@ -342,6 +343,29 @@ def gemm_block_scaled(fmt: int, A, sA, B, sB, tA=None, tB=None, tA_scope="row", 
                                                         _ptr(B), _ptr(sB), _ptr(tB), SCOPE[tB_scope], _ptr(out),
                                                         out.stride(0), _stream(A.device)))
     return out
+
+
+class _GemmProblem(ctypes.Structure):
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("A", _c_void_p), ("sA", _c_void_p), ("tA", _c_void_p),
+                ("tA_scope", _int), ("B", _c_void_p), ("sB", _c_void_p), ("tB", _c_void_p), ("tB_scope", _int),
+                ("C", _c_void_p), ("ldc", _i64)]
+
+
+def gemm_block_scaled_batch(fmt: int, problems):
+    """Several gemm_block_scaled problems of one format in one launch. problems: list of
+    dicts with A, sA, B, sB, out and optionally tA, tB, tA_scope, tB_scope."""
+    n = len(problems)
+    arr = (_GemmProblem * n)()
+    dev = problems[0]["A"].device
+    for i, q in enumerate(problems):
+        A, B_, out = q["A"], q["B"], q["out"]
+        K = A.shape[1] * (2 if fmt in _PACKED4 else 1)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        arr[i] = _GemmProblem(A.shape[0], B_.shape[0], K, A.data_ptr(), ptr(q.get("sA")), ptr(q.get("tA")),
+                              SCOPE[q.get("tA_scope", "row")], B_.data_ptr(), ptr(q.get("sB")), ptr(q.get("tB")),
+                              SCOPE[q.get("tB_scope", "tensor")], out.data_ptr(), out.stride(0))
+    _check("gemm_block_scaled_batch", lib().gemm_block_scaled_batch(fmt, ctypes.cast(arr, _c_void_p), n, _stream(dev)))
+    return [q["out"] for q in problems]
 
 
 def gemm_fp8_blockwise(A, sA, B, sB, b_blocks: bool = True, out=None):

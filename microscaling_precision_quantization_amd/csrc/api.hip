@@ -36,6 +36,10 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
                                const void* sA, const float* tA, int tA_mode, const void* B, const void* sB,
                                const float* tB, int tB_mode, float* C, void* ws, hipStream_t st);
 size_t grouped_gemm_ws_bytes(int64_t groups);
+hipError_t launch_gemm_batch(int fmt, int n, const int64_t* M, const int64_t* N, const int64_t* K,
+                             const void* const* A, const void* const* sA, const float* const* tA, const int* tA_mode,
+                             const void* const* B, const void* const* sB, const float* const* tB, const int* tB_mode,
+                             float* const* C, const int64_t* ldc, hipStream_t st);
 hipError_t launch_gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const void* B,
                                          const void* sB, float* C, int64_t ldc, hipStream_t st);
 }  // namespace mxq
@@ -362,6 +366,46 @@ mxq_status gemm_block_scaled(mxq_format fmt, int64_t M, int64_t N, int64_t K, co
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   if (M == 0 || N == 0) return MXQ_OK;
   return hip_status(mxq::launch_gemm((int)fmt, M, N, K, A, sA, tA, ta, B, sB, tB, tb, C, ldc, S(stream)));
+}
+
+mxq_status gemm_block_scaled_batch(mxq_format fmt, const mxq_gemm_problem* problems, int count, void* stream) {
+  if (count < 1 || count > MXQ_GEMM_BATCH_MAX) return MXQ_ERR_SHAPE;
+  if (!problems) return MXQ_ERR_NULL;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4) return MXQ_ERR_FORMAT;
+  int64_t M[MXQ_GEMM_BATCH_MAX], N[MXQ_GEMM_BATCH_MAX], K[MXQ_GEMM_BATCH_MAX], ldc[MXQ_GEMM_BATCH_MAX];
+  const void *A[MXQ_GEMM_BATCH_MAX], *sA[MXQ_GEMM_BATCH_MAX], *B[MXQ_GEMM_BATCH_MAX], *sB[MXQ_GEMM_BATCH_MAX];
+  const float *tA[MXQ_GEMM_BATCH_MAX], *tB[MXQ_GEMM_BATCH_MAX];
+  int ta[MXQ_GEMM_BATCH_MAX], tb[MXQ_GEMM_BATCH_MAX];
+  float* C[MXQ_GEMM_BATCH_MAX];
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const mxq_gemm_problem& q = problems[i];
+    if (q.M < 0 || q.N < 0 || q.K < 0) return MXQ_ERR_SHAPE;
+    if (q.M == 0 || q.N == 0) continue;                       // empty problems are skipped
+    if (!q.A || !q.B || !q.C) return MXQ_ERR_NULL;
+    if (fmt != MXQ_BF16 && (!q.sA || !q.sB)) return MXQ_ERR_NULL;
+    int a_mode = 0, b_mode = 0;
+    if (fmt == MXQ_NVFP4) {
+      if (!q.tA || !q.tB) return MXQ_ERR_NULL;
+      a_mode = scope_mode(q.tA_scope);
+      b_mode = scope_mode(q.tB_scope);
+      if ((a_mode != 0 && a_mode != 1) || (b_mode != 0 && b_mode != 1)) return MXQ_ERR_FORMAT;
+    }
+    if (fmt != MXQ_BF16 && q.K % 32) return MXQ_ERR_SHAPE;
+    if (fmt == MXQ_BF16 && q.K % 8) return MXQ_ERR_SHAPE;
+    if (q.K > kMaxGemmK || q.ldc < q.N) return MXQ_ERR_SHAPE;
+    if (!al16(q.A) || !al16(q.B) || !al4(q.C)) return MXQ_ERR_ALIGN;
+    M[n] = q.M; N[n] = q.N; K[n] = q.K; ldc[n] = q.ldc;
+    A[n] = q.A; sA[n] = q.sA; tA[n] = q.tA; ta[n] = a_mode;
+    B[n] = q.B; sB[n] = q.sB; tB[n] = q.tB; tb[n] = b_mode;
+    C[n] = q.C;
+    ++n;
+  }
+  if (n == 0) return MXQ_OK;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) blocks += ((M[i] + 127) / 128) * ((N[i] + 127) / 128) + 8;
+  if (blocks > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+  return hip_status(mxq::launch_gemm_batch((int)fmt, n, M, N, K, A, sA, tA, ta, B, sB, tB, tb, C, ldc, S(stream)));
 }
 
 mxq_status gemm_fp8_blockwise(int64_t M, int64_t N, int64_t K, const void* A, const float* sA, const void* B,

@@ -48,6 +48,7 @@
 // Operand layouts of the 32x32x16 16-bit MFMAs (measured): lane l supplies row
 // l % 32 and 8 consecutive K; accumulator r of lane l is
 // C[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32].
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -824,6 +825,42 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   exact_gemm_tile<LD, BM, BN, SM, 1, WIDE>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
+// Several independent dense problems in one launch (e.g. the fprop, dgrad and wgrad GEMMs
+// of a layer): workgroups [block0, block0 + 8 ceil(tiles / 8)) belong to job j. The host
+// orders jobs by K, longest first, so the long tiles start first and the epilogue stores of
+// finished tiles overlap the main loops of others.
+constexpr int kMaxBatch = 8;
+struct BatchJob {
+  ExactProblem p;
+  int64_t tiles_m, tiles_n, block0;
+};
+struct BatchJobs {
+  BatchJob j[kMaxBatch];
+  int n;
+};
+
+template <int LD, int BM, int BN, int SM, bool WIDE>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) exact_batch_kernel(const BatchJobs jobs) {
+  using C = gx::Cfg<LD, BM, BN, SM, 1, WIDE>;
+  MXQ_EXACT_LDS(C)
+  int jsel = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (i < jobs.n && (int64_t)blockIdx.x >= jobs.j[i].block0) jsel = i;
+  int64_t tm = 0, tn = 0;
+  ExactProblem p;
+  bool ok = false;
+  // static indices only: the table stays in kernel arguments
+#pragma unroll
+  for (int i = 0; i < kMaxBatch; ++i)
+    if (i == jsel) {
+      p = jobs.j[i].p;
+      ok = exact_map_tile((int64_t)blockIdx.x - jobs.j[i].block0, jobs.j[i].tiles_m, jobs.j[i].tiles_n, tm, tn);
+    }
+  if (!ok) return;
+  exact_gemm_tile<LD, BM, BN, SM, 1, WIDE>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
+}
+
 // Group of a tile: the largest g with tile_prefix[g] <= tile (tile_prefix is non-decreasing
 // and tile < tile_prefix[groups]). Each wave narrows the range 64-fold per round with one
 // load per lane and a ballot (two rounds for up to 4096 groups).
@@ -939,6 +976,81 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, 
   else if (fmt == 2) launch_dense_ld<2>(p, M, N, K, st);
   else if (fmt == 4) launch_dense_ld<3>(p, M, N, K, st);
   else launch_dense_ld<0>(p, M, N, K, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const float* tA,
+                       int tA_mode, const void* B, const void* sB, const float* tB, int tB_mode, float* C,
+                       int64_t ldc, hipStream_t st);
+
+// Batched dense GEMMs of one format: one launch, jobs ordered by K (longest first), one
+// tile size and scale mode for all (the largest the batch allows). With 256 x 256 tiles, a
+// job that would cover fewer than 128 of them (too few to share the CUs with the others
+// for long) runs as its own launch with the single-problem tile rule instead.
+hipError_t launch_gemm_batch(int fmt, int n, const int64_t* M, const int64_t* N, const int64_t* K,
+                             const void* const* A, const void* const* sA, const float* const* tA, const int* tA_mode,
+                             const void* const* B, const void* const* sB, const float* const* tB, const int* tB_mode,
+                             float* const* C, const int64_t* ldc, hipStream_t st) {
+  const int ld = fmt == 1 ? 1 : fmt == 2 ? 2 : fmt == 4 ? 3 : 0;
+  int order[kMaxBatch];
+  for (int i = 0; i < n; ++i) order[i] = i;
+  for (int i = 1; i < n; ++i)                          // insertion sort, K descending (stable)
+    for (int k = i; k > 0 && K[order[k]] > K[order[k - 1]]; --k) std::swap(order[k], order[k - 1]);
+  int64_t t256 = 0;
+  for (int i = 0; i < n; ++i) t256 += ((M[i] + 255) / 256) * ((N[i] + 255) / 256);
+  const int bt = t256 >= 192 ? 256 : 128;
+  bool alone[kMaxBatch];
+  int sm = 2, nb = 0;
+  for (int i = 0; i < n; ++i) {
+    alone[i] = bt == 256 && ((M[i] + 255) / 256) * ((N[i] + 255) / 256) < 128;
+    if (!alone[i]) { sm = std::min(sm, scale_mode(ld, K[i], false)); ++nb; }
+  }
+  BatchJobs jobs;
+  jobs.n = 0;
+  int64_t blocks = 0;
+  for (int q = 0; q < n; ++q) {
+    const int i = order[q];
+    if (alone[i]) continue;
+    const int qq = jobs.n++;
+    ExactProblem& p = jobs.j[qq].p;
+    p.A = (const uint8_t*)A[i]; p.sA = (const uint8_t*)sA[i]; p.tA = tA[i]; p.tA_mode = tA_mode[i];
+    p.a_idx = nullptr; p.a_rows = M[i]; p.a_base = 0; p.m_valid = M[i]; p.lda = K[i];
+    p.B = (const uint8_t*)B[i]; p.sB = (const uint8_t*)sB[i]; p.tB = tB[i]; p.tB_mode = tB_mode[i];
+    p.n_valid = N[i]; p.ldb = K[i];
+    p.k_begin = 0; p.k_end = K[i]; p.C = C[i]; p.ldc = ldc[i];
+    jobs.j[qq].tiles_m = (M[i] + bt - 1) / bt;
+    jobs.j[qq].tiles_n = (N[i] + bt - 1) / bt;
+    jobs.j[qq].block0 = blocks;
+    blocks += (jobs.j[qq].tiles_m * jobs.j[qq].tiles_n + 7) / 8 * 8;    // XCD-aware raster per job
+  }
+  for (int q = 0; q < n; ++q) {                       // the jobs that run alone, longest K first
+    const int i = order[q];
+    if (!alone[i]) continue;
+    const hipError_t e = launch_gemm(fmt, M[i], N[i], K[i], A[i], sA[i], tA[i], tA_mode[i], B[i], sB[i], tB[i],
+                                     tB_mode[i], C[i], ldc[i], st);
+    if (e != hipSuccess) return e;
+  }
+  if (nb == 0 || blocks == 0) return hipGetLastError();
+  auto go = [&](auto LDC, auto BTC, auto SMC) {
+    constexpr int L = decltype(LDC)::value, T = decltype(BTC)::value, S = decltype(SMC)::value;
+    constexpr bool WIDE = S == 2 && L != 0;
+    hipLaunchKernelGGL((exact_batch_kernel<L, T, T, S, WIDE>), dim3((unsigned)blocks), dim3(256), 0, st, jobs);
+  };
+  auto by_sm = [&](auto LDC, auto BTC) {
+    if constexpr (decltype(LDC)::value != 0) {
+      if (sm == 2) { go(LDC, BTC, ic<2>{}); return; }
+    }
+    if (sm >= 1) go(LDC, BTC, ic<1>{});
+    else go(LDC, BTC, ic<0>{});
+  };
+  auto by_bt = [&](auto LDC) {
+    if (bt == 256) by_sm(LDC, ic<256>{});
+    else by_sm(LDC, ic<128>{});
+  };
+  if (ld == 1) by_bt(ic<1>{});
+  else if (ld == 2) by_bt(ic<2>{});
+  else if (ld == 3) by_bt(ic<3>{});
+  else by_bt(ic<0>{});
   return hipGetLastError();
 }
 

@@ -60,14 +60,20 @@ class LinearMxfp8:
         return {"fprop": (xr, xrs, wr, wrs, self.y), "dgrad": (dr, drs, wc, wcs, self.dx),
                 "wgrad": (dc, dcs, xc, xcs, self.dw)}
 
+    FMT = B.MXFP8
+
     def gemm(self, name: str):
         A, sA, Bq, sB, out = self.gemm_args()[name]
-        B.gemm_block_scaled(B.MXFP8, A, sA, Bq, sB, out=out)
+        B.gemm_block_scaled(self.FMT, A, sA, Bq, sB, out=out)
+
+    def gemm_all(self):
+        """fprop, dgrad and wgrad in one batched launch (bit-identical to three calls)."""
+        B.gemm_block_scaled_batch(self.FMT, [dict(A=A, sA=sA, B=Bq, sB=sB, out=out)
+                                             for A, sA, Bq, sB, out in self.gemm_args().values()])
 
     def step(self, x, w, dy):
         self.quantize(x, w, dy)
-        for n in ("fprop", "dgrad", "wgrad"):
-            self.gemm(n)
+        self.gemm_all()
 
 
 class LinearMxfp4(LinearMxfp8):
@@ -80,12 +86,10 @@ class LinearMxfp4(LinearMxfp8):
                   for n, (r, c) in {"x": (T, Di), "w": (Do, Di), "dy": (T, Do)}.items()}
         self.y, self.dx, self.dw = _f32((T, Do), dev), _f32((T, Di), dev), _f32((Do, Di), dev)
 
+    FMT = B.MXFP4
+
     def quantize(self, x, w, dy):
         B.quantize_mxfp4_multi([x, w, dy], [self.q["x"], self.q["w"], self.q["dy"]])
-
-    def gemm(self, name: str):
-        A, sA, Bq, sB, out = self.gemm_args()[name]
-        B.gemm_block_scaled(B.MXFP4, A, sA, Bq, sB, out=out)
 
 
 class LinearFp8Block:
@@ -384,6 +388,11 @@ class StressStep:
         A, sA, Bq, sB = self.mxfp8_gemm_args()[name]
         B.gemm_block_scaled(B.MXFP8, A, sA, Bq, sB, out=self.c[name])
 
+    def mxfp8_gemm_all(self):
+        """fprop, dgrad and wgrad in one batched launch (bit-identical to three calls)."""
+        B.gemm_block_scaled_batch(B.MXFP8, [dict(A=A, sA=sA, B=Bq, sB=sB, out=self.c[k])
+                                            for k, (A, sA, Bq, sB) in self.mxfp8_gemm_args().items()])
+
     def quantize_rht(self, a, b):
         for k, x in (("a", a), ("b", b)):
             q, s, t = self.nv[k]
@@ -420,7 +429,6 @@ class StressStep:
 
     def step(self, a, b):
         self.quantize_mxfp8(a, b)
-        for k in ("fprop", "dgrad", "wgrad"):
-            self.mxfp8_gemm(k)
+        self.mxfp8_gemm_all()
         self.quantize_rht(a, b)
         self.nvfp4_wgrad()

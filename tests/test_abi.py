@@ -88,6 +88,22 @@ def test_fp8_block_validation():
     assert g(0, 32, 128, P, P, P, P, 1, P, 32, None) == 0
 
 
+def test_gemm_batch_validation():
+    L = B.lib()
+    mk = lambda *d: (B._GemmProblem * len(d))(*[B._GemmProblem(*x) for x in d])
+    ok = (32, 32, 64, P, P, None, 0, P, P, None, 0, P, 32)
+    call = lambda fmt, arr, n: L.gemm_block_scaled_batch(fmt, ctypes.cast(arr, ctypes.c_void_p), n, None)
+    assert call(1, mk(ok), 0) == 2
+    assert call(1, mk(*[ok] * 9), 9) == 2
+    assert call(9, mk(ok), 1) == 4
+    assert call(1, mk(ok, (32, 32, 48, P, P, None, 0, P, P, None, 0, P, 32)), 2) == 2     # K % 32
+    assert call(1, mk(ok, (32, 32, 64, P, None, None, 0, P, P, None, 0, P, 32)), 2) == 1  # scales missing
+    assert call(2, mk((32, 32, 64, P, P, None, 0, P, P, P, 1, P, 32)), 1) == 1             # NVFP4 without tA
+    assert call(1, mk(ok, (32, 32, 64, MIS, P, None, 0, P, P, None, 0, P, 32)), 2) == 3
+    assert call(1, mk((0, 32, 64, None, None, None, 0, None, None, None, 0, None, 32)), 1) == 0   # empty: no-op
+    assert L.gemm_block_scaled_batch(1, None, 1, None) == 1
+
+
 def multi(descs):
     arr = (B._Mxfp8Tensor * max(len(descs), 1))(*[B._Mxfp8Tensor(*d) for d in descs])
     return B.lib().quantize_mxfp8_multi(ctypes.cast(arr, ctypes.c_void_p), len(descs), None)

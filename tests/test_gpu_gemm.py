@@ -368,3 +368,56 @@ def test_mxfp8_exact_path_integer_operands_exact():
     qb, sb, _ = mx_operands(inputs.to_bf16_bits(b))
     c = host(mxq.gemm_block_scaled(mxq.MXFP8, qa, sa, qb, sb))
     assert np.array_equal(c, (a @ b.T).astype(np.float32))
+
+
+# ------------------------------ batched -------------------------------------
+
+def _batch_case(fmt, shapes, seed):
+    g = inputs.rng(150, seed)
+    probs = []
+    for M, N, K in shapes:
+        if M == 0:                                     # an empty problem: skipped by the batch
+            u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device="cuda")
+            probs.append(dict(A=u8(0, K), sA=u8(0, K // 32), B=u8(N, K), sB=u8(N, K // 32),
+                              out=torch.empty((0, N), device="cuda")))
+            continue
+        a = inputs.to_bf16_bits(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))
+        b = inputs.normal_bf16(g, (N, K), 0.05)
+        if fmt == mxq.MXFP8:
+            qa, sa, _, _ = mxq.quantize_mxfp8(dev_bf16(a), True, False)
+            qb, sb, _, _ = mxq.quantize_mxfp8(dev_bf16(b), True, False)
+            d = dict(A=qa, sA=sa, B=qb, sB=sb)
+        elif fmt == mxq.MXFP4:
+            qa, sa, _, _ = mxq.quantize_mxfp4(dev_bf16(a), True, False)
+            qb, sb, _, _ = mxq.quantize_mxfp4(dev_bf16(b), True, False)
+            d = dict(A=qa, sA=sa, B=qb, sB=sb)
+        elif fmt == mxq.NVFP4:
+            qa, sa, ta = mxq.quantize_nvfp4_per_token(dev_bf16(a))
+            qb, sb, tb = mxq.quantize_nvfp4(dev_bf16(b), scope="tensor")
+            d = dict(A=qa, sA=sa, B=qb, sB=sb, tA=ta, tB=tb, tA_scope="row", tB_scope="tensor")
+        else:
+            d = dict(A=dev_bf16(a), sA=None, B=dev_bf16(b), sB=None)
+        d["out"] = torch.full((M, N + 3), 5.0, device="cuda")[:, :N]
+        probs.append(d)
+    return probs
+
+
+@pytest.mark.parametrize("fmt,shapes", [
+    ("mxfp8", [(2048, 8192, 2048), (2048, 2048, 8192), (8192, 2048, 2048)]),     # the linear layer's three GEMMs
+    ("mxfp8", [(300, 200, 96), (64, 1000, 1024), (257, 513, 160), (0, 64, 64)]),  # ragged, K % 64 != 0, empty
+    ("nvfp4", [(300, 200, 256), (256, 512, 2048)]),
+    ("mxfp4", [(4196, 3112, 512), (64, 1000, 1024), (32, 32, 32)]),
+    ("bf16", [(300, 200, 96), (128, 256, 1024)]),
+])
+def test_gemm_batch_matches_single_calls(fmt, shapes):
+    f = {"mxfp8": mxq.MXFP8, "nvfp4": mxq.NVFP4, "mxfp4": mxq.MXFP4, "bf16": mxq.BF16}[fmt]
+    probs = _batch_case(f, shapes, len(shapes) + f)
+    mxq.gemm_block_scaled_batch(f, probs)
+    for q, (M, N, K) in zip(probs, shapes):
+        if M == 0:
+            continue
+        ref = mxq.gemm_block_scaled(f, q["A"], q["sA"], q["B"], q["sB"], tA=q.get("tA"), tB=q.get("tB"),
+                                    tA_scope=q.get("tA_scope", "row"), tB_scope=q.get("tB_scope", "tensor"))
+        got = host(q["out"].contiguous())
+        assert np.array_equal(got.view(np.uint32), host(ref).view(np.uint32)), (fmt, M, N, K)
+        assert np.all(host(q["out"].as_strided((M, 3), (N + 3, 1), N)) == 5.0)     # padding columns untouched

@@ -187,8 +187,8 @@ swiglu_nvfp4_kernel(const float* __restrict__ gu, int64_t rows, int64_t inter, u
     const int64_t e = (int64_t)i * 512 + 8 * lane;
     uint32_t p[4] = {0, 0, 0, 0};
     if (e < inter) {
-      const float4 g0 = *reinterpret_cast<const float4*>(g + e), g1 = *reinterpret_cast<const float4*>(g + e + 4);
-      const float4 u0 = *reinterpret_cast<const float4*>(u + e), u1 = *reinterpret_cast<const float4*>(u + e + 4);
+      const float4 g0 = load_stream16f(g + e), g1 = load_stream16f(g + e + 4);
+      const float4 u0 = load_stream16f(u + e), u1 = load_stream16f(u + e + 4);
       p[0] = f32_to_bf16_rne(swiglu1(g0.x, u0.x)) | (f32_to_bf16_rne(swiglu1(g0.y, u0.y)) << 16);
       p[1] = f32_to_bf16_rne(swiglu1(g0.z, u0.z)) | (f32_to_bf16_rne(swiglu1(g0.w, u0.w)) << 16);
       p[2] = f32_to_bf16_rne(swiglu1(g1.x, u1.x)) | (f32_to_bf16_rne(swiglu1(g1.y, u1.y)) << 16);
@@ -264,7 +264,7 @@ combine_kernel(const float* __restrict__ o, int64_t total_slots, int64_t topk, i
       const float wj = w[tok * topk + j];
       const int64_t slot = slot_of[tok * topk + j];
       if (slot < 0 || slot >= total_slots) continue;
-      const float4 v = *reinterpret_cast<const float4*>(o + slot * hidden + c);
+      const float4 v = load_stream16f(o + slot * hidden + c);
       acc.x += wj * v.x; acc.y += wj * v.y; acc.z += wj * v.z; acc.w += wj * v.w;
     }
     *reinterpret_cast<float4*>(y + tok * hidden + c) = acc;

@@ -92,7 +92,7 @@ quant_mxfp8_kernel(const QJobs jobs) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t r = R0 + rl0 + j;
-    v[j] = (col_ok && r < rows) ? *reinterpret_cast<const uint4*>(x + r * ld_x + c) : make_uint4(0, 0, 0, 0);
+    v[j] = (col_ok && r < rows) ? load_stream16(x + r * ld_x + c) : make_uint4(0, 0, 0, 0);
   }
 
   if (DO_ROW) {

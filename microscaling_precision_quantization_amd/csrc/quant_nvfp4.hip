@@ -170,7 +170,7 @@ nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t e = (int64_t)i * 512 + 8 * lane;
-    v[i] = (e < cols) ? *reinterpret_cast<const uint4*>(xr + e) : make_uint4(0, 0, 0, 0);
+    v[i] = (e < cols) ? load_stream16(xr + e) : make_uint4(0, 0, 0, 0);
     if (!RHT)
       amax_bits = pk_max_u16(amax_bits, pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
                                                    pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu)));
@@ -275,7 +275,7 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
   uint4 v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    v[j] = ok ? *reinterpret_cast<const uint4*>(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
+    v[j] = ok ? load_stream16(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
 
   float sg[16];
   if (RHT) {
@@ -423,7 +423,7 @@ nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int6
   uint4 v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    v[j] = ok ? *reinterpret_cast<const uint4*>(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
+    v[j] = ok ? load_stream16(x + (r0 + j) * ld_x + c) : make_uint4(0, 0, 0, 0);
   float s_enc = 1.0f;
   if (ok) {
     float tt;

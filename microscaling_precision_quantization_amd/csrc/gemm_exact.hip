@@ -1146,9 +1146,11 @@ template <int LD, int BT, int SM>
 static void launch_grouped_t(const ExactProblem& p, const int64_t* offsets, const int64_t* prefix, int64_t max_tiles,
                              int64_t groups, int vary_k, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tn = (N + BT - 1) / BT;
-  // expert tiles keep the narrow stages: wide NVFP4 stages leave two LDS stages at half LDS
-  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, 2, false>), dim3((unsigned)max_tiles), dim3(256), 0, st, p, offsets,
-                     prefix, groups, vary_k, M, N, tn);
+  // expert tiles keep the narrow stages: wide NVFP4 stages leave two LDS stages at half LDS.
+  // 128 x 128 tiles run two workgroups per CU, 256 x 256 tiles one.
+  constexpr int OCC = BT == 256 ? 1 : 2;
+  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, OCC, false>), dim3((unsigned)max_tiles), dim3(256), 0, st, p,
+                     offsets, prefix, groups, vary_k, M, N, tn);
 }
 
 hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, int vary_k, int64_t total, int64_t M,
@@ -1156,8 +1158,10 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
                                const void* sA, const float* tA, int tA_mode, const void* B, const void* sB,
                                const float* tB, int tB_mode, float* C, void* ws, hipStream_t st) {
   int64_t* prefix = (int64_t*)ws;
-  // Expert groups are small (hundreds of rows): 128 x 128 tiles.
-  constexpr int BT = 128;
+  // Expert groups are small (hundreds of rows): 128 x 128 tiles. A weight gradient
+  // (vary_k) has the full (M, N) output per group: 256 x 256 tiles once that gives each
+  // group at least 64 of them.
+  const int BT = (vary_k && ((M + 255) / 256) * ((N + 255) / 256) >= 64) ? 256 : 128;
   const int64_t tiles_n = (N + BT - 1) / BT;
   const int64_t tiles_m_fixed = vary_k ? (M + BT - 1) / BT : 0;
   const int64_t align = (fmt == 1 || fmt == 4) ? 32 : fmt == 2 ? 16 : 8;
@@ -1177,7 +1181,14 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   const int ld = fmt == 1 ? 1 : fmt == 2 ? 2 : fmt == 4 ? 3 : 0;
   const int sm = scale_mode(ld, p.lda, vary_k != 0);
   auto go = [&](auto LDC, auto SMC) {
-    launch_grouped_t<decltype(LDC)::value, BT, decltype(SMC)::value>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+    constexpr int L = decltype(LDC)::value, S = decltype(SMC)::value;
+    if constexpr (S == 0 && L != 2) {         // vary_k runs with SM 0 and never with NVFP4
+      if (BT == 256) {
+        launch_grouped_t<L, 256, S>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+        return;
+      }
+    }
+    launch_grouped_t<L, 128, S>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
   };
   auto by_sm = [&](auto LDC) {
     if constexpr (decltype(LDC)::value != 0) {

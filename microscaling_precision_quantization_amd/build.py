@@ -22,8 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quant_mxfp8.hip", "quant_nvfp4.hip", "quant_fp8_block.hip", "dequant_moe.hip", "gemm_mxfp8.hip",
-           "gemm_exact.hip"]
+SOURCES = ["api.hip", "quant_mxfp8.hip", "quant_nvfp4.hip", "quant_fp8_block.hip", "dequant_moe.hip", "gemm_exact.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

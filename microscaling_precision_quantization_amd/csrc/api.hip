@@ -40,8 +40,6 @@ hipError_t launch_gemm_batch(int fmt, int n, const int64_t* M, const int64_t* N,
                              const void* const* A, const void* const* sA, const float* const* tA, const int* tA_mode,
                              const void* const* B, const void* const* sB, const float* const* tB, const int* tB_mode,
                              float* const* C, const int64_t* ldc, hipStream_t st);
-hipError_t launch_gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const void* B,
-                                         const void* sB, float* C, int64_t ldc, hipStream_t st);
 }  // namespace mxq
 
 namespace {
@@ -426,7 +424,7 @@ mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A
   if (K % 32 || ldc < N) return MXQ_ERR_SHAPE;
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   if (M == 0 || N == 0) return MXQ_OK;
-  return hip_status(mxq::launch_gemm_mxfp8_matrix_core(M, N, K, A, sA, B, sB, C, ldc, S(stream)));
+  return hip_status(mxq::launch_gemm(6, M, N, K, A, sA, nullptr, 0, B, sB, nullptr, 0, C, ldc, S(stream)));
 }
 
 mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64_t* offsets, int vary_k,

@@ -288,6 +288,21 @@ def test_grouped_bf16_vary_m():
     assert_gemm_close(host(c), ref, "bf16 grouped")
 
 
+def test_grouped_bf16_vary_m_large_groups():
+    """Groups averaging >= 384 rows run on 256 x 256 tiles: ragged group sizes (one
+    empty, one past two tiles), N not a multiple of the tile."""
+    g = inputs.rng(90, 0)
+    sizes = np.array([520, 0, 300, 700])
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    S, G, N, K = int(off[-1]), len(sizes), 300, 192
+    a = inputs.normal_bf16(g, (S, K), 1.0)
+    w = inputs.normal_bf16(g, (G * N, K), 0.05)
+    c = mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a), dev_bf16(w), N=N, K=K)
+    ref = omoe.grouped_gemm_ref(F.bf16_bits_to_f32(a).astype(np.float64), off,
+                                F.bf16_bits_to_f32(w).astype(np.float64).reshape(G, N, -1))
+    assert_gemm_close(host(c), ref, "bf16 grouped, large groups")
+
+
 # --------------------------------- MoE glue ---------------------------------
 
 def test_swiglu_requant_and_combine():

@@ -147,6 +147,27 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two FP32 -> two BF16 (RNE), element a in the low half: gfx950's packed convert. An
+// exhaustive check over every non-NaN binary32 input (denormals included, in the
+// library's denormal-preserving mode) matched f32_to_bf16_rne bit for bit.
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  v2f_t f;
+  f.x = a;
+  f.y = b;
+  const v2bf_t h = __builtin_convertvector(f, v2bf_t);
+  uint32_t o;
+  __builtin_memcpy(&o, &h, 4);
+  return o;
+}
+// Byte SEL of w (two E2M1 codes, low nibble first) -> two FP32 values, exact (hardware
+// decode with scale 2^0; checked against e2m1_to_f32 on all 256 bytes).
+template <int SEL>
+__device__ __forceinline__ v2f_t e2m1x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
 // E4M3 byte -> FP32 (exact). Codes 0x7F/0xFF (NaN) never occur in our data.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t e = (c >> 3) & 0xF, m = c & 7;

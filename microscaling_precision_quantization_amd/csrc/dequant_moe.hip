@@ -28,6 +28,17 @@ dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, con
   if (idx >= rows * per_row) return;
   const int64_t r = idx / per_row, c0 = (idx % per_row) * 16;
   float v[16];
+  // 16 E2M1 codes (8 bytes) -> v[0..15], scaled by sc (exact: E2M1 * E4M3 or * 2^k)
+  auto fp4x16 = [&](uint32_t w0, uint32_t w1, float sc) {
+    const uint32_t w[2] = {w0, w1};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const v2f_t e0 = e2m1x2_to_f32<0>(w[k]), e1 = e2m1x2_to_f32<1>(w[k]);
+      const v2f_t e2 = e2m1x2_to_f32<2>(w[k]), e3 = e2m1x2_to_f32<3>(w[k]);
+      v[8 * k + 0] = e0.x * sc; v[8 * k + 1] = e0.y * sc; v[8 * k + 2] = e1.x * sc; v[8 * k + 3] = e1.y * sc;
+      v[8 * k + 4] = e2.x * sc; v[8 * k + 5] = e2.y * sc; v[8 * k + 6] = e3.x * sc; v[8 * k + 7] = e3.y * sc;
+    }
+  };
   if (FMT == 1) {
     const uint4 b = *reinterpret_cast<const uint4*>(q + r * cols + c0);
     const float sc = e8m0_to_float(s[r * (cols / 32) + c0 / 32]);
@@ -36,20 +47,13 @@ dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, con
     for (int i = 0; i < 16; ++i) v[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFF) * sc;
   } else if (FMT == 4) {
     const uint2 b = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c0 / 2);
-    const float sc = e8m0_to_float(s[r * (cols / 32) + c0 / 32]);
-    const uint32_t w[2] = {b.x, b.y};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = e2m1_to_f32((w[i / 8] >> (4 * (i % 8))) & 0xF) * sc;   // exact
+    fp4x16(b.x, b.y, e8m0_to_float(s[r * (cols / 32) + c0 / 32]));
   } else {
     const uint2 b = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c0 / 2);
-    const float S = e4m3_to_f32(s[r * (cols / 16) + c0 / 16]);
     const float tt = t_mode == 0 ? t[r] : t_mode == 1 ? t[0] : t[r / group_rows];
-    const uint32_t w[2] = {b.x, b.y};
+    fp4x16(b.x, b.y, e4m3_to_f32(s[r * (cols / 16) + c0 / 16]));   // q * S exact
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float qs = e2m1_to_f32((w[i / 8] >> (4 * (i % 8))) & 0xF) * S;   // exact
-      v[i] = qs * tt;
-    }
+    for (int i = 0; i < 16; ++i) v[i] *= tt;
   }
   if (OUT_F32) {
     float4* o = reinterpret_cast<float4*>((float*)out + r * cols + c0);
@@ -58,7 +62,7 @@ dequant_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, con
   } else {
     uint32_t p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = f32_to_bf16_rne(v[2 * i]) | (f32_to_bf16_rne(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 8; ++i) p[i] = bf16x2_rne(v[2 * i], v[2 * i + 1]);
     uint4* o = reinterpret_cast<uint4*>((uint16_t*)out + r * cols + c0);
     o[0] = make_uint4(p[0], p[1], p[2], p[3]);
     o[1] = make_uint4(p[4], p[5], p[6], p[7]);
@@ -129,10 +133,17 @@ dequant_t_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, c
           const float tt = t_mode == 0 ? t[r] : t_mode == 1 ? t[0] : t[r / group_rows];
           const uint32_t w[2] = {b.x, b.y};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) v[i] = (e2m1_to_f32((w[i / 8] >> (4 * (i % 8))) & 0xF) * S) * tt;
+          for (int k = 0; k < 2; ++k) {                     // (q * S) exact, then * t
+            const v2f_t e0 = e2m1x2_to_f32<0>(w[k]), e1 = e2m1x2_to_f32<1>(w[k]);
+            const v2f_t e2 = e2m1x2_to_f32<2>(w[k]), e3 = e2m1x2_to_f32<3>(w[k]);
+            v[8 * k + 0] = (e0.x * S) * tt; v[8 * k + 1] = (e0.y * S) * tt;
+            v[8 * k + 2] = (e1.x * S) * tt; v[8 * k + 3] = (e1.y * S) * tt;
+            v[8 * k + 4] = (e2.x * S) * tt; v[8 * k + 5] = (e2.y * S) * tt;
+            v[8 * k + 6] = (e3.x * S) * tt; v[8 * k + 7] = (e3.y * S) * tt;
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = f32_to_bf16_rne(v[2 * i]) | (f32_to_bf16_rne(v[2 * i + 1]) << 16);
+        for (int i = 0; i < 8; ++i) p[i] = bf16x2_rne(v[2 * i], v[2 * i + 1]);
       }
     }
 #pragma unroll

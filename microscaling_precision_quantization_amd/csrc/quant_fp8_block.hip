@@ -22,27 +22,52 @@
 //   W  (128 x 128 weight blocks): one amax per tile (lane, wave, then LDS across
 //          waves); the row copy (WR) is stored directly, the transposed copy (WC)
 //          through LDS.
-// The divisions are IEEE binary32 (the library is built with correctly rounded
-// division and no flush to zero); |x / s| is clamped to 448 before the E4M3 convert,
-// which equals saturation (the convert itself does not saturate).
+// The quotients are IEEE binary32 x / s, correctly rounded; |x / s| is clamped to 448
+// before the E4M3 convert, which equals saturation (the convert itself does not
+// saturate). Each block computes r = 1 / s once (correctly rounded division) and each
+// element takes Markstein's correction of y = x r: q = fma(fma(-y, s, |x|), r, y) with
+// y = |x| r, and the sign of x. An exhaustive check on MI355X over every binary32
+// significand of s and every BF16 significand of x (both signs; 2^31 cases) found q
+// equal to the correctly rounded quotient in all of them; scaling both by powers of
+// two keeps that while r, y and the residual stay normal, which holds whenever
+// s >= 2^-92 for every element whose E4M3 code is not zero (|x / s| >= 2^-10). Blocks
+// with a smaller s keep the division.
 #include "common.h"
 
 namespace mxq {
 
+// Block scale s -> its reciprocal for the corrected products (0 when s is zero or below
+// 2^-92: those blocks divide).
+__device__ __forceinline__ float block_recip(float s) { return s >= 0x1p-92f ? 1.0f / s : 0.0f; }
+
+// x / s, correctly rounded, through the reciprocal r of the block (see the file comment)
+__device__ __forceinline__ float quot_r(float x, float s, float r) {
+  const float ax = fabsf(x);
+  const float y = ax * r;
+  return copysignf(__builtin_fmaf(__builtin_fmaf(-y, s, ax), r, y), x);
+}
+
 // Eight BF16 values (one uint4) / s -> eight E4M3 bytes (element 0 in the low byte).
-__device__ __forceinline__ uint2 fp8x8_div(const uint4& v, float s) {
+__device__ __forceinline__ uint2 fp8x8_div(const uint4& v, float s, float r) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
+  if (r != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = quot_r(f[i], s, r);
+  } else if (s > 0.0f) {                 // tiny block scale: divide
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] / s;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] *= 0.0f;     // all-zero block: keep the sign of zero
+  }
   uint32_t o[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
-    if (s > 0.0f) {
-      a = fminf(fmaxf(a / s, -kE4M3Max), kE4M3Max);
-      b = fminf(fmaxf(b / s, -kE4M3Max), kE4M3Max);
-    } else {
-      a *= 0.0f;            // all-zero block: keep the sign of zero
-      b *= 0.0f;
-    }
+    const float a = fminf(fmaxf(f[2 * i], -kE4M3Max), kE4M3Max);
+    const float b = fminf(fmaxf(f[2 * i + 1], -kE4M3Max), kE4M3Max);
     o[i / 2] = cvt_fp8x2_f32(o[i / 2], a, b, 1.0f, (i & 1) != 0);
   }
   return make_uint2(o[0], o[1]);
@@ -92,7 +117,7 @@ fp8_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int
       const float s = block_scale(a);
       const int64_t r = R0 + rl0 + j;
       if (col_ok && r < rows) {
-        *reinterpret_cast<uint2*>(q_row + r * cols + c) = fp8x8_div(v[j], s);
+        *reinterpret_cast<uint2*>(q_row + r * cols + c) = fp8x8_div(v[j], s, block_recip(s));
         if (c16 == 0) s_row[r * (cols / 128) + ct] = s;
       }
     }
@@ -141,11 +166,12 @@ fp8_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int
     }
   }
 
+  const float r_tile = block_recip(s_tile);
   if constexpr (WR) {                    // weight row copy, stored directly
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t r = R0 + rl0 + j;
-      if (col_ok && r < rows) *reinterpret_cast<uint2*>(q_row + r * cols + c) = fp8x8_div(v[j], s_tile);
+      if (col_ok && r < rows) *reinterpret_cast<uint2*>(q_row + r * cols + c) = fp8x8_div(v[j], s_tile, r_tile);
     }
     if (threadIdx.x == 0) s_row[band * col_tiles + ct] = s_tile;
   }
@@ -154,9 +180,9 @@ fp8_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int
     // swizzle as in the MXFP8 quantizer)
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      float s;
-      if constexpr (WC) s = s_tile;
-      else s = s_col[cc];
+      float s, rc;
+      if constexpr (WC) { s = s_tile; rc = r_tile; }
+      else { s = s_col[cc]; rc = block_recip(s); }
       const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
       uint32_t wd[8];
 #pragma unroll
@@ -168,7 +194,7 @@ fp8_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int
                                     __builtin_amdgcn_perm(wd[5], wd[4], sel), __builtin_amdgcn_perm(wd[7], wd[6], sel));
       const int cl = 8 * c16 + cc;
       const int g = (4 * w + m) ^ ((c16 & 3) * 4);
-      *reinterpret_cast<uint2*>(lcol + cl * 128 + g * 8) = fp8x8_div(col8, s);
+      *reinterpret_cast<uint2*>(lcol + cl * 128 + g * 8) = fp8x8_div(col8, s, rc);
     }
     __syncthreads();
     const int t = threadIdx.x;

@@ -71,6 +71,27 @@ def test_act_edge_cases_both_copies_and_strided_input():
     check_act(np.ascontiguousarray(xb[:, :256]), rowwise=True, colwise=True, what="strided", x_dev=wide[:, :256])
 
 
+def test_scales_across_the_reciprocal_threshold_and_negative_zeros():
+    """Block scales from 2^-104 to 2^-80 (the kernel divides below 2^-92 and multiplies
+    by a corrected reciprocal above), each tile mixing its maximum with values a few
+    binades below, exact ties of the E4M3 grid and negative zeros; activation rows,
+    transposed columns and 128 x 128 weight blocks, byte for byte against the oracle."""
+    g = inputs.rng(144, 0)
+    rows, cols = 256, 128 * 25
+    x = g.standard_normal((rows, cols)) * np.exp2(g.integers(-6, 1, (rows, cols)))
+    e = np.repeat(np.arange(-104, -79)[None, :], rows, axis=0).repeat(128, axis=1)   # one exponent per tile column
+    x = x * np.exp2(e + np.log2(448.0))
+    x[:, ::128] = 448.0 * np.exp2(e[:, ::128]) * np.where(g.random((rows, 25)) < 0.5, -1.0, 1.0)
+    xb = bf16(x)
+    xb[::7, 3::17] = 0x8000                                     # -0 inside live tiles
+    check_act(xb, rowwise=True, colwise=True, what="threshold")
+    q, s, qt, st = mxq.quantize_fp8_block_weight(dev_bf16(xb))
+    eq, es, eqt, est = ob.quantize_weight(xb)
+    assert_bytes_equal(host(q), eq, "threshold weight codes")
+    assert_bytes_equal(host(qt), eqt, "threshold weight^T codes")
+    assert_bytes_equal(host(s).view(np.uint32), es.view(np.uint32), "threshold weight scales")
+
+
 @pytest.mark.parametrize("shape", [(128, 128), (384, 256), (1024, 7168)])
 def test_weight_128x128_both_copies(shape):
     g = inputs.rng(143, shape[0] + shape[1])

@@ -213,6 +213,28 @@ def test_grouped_nvfp4_gather_vary_m():
             assert_gemm_close(ch[lo:hi], ref[lo:hi], f"expert {e}")
 
 
+def test_grouped_nvfp4_gather_128x256_tiles():
+    """Row-grouped NVFP4 with K % 256 == 0 runs on 128 x 256 tiles: groups from empty to
+    three row tiles, N = 300 (a ragged second column tile), gathered A rows."""
+    x, r, w = small_moe(T=600, H=512, G=5, k=2, N=300, seed=4)
+    G, N = 5, 300
+    qx, sx, tx = mxq.quantize_nvfp4_per_token(dev_bf16(x))
+    qw, sw, tw = mxq.quantize_nvfp4(dev_bf16(w), scope="group", group_rows=N)
+    c = mxq.grouped_gemm_block_scaled(mxq.NVFP4, dev(r.offsets.astype(np.int64)), qx, qw, N=N, K=x.shape[1], sA=sx,
+                                      sB=sw, tA=tx, tB=tw, tA_scope="row", tB_scope="group",
+                                      a_row_index=dev(r.row_index.astype(np.int32)))
+    xh = onv.dequantize_exact(host(qx), host(sx), host(tx))[r.row_index]
+    wh = onv.dequantize_exact(host(qw), host(sw), np.repeat(host(tw), N)).reshape(G, N, -1)
+    ref = omoe.grouped_gemm_ref(xh, r.offsets, wh)
+    ch = host(c)
+    sizes = np.diff(r.offsets)
+    assert sizes[3] == 0 and sizes.max() > 256
+    for e in range(G):
+        lo, hi = r.offsets[e], r.offsets[e + 1]
+        if hi > lo:
+            assert_gemm_close(ch[lo:hi], ref[lo:hi], f"expert {e}")
+
+
 def test_grouped_nvfp4_dgrad_on_2d_expert_weights():
     """2D-scaled expert weights give an NVFP4 dgrad: per expert dX_g = dGU_g W_g with the
     per-expert transposed copy (G, K, N) as the stacked B operand."""

@@ -299,6 +299,25 @@ def test_grouped_vary_k_wgrad(fmt):
             assert_gemm_close(ch[e], ref, f"{fmt} group {e}")
 
 
+def test_grouped_bf16_vary_k_wide_output():
+    """BF16 weight gradients with outputs of 64+ 256-tiles run on 128 x 256 tiles: per-group
+    K of 40, 0 and 168 (K tails inside a stage), N = 2100 (a ragged column tile)."""
+    g = inputs.rng(91, 0)
+    M, N = 2048, 2100
+    sizes = np.array([40, 0, 168])
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    S = int(off[-1])
+    a = inputs.normal_bf16(g, (M, S), 1.0)
+    b = inputs.normal_bf16(g, (N, S), 1.0)
+    c = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a), dev_bf16(b), N=N, K=0, vary_k=True, M=M))
+    ah, bh = F.bf16_bits_to_f32(a).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64)
+    for e in range(len(sizes)):
+        if sizes[e] == 0:
+            assert np.all(c[e] == 0.0)
+        else:
+            assert_gemm_close(c[e], ah[:, off[e]:off[e + 1]] @ bh[:, off[e]:off[e + 1]].T, f"wide wgrad group {e}")
+
+
 def test_grouped_bf16_vary_m():
     x, r, w = small_moe(seed=2)
     G, N = 8, 192

@@ -461,6 +461,7 @@ def _batch_case(fmt, shapes, seed):
 @pytest.mark.parametrize("fmt,shapes", [
     ("mxfp8", [(2048, 8192, 2048), (2048, 2048, 8192), (8192, 2048, 2048)]),     # the linear layer's three GEMMs
     ("mxfp8", [(300, 200, 96), (64, 1000, 1024), (257, 513, 160), (0, 64, 64)]),  # ragged, K % 64 != 0, empty
+    ("mxfp8", [(2100, 3000, 1024), (1500, 2300, 512), (0, 64, 512), (3000, 700, 512)]),   # 128x256 tiles, ragged
     ("nvfp4", [(300, 200, 256), (256, 512, 2048)]),
     ("mxfp4", [(4196, 3112, 512), (64, 1000, 1024), (32, 32, 32)]),
     ("bf16", [(300, 200, 96), (128, 256, 1024)]),

@@ -1125,12 +1125,13 @@ hipError_t launch_gemm_batch(int fmt, int n, const int64_t* M, const int64_t* N,
   int64_t t256 = 0;
   for (int i = 0; i < n; ++i) t256 += ((M[i] + 255) / 256) * ((N[i] + 255) / 256);
   const int bt = t256 >= 192 ? 256 : 128;
-  // MXFP8 with 16-byte scale chunks (every K % 512 == 0) and enough work: every problem on
-  // 128 x 256 tiles at two workgroups per CU, none alone (the linear layer's three GEMMs:
-  // 6% faster than 256 x 256 tiles plus a separate 128 x 128 dgrad)
+  // MXFP8 with 16-byte scale chunks (every K % 512 == 0) and a few 256-tiles per CU: every
+  // problem on 128 x 256 tiles at two workgroups per CU, none alone (the linear layer's
+  // three GEMMs: 6% faster than 256 x 256 tiles plus a separate 128 x 128 dgrad). Batches of
+  // four or more 256-tiles per CU (three 8192^3 GEMMs) keep the 256 x 256 tiles.
   int sm_all = 2;
   for (int i = 0; i < n; ++i) sm_all = std::min(sm_all, scale_mode(ld, K[i], false));
-  const bool rect = ld == 1 && sm_all == 2 && t256 >= 192;
+  const bool rect = ld == 1 && sm_all == 2 && t256 >= 192 && t256 < 1024;
   bool alone[kMaxBatch];
   int sm = 2, nb = 0;
   for (int i = 0; i < n; ++i) {

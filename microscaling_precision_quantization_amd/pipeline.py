@@ -343,10 +343,12 @@ class SharedExpertBf16:
 
     def backward(self, x, w_sgu, w_sd, d_o, d_gu):
         self.transposes(x, w_sgu, w_sd, d_o, d_gu)
-        B.gemm_block_scaled(B.BF16, d_o, None, self.w_sdT[0], None, out=self.dh)
-        B.gemm_block_scaled(B.BF16, self.d_oT[0], None, self.hT[0], None, out=self.dw_sd)
-        B.gemm_block_scaled(B.BF16, d_gu, None, self.w_sguT[0], None, out=self.dx)
-        B.gemm_block_scaled(B.BF16, self.d_guT[0], None, self.xT[0], None, out=self.dw_sgu)
+        # the four backward GEMMs are independent: one batched launch (longest K first)
+        B.gemm_block_scaled_batch(B.BF16, [
+            dict(A=d_o, sA=None, B=self.w_sdT[0], sB=None, out=self.dh),
+            dict(A=self.d_oT[0], sA=None, B=self.hT[0], sB=None, out=self.dw_sd),
+            dict(A=d_gu, sA=None, B=self.w_sguT[0], sB=None, out=self.dx),
+            dict(A=self.d_guT[0], sA=None, B=self.xT[0], sB=None, out=self.dw_sgu)])
 
     def gemm_flops(self) -> dict:
         T, H, I = self.T, self.H, self.I

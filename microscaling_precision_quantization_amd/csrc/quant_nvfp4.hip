@@ -550,6 +550,10 @@ static void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
     hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 4, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
   else if (ch <= 8)
     hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 8, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
+  else if (ch <= 12)
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 12, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
+  else if (ch <= 14)
+    hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 14, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
   else if (ch <= 16)
     hipLaunchKernelGGL((nvfp4_rows_kernel<MODE, 16, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s, t, seed);
   else

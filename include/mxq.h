@@ -495,8 +495,10 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
  *   ("Miles Blackwell RL", remio.ai, section "Un Cuantizador Compartido ..."), and
  *   per-token NVFP4 on the expert activations (same page, section "La
  *   Compatibilidad ..."). Each slot row (token, expert) is one scale scope.
- *   h = silu(g) * u in binary32 (g = row[0:inter], u = row[inter:2*inter]), rounded
- *   to BF16; then the per-token quantizer above on the BF16 row.
+ *   h = silu(g) * u = g / (1 + exp(-g)) * u in binary32 (g = row[0:inter],
+ *   u = row[inter:2*inter]) with the hardware exponential, rounded to BF16: within one
+ *   BF16 ulp of the exactly computed value; then the per-token quantizer above on the
+ *   BF16 row (bit-exact on that h).
  *
  *   gate_up : FP32 (rows, 2*inter); h_bf16 : optional BF16 (rows, inter) copy of h
  *   (NULL = not written); q (rows, inter/2), s (rows, inter/16), t (rows).

@@ -180,7 +180,16 @@ hipError_t launch_dequant_t(int fmt, const void* q, const void* s, const float* 
 // h = silu(g) * u = g / (1 + exp(-g)) * u in binary32, rounded to BF16, then the
 // per-token quantizer's arithmetic on the BF16 row.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float swiglu1(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// g >= -80: exp(-g) through the hardware base-2 exponential (relative error ~|g| 2^-24,
+// far below the BF16 rounding of h; for large g it underflows to 0, which leaves h = g u
+// as the exact value rounds), the division correctly rounded.
+// g < -80: exp(-g) nears the binary32 overflow (at g = -88.7) and exp(g) would lose its
+// precision as a denormal, so h = g e^g u (1 + e^g rounds to 1) is formed as
+// -sign(u) exp(g + ln|g| + ln|u|) with the accurate functions.
+__device__ __forceinline__ float swiglu1(float g, float u) {
+  if (g >= -80.0f) return g / (1.0f + __expf(-g)) * u;
+  return copysignf(expf(g + logf(-g) + logf(fabsf(u))), -u);
+}
 
 template <int CH>
 __global__ void __launch_bounds__(256)

@@ -346,6 +346,19 @@ def test_grouped_bf16_vary_m_large_groups():
 
 # --------------------------------- MoE glue ---------------------------------
 
+def test_swiglu_extreme_gates():
+    """Gates across the exponential's overflow and underflow points (|g| up to 120) and
+    signed zeros: h stays within one BF16 ulp of the FP64 SwiGLU."""
+    g = inputs.rng(87, 1)
+    rows, inter = 64, 512
+    gate = np.concatenate([np.linspace(-120, 120, 241), [0.0, -0.0, 1e-30, -1e-30, 87.3, -87.3, 88.8, -88.8, 89.5, -89.5]])
+    gate = np.resize(gate, rows * inter).reshape(rows, inter)
+    up = g.standard_normal((rows, inter)) * np.exp2(g.integers(-20, 20, (rows, 1)))
+    gu = np.concatenate([gate, up], axis=1).astype(np.float32)
+    h, q, s, t = mxq.moe_swiglu_quantize_nvfp4(dev(gu))
+    assert np.max(omoe.bf16_ulp_distance(host(h), omoe.swiglu_bf16_ref(gu))) <= 1
+
+
 def test_swiglu_requant_and_combine():
     g = inputs.rng(87, 0)
     rows, inter = 300, 768

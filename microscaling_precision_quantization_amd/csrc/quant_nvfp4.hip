@@ -605,6 +605,44 @@ hipError_t launch_quant_nvfp4_token(const void* x, int64_t tokens, int64_t hidde
 // General entry: scope 0 = ROW, 1 = TENSOR, 2 = GROUP. RHT signs are passed as
 // a 16-bit mask (bit i set <=> sign i is -1); rht = 0 disables the transform.
 // SR = stochastic rounding of the elements with the given seed.
+// Scope maxima of |x| when every scope is one contiguous span of `span` elements (rows
+// stored back to back): the first pass of the per-tensor / per-group quantizer as a flat
+// streaming reduction. Workgroup b reduces part b % per_scope of scope b / per_scope,
+// eight 16-byte loads in flight per lane, and folds its maximum into scope_amax with
+// one atomic (BF16 magnitudes compare as their bit patterns).
+__global__ void __launch_bounds__(256)
+scope_amax_flat_kernel(const uint16_t* __restrict__ x, int64_t span, int per_scope, uint32_t* __restrict__ scope_amax) {
+  const int64_t g = blockIdx.x / per_scope;
+  const int64_t part = blockIdx.x % per_scope;
+  const int64_t units = span / 8;                                    // 16-byte units (span % 8 == 0)
+  const int64_t u0 = units * part / per_scope, u1 = units * (part + 1) / per_scope;
+  const uint16_t* base = x + g * span;
+  uint32_t m = 0;
+  int64_t u = u0 + threadIdx.x;
+  for (; u + 7 * 256 < u1; u += 8 * 256) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = load_stream16(base + (u + k * 256) * 8);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      m = pk_max_u16(m, pk_max_u16(pk_max_u16(v[k].x & 0x7FFF7FFFu, v[k].y & 0x7FFF7FFFu),
+                                   pk_max_u16(v[k].z & 0x7FFF7FFFu, v[k].w & 0x7FFF7FFFu)));
+  }
+  for (; u < u1; u += 256) {
+    const uint4 v = load_stream16(base + u * 8);
+    m = pk_max_u16(m, pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                                 pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu)));
+  }
+  const float a = wave_max_f32(__uint_as_float(max_halves(m) << 16));
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = __float_as_uint(a);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t mm = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (mm) atomicMax(scope_amax + g, mm);
+  }
+}
+
 template <bool SR>
 static hipError_t quant_nvfp4_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int scope,
                                    int64_t group_rows, int transpose, int rht, uint32_t neg_mask, uint8_t* qp,
@@ -622,7 +660,16 @@ static hipError_t quant_nvfp4_impl(const uint16_t* x, int64_t rows, int64_t cols
       launch_rows<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st);
       launch_rows<1, true, SR>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st, seed);
     } else {
-      launch_rows<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
+      if (ld_x == cols) {                       // contiguous scopes: flat streaming amax
+        const int64_t span = gr * cols, units = span / 8;
+        const int64_t want = (2048 + n_scopes - 1) / n_scopes;         // ~2048 workgroups in all
+        const int64_t cap = units / 2048 > 0 ? units / 2048 : 1;      // >= 2048 units each
+        const int per_scope = (int)(want < cap ? want : cap);
+        hipLaunchKernelGGL(scope_amax_flat_kernel, dim3((unsigned)(n_scopes * per_scope)), dim3(256), 0, st, x, span,
+                           per_scope, ws_amax);
+      } else {
+        launch_rows<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
+      }
       launch_rows<1, false, SR>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st, seed);
     }
   } else {

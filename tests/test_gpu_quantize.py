@@ -195,6 +195,26 @@ def test_nvfp4_per_token_deepseek_activations_sampled():
     assert_bytes_equal(t[rows].view(np.uint32), et.view(np.uint32), "sampled token scales")
 
 
+def test_nvfp4_group_amax_at_group_edges():
+    """Contiguous groups large enough that each group's maximum is reduced in 64 parts:
+    every group's maximum sits on its last element, next to a larger first element of
+    the following group; all-zero group included. Bytes and t against the oracle."""
+    g = inputs.rng(95, 1)
+    G, N, K = 5, 256, 4096
+    x = g.standard_normal((G * N, K)) * 0.02
+    for e in range(G):
+        x[e * N + N - 1, K - 1] = 3.0 * (e + 1)          # group maximum, last element
+        if e + 1 < G:
+            x[(e + 1) * N, 0] = -50.0 * (e + 2)          # the next group's first element, larger
+    x[2 * N:3 * N] = 0.0
+    wb = inputs.to_bf16_bits(x)
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(wb), scope="group", group_rows=N)
+    eq, es, et = onv.quantize_per_group(wb, np.arange(G + 1) * N)
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "group t")
+    assert_bytes_equal(host(q), eq, "group packed")
+    assert_bytes_equal(host(s), es, "group scales")
+
+
 def test_nvfp4_per_tensor_and_group_weights():
     g = inputs.rng(95, 0)
     G, N, K = 5, 96, 256

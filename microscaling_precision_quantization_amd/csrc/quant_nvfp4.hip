@@ -574,37 +574,6 @@ static void launch_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
 
 
 // 2D weights: scope amax pass (rows kernel, MODE 2), then the 16x16-block pass.
-hipError_t launch_quant_nvfp4_2d(const void* xv, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
-                                 void* q_row, void* s_row, void* q_colT, void* s_colT, float* t, uint32_t* ws_amax,
-                                 int64_t n_scopes, hipStream_t st) {
-  const uint16_t* x = (const uint16_t*)xv;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, 0u, n_scopes);
-  launch_rows<2, false>(x, rows, cols, ld_x, group_rows, 0u, ws_amax, nullptr, nullptr, nullptr, st);
-  const int64_t col_tiles = (cols + 127) / 128;
-  const int64_t bands = (rows + 255) / 256;
-  uint8_t *qr = (uint8_t*)q_row, *sr = (uint8_t*)s_row, *qc = (uint8_t*)q_colT, *sc = (uint8_t*)s_colT;
-  const int wide = qc && group_rows % 32 == 0 && ((uintptr_t)qc & 15) == 0 && ((uintptr_t)sc & 15) == 0;
-  const int dw_row = sr && (cols / 16) % 8 == 0 && ((uintptr_t)sr & 7) == 0;
-  dim3 grid((unsigned)(bands * col_tiles)), block(256);
-  if (qr && qc)
-    hipLaunchKernelGGL((nvfp4_2d_kernel<true, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
-  else if (qr)
-    hipLaunchKernelGGL((nvfp4_2d_kernel<true, false>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
-  else
-    hipLaunchKernelGGL((nvfp4_2d_kernel<false, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
-  hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_nvfp4_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x,
-                                    void* q, void* s, float* t, hipStream_t st) {
-  launch_rows<0, false>((const uint16_t*)x, tokens, hidden, ld_x, 1, 0u, nullptr, (uint8_t*)q, (uint8_t*)s, t, st);
-  return hipGetLastError();
-}
-
-// General entry: scope 0 = ROW, 1 = TENSOR, 2 = GROUP. RHT signs are passed as
-// a 16-bit mask (bit i set <=> sign i is -1); rht = 0 disables the transform.
-// SR = stochastic rounding of the elements with the given seed.
 // Scope maxima of |x| when every scope is one contiguous span of `span` elements (rows
 // stored back to back): the first pass of the per-tensor / per-group quantizer as a flat
 // streaming reduction. Workgroup b reduces part b % per_scope of scope b / per_scope,
@@ -643,6 +612,53 @@ scope_amax_flat_kernel(const uint16_t* __restrict__ x, int64_t span, int per_sco
   }
 }
 
+// First pass of a scope-scaled quantizer (no transform): scope maxima of |x| over row
+// groups of gr rows, flat when the rows are stored back to back.
+static void launch_scope_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t gr,
+                              int64_t n_scopes, uint32_t* ws_amax, hipStream_t st) {
+  if (ld_x == cols) {
+    const int64_t span = gr * cols, units = span / 8;
+    const int64_t want = (2048 + n_scopes - 1) / n_scopes;           // ~2048 workgroups in all
+    const int64_t cap = units / 2048 > 0 ? units / 2048 : 1;        // >= 2048 units each
+    const int per_scope = (int)(want < cap ? want : cap);
+    hipLaunchKernelGGL(scope_amax_flat_kernel, dim3((unsigned)(n_scopes * per_scope)), dim3(256), 0, st, x, span,
+                       per_scope, ws_amax);
+  } else {
+    launch_rows<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, nullptr, nullptr, nullptr, st);
+  }
+}
+
+hipError_t launch_quant_nvfp4_2d(const void* xv, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
+                                 void* q_row, void* s_row, void* q_colT, void* s_colT, float* t, uint32_t* ws_amax,
+                                 int64_t n_scopes, hipStream_t st) {
+  const uint16_t* x = (const uint16_t*)xv;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, 0u, n_scopes);
+  launch_scope_amax(x, rows, cols, ld_x, group_rows, n_scopes, ws_amax, st);
+  const int64_t col_tiles = (cols + 127) / 128;
+  const int64_t bands = (rows + 255) / 256;
+  uint8_t *qr = (uint8_t*)q_row, *sr = (uint8_t*)s_row, *qc = (uint8_t*)q_colT, *sc = (uint8_t*)s_colT;
+  const int wide = qc && group_rows % 32 == 0 && ((uintptr_t)qc & 15) == 0 && ((uintptr_t)sc & 15) == 0;
+  const int dw_row = sr && (cols / 16) % 8 == 0 && ((uintptr_t)sr & 7) == 0;
+  dim3 grid((unsigned)(bands * col_tiles)), block(256);
+  if (qr && qc)
+    hipLaunchKernelGGL((nvfp4_2d_kernel<true, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+  else if (qr)
+    hipLaunchKernelGGL((nvfp4_2d_kernel<true, false>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+  else
+    hipLaunchKernelGGL((nvfp4_2d_kernel<false, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+  hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                    void* q, void* s, float* t, hipStream_t st) {
+  launch_rows<0, false>((const uint16_t*)x, tokens, hidden, ld_x, 1, 0u, nullptr, (uint8_t*)q, (uint8_t*)s, t, st);
+  return hipGetLastError();
+}
+
+// General entry: scope 0 = ROW, 1 = TENSOR, 2 = GROUP. RHT signs are passed as
+// a 16-bit mask (bit i set <=> sign i is -1); rht = 0 disables the transform.
+// SR = stochastic rounding of the elements with the given seed.
 template <bool SR>
 static hipError_t quant_nvfp4_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int scope,
                                    int64_t group_rows, int transpose, int rht, uint32_t neg_mask, uint8_t* qp,
@@ -660,16 +676,7 @@ static hipError_t quant_nvfp4_impl(const uint16_t* x, int64_t rows, int64_t cols
       launch_rows<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st);
       launch_rows<1, true, SR>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st, seed);
     } else {
-      if (ld_x == cols) {                       // contiguous scopes: flat streaming amax
-        const int64_t span = gr * cols, units = span / 8;
-        const int64_t want = (2048 + n_scopes - 1) / n_scopes;         // ~2048 workgroups in all
-        const int64_t cap = units / 2048 > 0 ? units / 2048 : 1;      // >= 2048 units each
-        const int per_scope = (int)(want < cap ? want : cap);
-        hipLaunchKernelGGL(scope_amax_flat_kernel, dim3((unsigned)(n_scopes * per_scope)), dim3(256), 0, st, x, span,
-                           per_scope, ws_amax);
-      } else {
-        launch_rows<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st);
-      }
+      launch_scope_amax(x, rows, cols, ld_x, gr, n_scopes, ws_amax, st);
       launch_rows<1, false, SR>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st, seed);
     }
   } else {

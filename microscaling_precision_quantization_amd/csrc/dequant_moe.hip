@@ -163,12 +163,88 @@ dequant_t_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, c
   }
 }
 
+// NVFP4 without a row gather: 128 output columns (input rows, in pairs) x 128 input
+// columns per workgroup, so each input row of the tile is one 64-byte segment and each
+// output row one 256-byte segment. Lane (row pair jp, 16-byte unit ul) dequantizes 32
+// elements of two rows; the pairs go to LDS as dwords (row 2jp low, 2jp+1 high) at
+// 4-dword chunk (jp / 4) ^ sw(c), sw(c) = 2 (c / 32) mod 16, which keeps a wave's pair
+// writes on distinct banks. (Measured against the 64 x 64 kernel above: C4 gate_up
+// weights 5.04 -> 4.83 ms, activations 0.23 -> 0.17 ms; slower with a gather and for the
+// other formats, which keep the kernel above.)
+__global__ void __launch_bounds__(256)
+dequant_t_nv_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, const float* __restrict__ t,
+                    int t_mode, int64_t group_rows, int64_t cols, int64_t out_cols, uint16_t* __restrict__ out,
+                    int64_t ld_out) {
+  constexpr int EPU = 32, UPR = 4, TC = UPR * EPU;        // 128 input columns
+  __shared__ __attribute__((aligned(16))) uint32_t tile[TC * 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t g = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.y * TC, j0 = (int64_t)blockIdx.x * 128;
+  const int rr = lane / UPR, ul = lane % UPR;
+  const int jp = w * 16 + rr;                              // 0..63
+  const int64_t c = c0 + (int64_t)ul * EPU;
+  uint32_t lo[16], hi[16];                                 // BF16 pairs of rows 2jp / 2jp+1
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int64_t j = j0 + 2 * jp + half;
+    uint32_t p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = 0;
+    if (j < out_cols && j < group_rows && c < cols) {
+      const int64_t r = g * group_rows + j;
+      const float tt = t_mode == 0 ? t[r] : t_mode == 1 ? t[0] : t[r / group_rows];
+      const bool full = c + 32 <= cols;                    // else only the first 16 columns exist
+      uint4 b;
+      if (full) b = load_stream16(q + r * (cols / 2) + c / 2);
+      else { const uint2 b2 = *reinterpret_cast<const uint2*>(q + r * (cols / 2) + c / 2); b = make_uint4(b2.x, b2.y, 0, 0); }
+      const float S0 = e4m3_to_f32(s[r * (cols / 16) + c / 16]);
+      const float S1 = full ? e4m3_to_f32(s[r * (cols / 16) + c / 16 + 1]) : 0.0f;
+      const uint32_t wd[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {                        // (q * S) exact, then * t
+        const float S = k < 2 ? S0 : S1;
+        const v2f_t e0 = e2m1x2_to_f32<0>(wd[k]), e1 = e2m1x2_to_f32<1>(wd[k]);
+        const v2f_t e2 = e2m1x2_to_f32<2>(wd[k]), e3 = e2m1x2_to_f32<3>(wd[k]);
+        p[4 * k + 0] = bf16x2_rne((e0.x * S) * tt, (e0.y * S) * tt);
+        p[4 * k + 1] = bf16x2_rne((e1.x * S) * tt, (e1.y * S) * tt);
+        p[4 * k + 2] = bf16x2_rne((e2.x * S) * tt, (e2.y * S) * tt);
+        p[4 * k + 3] = bf16x2_rne((e3.x * S) * tt, (e3.y * S) * tt);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) (half ? hi : lo)[i] = p[i];
+  }
+  const int sw = (2 * ul) & 15;
+  const int pos = (((jp >> 2) ^ sw) << 2) | (jp & 3);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    tile[(ul * EPU + 2 * i) * 64 + pos] = (lo[i] & 0xFFFFu) | (hi[i] << 16);
+    tile[(ul * EPU + 2 * i + 1) * 64 + pos] = (lo[i] >> 16) | (hi[i] & 0xFFFF0000u);
+  }
+  __syncthreads();
+  // output row c of the tile: 128 BF16 = 16 chunks of 16 bytes, one per lane
+#pragma unroll
+  for (int k = 0; k < TC * 16 / 256; ++k) {
+    const int i = k * 256 + tid;
+    const int cl = i >> 4, qq = i & 15;
+    const int64_t cc = c0 + cl, j = j0 + 8 * qq;
+    const int swc = (2 * (cl / EPU)) & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + cl * 64 + ((qq ^ swc) << 2));
+    if (cc < cols && j < out_cols) *reinterpret_cast<uint4*>(out + (g * cols + cc) * ld_out + j) = v;
+  }
+}
+
 hipError_t launch_dequant_t(int fmt, const void* q, const void* s, const float* t, int t_mode, int64_t groups,
                             int64_t group_rows, int64_t cols, const int32_t* src_row, int64_t out_cols, void* out,
                             int64_t ld_out, hipStream_t st) {
-  dim3 grid((unsigned)((out_cols + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)groups), block(256);
   const uint8_t *qp = (const uint8_t*)q, *sp = (const uint8_t*)s;
   uint16_t* o = (uint16_t*)out;
+  if (fmt == 2 && !src_row) {
+    dim3 g2((unsigned)((out_cols + 127) / 128), (unsigned)((cols + 127) / 128), (unsigned)groups), b2(256);
+    hipLaunchKernelGGL(dequant_t_nv_kernel, g2, b2, 0, st, qp, sp, t, t_mode, group_rows, cols, out_cols, o, ld_out);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)((out_cols + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)groups), block(256);
   if (fmt == 1) hipLaunchKernelGGL((dequant_t_kernel<1>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, cols, src_row, out_cols, o, ld_out);
   else if (fmt == 2) hipLaunchKernelGGL((dequant_t_kernel<2>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, cols, src_row, out_cols, o, ld_out);
   else hipLaunchKernelGGL((dequant_t_kernel<3>), grid, block, 0, st, qp, sp, t, t_mode, group_rows, cols, src_row, out_cols, o, ld_out);

@@ -29,6 +29,26 @@ def test_dequantize_transposed_nvfp4_groups():
     assert_bytes_equal(out, np.ascontiguousarray(ref), "nvfp4 per-expert transpose")
 
 
+@pytest.mark.parametrize("scope", ["row", "tensor", "group"])
+def test_dequantize_transposed_nvfp4_ragged_tiles(scope):
+    """Without a gather: columns % 32 == 16 (a half 32-element unit at the tile edge),
+    200 output columns per group (a ragged second 128-column tile), two groups."""
+    G, N, K = 2, 200, 176
+    xb = inputs.to_bf16_bits(inputs.rng(120, 5).standard_normal((G * N, K)) * np.exp2(inputs.rng(120, 6).integers(-6, 6, (G * N, 1))))
+    if scope == "row":
+        q, s, t = mxq.quantize_nvfp4_per_token(dev_bf16(xb))
+        t_rows = host(t)
+    elif scope == "tensor":
+        q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="tensor")
+        t_rows = np.repeat(host(t), G * N)
+    else:
+        q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="group", group_rows=N)
+        t_rows = np.repeat(host(t), N)
+    out = host(mxq.binding.dequantize_transposed(mxq.NVFP4, q, s, t, t_scope=scope, groups=G, group_rows=N))
+    ref = onv.dequantize_bf16_bits(host(q), host(s), t_rows).reshape(G, N, K).transpose(0, 2, 1)
+    assert_bytes_equal(out, np.ascontiguousarray(ref), f"nvfp4 transpose, {scope} scale")
+
+
 def test_dequantize_transposed_gather_and_padding():
     T, H = 77, 272
     xb = inputs.to_bf16_bits(inputs.rng(120, 1).standard_normal((T, H)) * 3)

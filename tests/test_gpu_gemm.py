@@ -330,10 +330,10 @@ def test_grouped_bf16_vary_m():
 
 
 def test_grouped_bf16_vary_m_large_groups():
-    """Groups averaging >= 384 rows run on 256 x 256 tiles: ragged group sizes (one
-    empty, one past two tiles), N not a multiple of the tile."""
+    """Groups averaging >= 384 rows (here 430) run on 256 x 256 tiles: ragged group sizes
+    (one empty, one of four row tiles with a 132-row tail), N not a multiple of the tile."""
     g = inputs.rng(90, 0)
-    sizes = np.array([520, 0, 300, 700])
+    sizes = np.array([520, 0, 300, 900])
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     S, G, N, K = int(off[-1]), len(sizes), 300, 192
     a = inputs.normal_bf16(g, (S, K), 1.0)

@@ -821,10 +821,16 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // Whole rounds of R stages: stages past the end multiply zeros (their loads are
   // out of range), which adds nothing to the accumulators.
   const int rounds = (nk + R - 1) / R;
+  // BF16 tiles sharing a CU: the workgroup in its main loop issues ahead of one in its
+  // prologue or FP32 epilogue (DeepSeek expert wgrads 5% faster; no gain measured for the
+  // NVFP4 and MXFP8 kernels, which keep equal priorities)
+  constexpr bool PRIO = OCC > 1 && LD == 0;
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
   for (int r = 0; r < rounds; ++r) {
     const int kt = r * R;
     static_for<0, R>([&](auto RI) { stage(kt + RI.value, RI); });
   }
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   wait_vmcnt<0>();                    // no direct load may still target this workgroup's LDS
   exact_drain();
 

@@ -195,6 +195,31 @@ def test_nvfp4_per_token_deepseek_activations_sampled():
     assert_bytes_equal(t[rows].view(np.uint32), et.view(np.uint32), "sampled token scales")
 
 
+def test_nvfp4_strided_input_all_scopes():
+    """A row stride above the column count (rows not stored back to back): the scope
+    maxima take the per-row pass instead of the flat reduction; bytes against the oracle
+    on the contiguous copy for token, tensor and group scopes."""
+    g = inputs.rng(95, 2)
+    G, N, K = 3, 64, 512
+    xb = inputs.to_bf16_bits(g.standard_normal((G * N, K + 96)) * np.exp2(g.integers(-8, 8, (G * N, 1))))
+    wide = dev_bf16(xb)
+    sub = wide[:, :K]                                           # ld_x = K + 96
+    x = np.ascontiguousarray(xb[:, :K])
+    q, s, t = mxq.quantize_nvfp4_per_token(sub)
+    eq, es, et = onv.quantize_per_token(x)
+    assert_bytes_equal(host(q), eq, "strided token packed")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "strided token t")
+    q, s, t = mxq.quantize_nvfp4(sub, scope="tensor")
+    eq, es, et = onv.quantize_per_tensor(x)
+    assert_bytes_equal(host(q), eq, "strided tensor packed")
+    assert_bytes_equal(host(s), es, "strided tensor scales")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "strided tensor t")
+    q, s, t = mxq.quantize_nvfp4(sub, scope="group", group_rows=N)
+    eq, es, et = onv.quantize_per_group(x, np.arange(G + 1) * N)
+    assert_bytes_equal(host(q), eq, "strided group packed")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "strided group t")
+
+
 def test_nvfp4_group_amax_at_group_edges():
     """Contiguous groups large enough that each group's maximum is reduced in 64 parts:
     every group's maximum sits on its last element, next to a larger first element of

@@ -62,6 +62,7 @@
 namespace mxq {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 namespace gx {
@@ -871,7 +872,8 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         const float4 v = *reinterpret_cast<const float4*>(stg + rl * P + ch * 4);
         float* dstp = p.C + row * p.ldc + col;
         if (vec_ok && col + 4 <= p.n_valid) {
-          *reinterpret_cast<float4*>(dstp) = v;
+          const f32x4_nt vv = {v.x, v.y, v.z, v.w};
+          __builtin_nontemporal_store(vv, reinterpret_cast<f32x4_nt*>(dstp));
         } else {
           if (col < p.n_valid) dstp[0] = v.x;
           if (col + 1 < p.n_valid) dstp[1] = v.y;
@@ -891,7 +893,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
-          if (col < p.n_valid) p.C[row * p.ldc + col] = acc[i][j][r];
+          if (col < p.n_valid) __builtin_nontemporal_store(acc[i][j][r], p.C + row * p.ldc + col);
         }
       }
   }

@@ -15,6 +15,8 @@
 
 namespace mxq {
 
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // Dequantize: one thread per 16 consecutive elements of a row.
 // FMT: 1 MXFP8, 2 NVFP4, 4 MXFP4.
@@ -159,7 +161,12 @@ dequant_t_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, c
     const int cl = i >> 3, jc = (i & 7) * 8;
     const int64_t c = c0 + cl, j = j0 + jc;
     if (c < cols && j < out_cols)
-      *reinterpret_cast<uint4*>(out + (g * cols + c) * ld_out + j) = *reinterpret_cast<const uint4*>(tile + cl * P + jc);
+      {
+        // non-temporal: the output is not read here, the (gathered) input rows stay in L2
+        const uint4 vv = *reinterpret_cast<const uint4*>(tile + cl * P + jc);
+        const u32x4_nt v4 = {vv.x, vv.y, vv.z, vv.w};
+        __builtin_nontemporal_store(v4, reinterpret_cast<u32x4_nt*>(out + (g * cols + c) * ld_out + j));
+      }
   }
 }
 
@@ -230,7 +237,10 @@ dequant_t_nv_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s
     const int64_t cc = c0 + cl, j = j0 + 8 * qq;
     const int swc = (2 * (cl / EPU)) & 15;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + cl * 64 + ((qq ^ swc) << 2));
-    if (cc < cols && j < out_cols) *reinterpret_cast<uint4*>(out + (g * cols + cc) * ld_out + j) = v;
+    if (cc < cols && j < out_cols) {
+      const u32x4_nt v4 = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(v4, reinterpret_cast<u32x4_nt*>(out + (g * cols + cc) * ld_out + j));
+    }
   }
 }
 
@@ -289,7 +299,10 @@ swiglu_nvfp4_kernel(const float* __restrict__ gu, int64_t rows, int64_t inter, u
       p[1] = f32_to_bf16_rne(swiglu1(g0.z, u0.z)) | (f32_to_bf16_rne(swiglu1(g0.w, u0.w)) << 16);
       p[2] = f32_to_bf16_rne(swiglu1(g1.x, u1.x)) | (f32_to_bf16_rne(swiglu1(g1.y, u1.y)) << 16);
       p[3] = f32_to_bf16_rne(swiglu1(g1.z, u1.z)) | (f32_to_bf16_rne(swiglu1(g1.w, u1.w)) << 16);
-      if (h_out) *reinterpret_cast<uint4*>(h_out + row * inter + e) = make_uint4(p[0], p[1], p[2], p[3]);
+      if (h_out) {                                               // outputs leave with non-temporal stores
+        const u32x4_nt h4 = {p[0], p[1], p[2], p[3]};
+        __builtin_nontemporal_store(h4, reinterpret_cast<u32x4_nt*>(h_out + row * inter + e));
+      }
     }
     hb[i] = make_uint4(p[0], p[1], p[2], p[3]);
     amax_bits = pk_max_u16(amax_bits, pk_max_u16(pk_max_u16(p[0] & 0x7FFF7FFFu, p[1] & 0x7FFF7FFFu),
@@ -328,7 +341,7 @@ swiglu_nvfp4_kernel(const float* __restrict__ gu, int64_t rows, int64_t inter, u
     o = cvt_fp4x2_f32<2>(o, f[4] * r, f[5] * r);
     o = cvt_fp4x2_f32<3>(o, f[6] * r, f[7] * r);
     if (e < inter) {
-      *reinterpret_cast<uint32_t*>(q + row * (inter / 2) + e / 2) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<uint32_t*>(q + row * (inter / 2) + e / 2));
       if (!odd) s[row * (inter / 16) + e / 16] = (uint8_t)code;
     }
   }
@@ -363,7 +376,8 @@ combine_kernel(const float* __restrict__ o, int64_t total_slots, int64_t topk, i
       const float4 v = load_stream16f(o + slot * hidden + c);
       acc.x += wj * v.x; acc.y += wj * v.y; acc.z += wj * v.z; acc.w += wj * v.w;
     }
-    *reinterpret_cast<float4*>(y + tok * hidden + c) = acc;
+    const f32x4_nt a4 = {acc.x, acc.y, acc.z, acc.w};           // output not read here: keep it out of L2
+    __builtin_nontemporal_store(a4, reinterpret_cast<f32x4_nt*>(y + tok * hidden + c));
   }
 }
 

@@ -235,7 +235,9 @@ nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
       packed = pack8_e2m1(f, r);
     }
     if (e < cols) {
-      *reinterpret_cast<uint32_t*>(q + row * (cols / 2) + e / 2) = packed;
+      // tensor / group scopes (weights, read again only by a later GEMM): non-temporal
+      if (MODE == 1) __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(q + row * (cols / 2) + e / 2));
+      else *reinterpret_cast<uint32_t*>(q + row * (cols / 2) + e / 2) = packed;
       if (!odd) s[row * (cols / 16) + e / 16] = (uint8_t)code;
     }
   }
@@ -448,7 +450,7 @@ nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int6
       float f[8];
       unpack8(v[j], f);
       const uint32_t packed = pack8_e2m1(f, r);
-      if (ok) *reinterpret_cast<uint32_t*>(q_row + (r0 + j) * (cols / 2) + c / 2) = packed;
+      if (ok) __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(q_row + (r0 + j) * (cols / 2) + c / 2));
     }
     if ((c16 & 1) == 0)
 #pragma unroll
@@ -498,7 +500,7 @@ nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int6
       const int64_t gi = rr / group_rows, rl = rr - gi * group_rows;
       uint8_t* dst = q_colT + (gi * cols + col) * rb + rl / 2;
       if (wide_col) {                                 // group_rows % 32 == 0: whole aligned chunks
-        *reinterpret_cast<uint4*>(dst) = d;
+        { const u32x4_nt d4 = {d.x, d.y, d.z, d.w}; __builtin_nontemporal_store(d4, reinterpret_cast<u32x4_nt*>(dst)); }
       } else {                                        // 16-row granules, each inside one group
         *reinterpret_cast<uint2*>(dst) = make_uint2(d.x, d.y);
         const int64_t r2 = rr + 16;

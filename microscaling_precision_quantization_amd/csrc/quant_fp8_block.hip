@@ -25,13 +25,16 @@
 // The quotients are IEEE binary32 x / s, correctly rounded; |x / s| is clamped to 448
 // before the E4M3 convert, which equals saturation (the convert itself does not
 // saturate). Each block computes r = 1 / s once (correctly rounded division) and each
-// element takes Markstein's correction of y = x r: q = fma(fma(-y, s, |x|), r, y) with
-// y = |x| r, and the sign of x. An exhaustive check on MI355X over every binary32
-// significand of s and every BF16 significand of x (both signs; 2^31 cases) found q
-// equal to the correctly rounded quotient in all of them; scaling both by powers of
-// two keeps that while r, y and the residual stay normal, which holds whenever
-// s >= 2^-92 for every element whose E4M3 code is not zero (|x / s| >= 2^-10). Blocks
-// with a smaller s keep the division.
+// element takes Markstein's correction of y = x r: q = fma(-e, r, y) with the residual
+// e = fma(y, s, -x). An exhaustive check on MI355X over every binary32 significand of s
+// and every BF16 significand of x (both signs; 2^31 cases) found q equal to the
+// correctly rounded quotient in all of them; scaling both by powers of two keeps that
+// while r, y and the residual stay normal, which holds whenever s >= 2^-92 for every
+// element whose E4M3 code is not zero (|x / s| >= 2^-10). Negating x negates y, e and q
+// exactly, and the residual's order of operands keeps the sign of a zero x (x = -0
+// gives e = +0, q = -0 + -0 = -0). Blocks with a smaller s keep the division. With
+// s >= 2^-92 the scale is normal and |x / s| <= 448 (1 + 2^-23), which the convert
+// rounds to 448: only the division path needs the clamp.
 #include "common.h"
 
 namespace mxq {
@@ -42,9 +45,8 @@ __device__ __forceinline__ float block_recip(float s) { return s >= 0x1p-92f ? 1
 
 // x / s, correctly rounded, through the reciprocal r of the block (see the file comment)
 __device__ __forceinline__ float quot_r(float x, float s, float r) {
-  const float ax = fabsf(x);
-  const float y = ax * r;
-  return copysignf(__builtin_fmaf(__builtin_fmaf(-y, s, ax), r, y), x);
+  const float y = x * r;
+  return __builtin_fmaf(-__builtin_fmaf(y, s, -x), r, y);
 }
 
 // Eight BF16 values (one uint4) / s -> eight E4M3 bytes (element 0 in the low byte).
@@ -53,17 +55,21 @@ __device__ __forceinline__ uint2 fp8x8_div(const uint4& v, float s, float r) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
-  if (r != 0.0f) {
+  uint32_t o[2] = {0u, 0u};
+  if (r != 0.0f) {                       // |q| <= 448 (1 + 2^-23): converts to at most 448
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = quot_r(f[i], s, r);
-  } else if (s > 0.0f) {                 // tiny block scale: divide
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i / 2] = cvt_fp8x2_f32(o[i / 2], f[2 * i], f[2 * i + 1], 1.0f, (i & 1) != 0);
+    return make_uint2(o[0], o[1]);
+  }
+  if (s > 0.0f) {                        // tiny block scale: divide
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = f[i] / s;
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] *= 0.0f;     // all-zero block: keep the sign of zero
   }
-  uint32_t o[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float a = fminf(fmaxf(f[2 * i], -kE4M3Max), kE4M3Max);

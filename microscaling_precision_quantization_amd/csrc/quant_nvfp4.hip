@@ -281,10 +281,14 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
     v[j] = ok ? (MODE == 2 ? *reinterpret_cast<const uint4*>(x + (r0 + j) * ld_x + c) : load_stream16(x + (r0 + j) * ld_x + c))
               : make_uint4(0, 0, 0, 0);
 
-  float sg[16];
   if (RHT) {
+    // random signs: row j of every block is negated when bit j is set; a dword holds two
+    // columns of one row, so one XOR of both sign bits flips them exactly
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sg[i] = ((neg_mask >> i) & 1u) ? -1.0f : 1.0f;
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t f = ((neg_mask >> j) & 1u) ? 0x80008000u : 0u;
+      v[j].x ^= f; v[j].y ^= f; v[j].z ^= f; v[j].w ^= f;
+    }
   }
   float mloc = 0.0f;                                 // MODE 2: max over the lane's 8 columns
   float s_enc = 1.0f;
@@ -302,8 +306,6 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
     }
     if (RHT) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] *= sg[i];
-#pragma unroll
       for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -313,8 +315,12 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
           f[i + h] = a - b;
         }
       }
+      // the amax pass takes the maximum of the unnormalized sums and scales it once
+      // below: rounding is monotonic, so RN(max |f| / 4) = max RN(|f| / 4)
+      if (MODE != 2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] *= 0.25f;
+        for (int i = 0; i < 16; ++i) f[i] *= 0.25f;
+      }
     }
     float a = 0.0f;
 #pragma unroll
@@ -344,6 +350,7 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
   }
 
   if (MODE == 2) {
+    if (RHT) mloc *= 0.25f;
     // The lane's 8 columns share a scope (group_rows % 8 == 0). Reduce over the
     // workgroup when its whole column tile lies in one scope.
     const int64_t tile_c1 = min(C0 + 128, cols) - 1;

@@ -212,7 +212,10 @@ nvfp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
   }
   float s_enc, t;
   scope_scales(A, s_enc, t);
-  if (MODE == 0 && lane == 0) t_out[row] = t;
+  if (lane == 0) {                     // decode scale: per row, or per scope from its first row
+    if (MODE == 0) t_out[row] = t;
+    else if (row % group_rows == 0) t_out[row / group_rows] = t;
+  }
 
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -261,8 +264,8 @@ __global__ void __launch_bounds__(256)
 nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
                   int64_t group_rows, uint32_t neg_mask,
                   uint32_t* __restrict__ scope_amax,
-                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t col_tiles, int wide_stores,
-                  uint64_t seed) {
+                  uint8_t* __restrict__ q, uint8_t* __restrict__ s, float* __restrict__ t_out, int64_t col_tiles,
+                  int wide_stores, uint64_t seed) {
   // packed tile: column cl at cl * 128, 8-byte granule g = 4w + m at (g ^ 4 * (cl / 8 % 4))
   __shared__ __attribute__((aligned(16))) uint8_t lq[MODE == 1 ? 128 * 128 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t ls[MODE == 1 ? 128 * 16 : 16];
@@ -295,6 +298,8 @@ nvfp4_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, in
   if (MODE == 1 && ok) {
     float tt;
     scope_scales(__uint_as_float(scope_amax[c / group_rows]), s_enc, tt);   // 8 columns, one scope
+    // the decode scale of a scope, from the lane that holds its first column in the first band
+    if (band == 0 && w == 0 && m == 0 && c % group_rows == 0) t_out[c / group_rows] = tt;
   }
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) {
@@ -418,8 +423,8 @@ template <bool DO_ROW, bool DO_COL>
 __global__ void __launch_bounds__(256)
 nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
                 const uint32_t* __restrict__ scope_amax, uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
-                uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT, int64_t col_tiles, int wide_col,
-                int dw_row) {
+                uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT, float* __restrict__ t_out,
+                int64_t col_tiles, int wide_col, int dw_row) {
   __shared__ __attribute__((aligned(16))) uint8_t lq[DO_COL ? 128 * 128 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t lsc[DO_COL ? 128 * 16 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t lsr[DO_ROW ? 256 * 8 : 16];
@@ -439,6 +444,8 @@ nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int6
   if (ok) {
     float tt;
     scope_scales(__uint_as_float(scope_amax[r0 / group_rows]), s_enc, tt);   // 16 rows, one scope
+    // the decode scale of a scope, from the lane that holds its first row in column 0
+    if (c == 0 && r0 % group_rows == 0) t_out[r0 / group_rows] = tt;
   }
   uint32_t am = 0;
 #pragma unroll
@@ -536,14 +543,6 @@ nvfp4_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int6
 }
 
 // t[g] = decode scale of scope g, from the amax in the workspace.
-__global__ void nvfp4_scope_t_kernel(const uint32_t* __restrict__ scope_amax, float* __restrict__ t, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s_enc, tt;
-  scope_scales(__uint_as_float(scope_amax[i]), s_enc, tt);
-  t[i] = tt;
-}
-
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -571,14 +570,15 @@ static void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
 
 template <int MODE, bool RHT, bool SR = false>
 static void launch_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t group_rows,
-                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, hipStream_t st, uint64_t seed = 0) {
+                        uint32_t sg, uint32_t* ws, uint8_t* q, uint8_t* s, float* t, hipStream_t st,
+                        uint64_t seed = 0) {
   const int64_t col_tiles = (cols + 127) / 128;
   const int64_t bands = (rows + 255) / 256;
   // 16-byte stores need 16-byte aligned output rows (and bases)
   const int wide = rows % 32 == 0 && ((uintptr_t)q & 15) == 0 && ((uintptr_t)s & 15) == 0;
   dim3 grid((unsigned)(bands * col_tiles)), block(256);
   hipLaunchKernelGGL((nvfp4_cols_kernel<MODE, RHT, SR>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, sg, ws, q, s,
-                     col_tiles, wide, seed);
+                     t, col_tiles, wide, seed);
 }
 
 
@@ -650,12 +650,11 @@ hipError_t launch_quant_nvfp4_2d(const void* xv, int64_t rows, int64_t cols, int
   const int dw_row = sr && (cols / 16) % 8 == 0 && ((uintptr_t)sr & 7) == 0;
   dim3 grid((unsigned)(bands * col_tiles)), block(256);
   if (qr && qc)
-    hipLaunchKernelGGL((nvfp4_2d_kernel<true, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+    hipLaunchKernelGGL((nvfp4_2d_kernel<true, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, t, col_tiles, wide, dw_row);
   else if (qr)
-    hipLaunchKernelGGL((nvfp4_2d_kernel<true, false>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
+    hipLaunchKernelGGL((nvfp4_2d_kernel<true, false>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, t, col_tiles, wide, dw_row);
   else
-    hipLaunchKernelGGL((nvfp4_2d_kernel<false, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, col_tiles, wide, dw_row);
-  hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
+    hipLaunchKernelGGL((nvfp4_2d_kernel<false, true>), grid, block, 0, st, x, rows, cols, ld_x, group_rows, ws_amax, qr, sr, qc, sc, t, col_tiles, wide, dw_row);
   return hipGetLastError();
 }
 
@@ -690,14 +689,13 @@ static hipError_t quant_nvfp4_impl(const uint16_t* x, int64_t rows, int64_t cols
     }
   } else {
     if (rht) {
-      launch_cols<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st);
-      launch_cols<1, true, SR>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, st, seed);
+      launch_cols<2, true>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, nullptr, st);
+      launch_cols<1, true, SR>(x, rows, cols, ld_x, gr, neg_mask, ws_amax, qp, sp, t, st, seed);
     } else {
-      launch_cols<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st);
-      launch_cols<1, false, SR>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, st, seed);
+      launch_cols<2, false>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, nullptr, st);
+      launch_cols<1, false, SR>(x, rows, cols, ld_x, gr, 0u, ws_amax, qp, sp, t, st, seed);
     }
   }
-  hipLaunchKernelGGL(nvfp4_scope_t_kernel, dim3((unsigned)((n_scopes + 255) / 256)), dim3(256), 0, st, ws_amax, t, n_scopes);
   return hipGetLastError();
 }
 

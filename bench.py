@@ -154,6 +154,7 @@ class Linear:
                       (n_el - w_el) * FP8B_ACT + w_el * FP8B_W, "hbm")]
         out += [Stage("gemm_fp8_blockwise_" + g, (lambda g=g: L8.gemm(g)), self.gemm_flop, "mfma", "bf16")
                 for g in ("fprop", "dgrad", "wgrad")]
+        out += [Stage("gemm_fp8_blockwise_batched", L8.gemm_all, 3 * self.gemm_flop, "mfma", "bf16")]
         return out
 
     def cpu_baseline(self):

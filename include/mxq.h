@@ -434,6 +434,33 @@ mxq_status gemm_fp8_blockwise(int64_t M, int64_t N, int64_t K, const void* A, co
                               void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gemm_fp8_blockwise_batch -- up to MXQ_GEMM_BATCH_MAX independent gemm_fp8_blockwise
+ * problems in one launch (e.g. the fprop, dgrad and wgrad GEMMs of a blockwise-FP8
+ * linear layer).
+ *   Defined by: as gemm_fp8_blockwise (aib.vote, second paragraph; remio.ai, section
+ *   "NVFP4 por token cuestiona ...").
+ *   Each problem's C is bit-identical to what gemm_fp8_blockwise writes for it (same
+ *   tiles and accumulation order). The problems share one launch, longest K first, so
+ *   a problem with few long tiles (a layer's dgrad) runs beside the others' tiles.
+ *   problems : HOST array of `count` descriptors (1 <= count <= MXQ_GEMM_BATCH_MAX);
+ *              each field follows gemm_fp8_blockwise's argument of the same name.
+ *              Problems with M or N = 0 are skipped; any invalid descriptor fails the
+ *              whole call before anything is launched (MXQ_ERR_SHAPE / NULL / FORMAT /
+ *              ALIGN as for gemm_fp8_blockwise). Output buffers must not overlap.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K;
+  const void* A;
+  const float* sA;
+  const void* B;
+  const float* sB;
+  int b_blocks;
+  float* C;
+  int64_t ldc;
+} mxq_fp8_block_problem;
+mxq_status gemm_fp8_blockwise_batch(const mxq_fp8_block_problem* problems, int count, void* stream);
+
+/* ---------------------------------------------------------------------------
  * gemm_mxfp8_matrix_core -- MXFP8 GEMM C = A_hat B_hat^T on the gfx950 scaled FP8
  * MFMA, which consumes the E8M0 block scales natively (one byte per row and
  * 32-K block of each operand).

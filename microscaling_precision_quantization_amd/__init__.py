@@ -6,7 +6,7 @@ seeded synthetic workloads.
 """
 
 from .binding import (BF16, MXFP4, MXFP8, NVFP4, MxqError, abi_version, dequantize,  # noqa: F401
-                      gemm_block_scaled, gemm_block_scaled_batch, gemm_fp8_blockwise, quantize_fp8_block_act, quantize_fp8_block_weight, gemm_mxfp8_matrix_core, grouped_gemm_block_scaled, moe_combine,
+                      gemm_block_scaled, gemm_block_scaled_batch, gemm_fp8_blockwise, gemm_fp8_blockwise_batch, quantize_fp8_block_act, quantize_fp8_block_weight, gemm_mxfp8_matrix_core, grouped_gemm_block_scaled, moe_combine,
                       moe_swiglu_quantize_nvfp4, quantize_mxfp4, quantize_mxfp4_multi, quantize_mxfp8, quantize_mxfp8_multi, quantize_nvfp4,
                       quantize_nvfp4_2d,
                       quantize_nvfp4_per_token, scale_bytes)

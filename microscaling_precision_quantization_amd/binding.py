@@ -38,6 +38,7 @@ _SIGS = {
     "gemm_block_scaled_batch": [_int, _c_void_p, _int, _c_void_p],
     "gemm_fp8_blockwise": [_i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _i64,
                            _c_void_p],
+    "gemm_fp8_blockwise_batch": [_c_void_p, _int, _c_void_p],
     "quantize_nvfp4_per_token": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "quantize_nvfp4": [_c_void_p, _i64, _i64, _i64, _int, _i64, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _size, _c_void_p],
@@ -377,6 +378,25 @@ def gemm_fp8_blockwise(A, sA, B, sB, b_blocks: bool = True, out=None):
     _check("gemm_fp8_blockwise", lib().gemm_fp8_blockwise(M, N, K, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), int(b_blocks),
                                                           _ptr(out), out.stride(0), _stream(A.device)))
     return out
+
+
+class _Fp8BlockProblem(ctypes.Structure):
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("A", _c_void_p), ("sA", _c_void_p), ("B", _c_void_p),
+                ("sB", _c_void_p), ("b_blocks", _int), ("C", _c_void_p), ("ldc", _i64)]
+
+
+def gemm_fp8_blockwise_batch(problems):
+    """Several gemm_fp8_blockwise problems in one launch. problems: list of dicts with A, sA,
+    B, sB, b_blocks and out."""
+    n = len(problems)
+    arr = (_Fp8BlockProblem * n)()
+    dev = problems[0]["A"].device
+    for i, q in enumerate(problems):
+        A, B_, out = q["A"], q["B"], q["out"]
+        arr[i] = _Fp8BlockProblem(A.shape[0], B_.shape[0], A.shape[1], A.data_ptr(), q["sA"].data_ptr(), B_.data_ptr(),
+                                  q["sB"].data_ptr(), int(q["b_blocks"]), out.data_ptr(), out.stride(0))
+    _check("gemm_fp8_blockwise_batch", lib().gemm_fp8_blockwise_batch(ctypes.cast(arr, _c_void_p), n, _stream(dev)))
+    return [q["out"] for q in problems]
 
 
 def gemm_mxfp8_matrix_core(A, sA, B, sB, out=None):

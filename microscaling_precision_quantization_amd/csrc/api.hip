@@ -417,6 +417,34 @@ mxq_status gemm_fp8_blockwise(int64_t M, int64_t N, int64_t K, const void* A, co
   return hip_status(mxq::launch_gemm(5, M, N, K, A, sA, nullptr, 0, B, sB, nullptr, b_blocks, C, ldc, S(stream)));
 }
 
+mxq_status gemm_fp8_blockwise_batch(const mxq_fp8_block_problem* problems, int count, void* stream) {
+  if (count < 1 || count > MXQ_GEMM_BATCH_MAX) return MXQ_ERR_SHAPE;
+  if (!problems) return MXQ_ERR_NULL;
+  int64_t M[MXQ_GEMM_BATCH_MAX], N[MXQ_GEMM_BATCH_MAX], K[MXQ_GEMM_BATCH_MAX], ldc[MXQ_GEMM_BATCH_MAX];
+  const void *A[MXQ_GEMM_BATCH_MAX], *sA[MXQ_GEMM_BATCH_MAX], *B[MXQ_GEMM_BATCH_MAX], *sB[MXQ_GEMM_BATCH_MAX];
+  const float* none[MXQ_GEMM_BATCH_MAX] = {};
+  int ta[MXQ_GEMM_BATCH_MAX] = {}, tb[MXQ_GEMM_BATCH_MAX];
+  float* C[MXQ_GEMM_BATCH_MAX];
+  int n = 0;
+  int64_t blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const mxq_fp8_block_problem& q = problems[i];
+    if (q.M < 0 || q.N < 0 || q.K < 0) return MXQ_ERR_SHAPE;
+    if (q.M == 0 || q.N == 0) continue;                       // empty problems are skipped
+    if (!q.A || !q.sA || !q.B || !q.sB || !q.C) return MXQ_ERR_NULL;
+    if (q.b_blocks != 0 && q.b_blocks != 1) return MXQ_ERR_FORMAT;
+    if (q.K % 128 || q.K > kMaxGemmK || q.ldc < q.N) return MXQ_ERR_SHAPE;
+    if (!al16(q.A) || !al16(q.B) || !al4(q.sA) || !al4(q.sB) || !al4(q.C)) return MXQ_ERR_ALIGN;
+    blocks += ((q.M + 127) / 128 * ((q.N + 127) / 128) + 7) / 8 * 8;
+    if (blocks > kMaxGridBlocks) return MXQ_ERR_SHAPE;
+    M[n] = q.M; N[n] = q.N; K[n] = q.K; ldc[n] = q.ldc;
+    A[n] = q.A; sA[n] = q.sA; B[n] = q.B; sB[n] = q.sB; tb[n] = q.b_blocks; C[n] = q.C;
+    ++n;
+  }
+  if (n == 0) return MXQ_OK;
+  return hip_status(mxq::launch_gemm_batch(5, n, M, N, K, A, sA, none, ta, B, sB, none, tb, C, ldc, S(stream)));
+}
+
 mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A, const void* sA, const void* B,
                                   const void* sB, float* C, int64_t ldc, void* stream) {
   if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;

@@ -1005,6 +1005,28 @@ __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 
   exact_gemm_tile<LD, 128, 256, SM, 2, false>(p, tm * 128, tn * 256, lds0, lds1, lds2, lds3, ldsc);
 }
 
+// The same for blockwise FP8 (two accumulator sets): 128 x 128 tiles, two workgroups per CU.
+template <int LD, int SM>
+__global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) exact_batch_occ2_kernel(const BatchJobs jobs) {
+  using C = gx::Cfg<LD, 128, 128, SM, 2, false>;
+  MXQ_EXACT_LDS(C)
+  int jsel = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (i < jobs.n && (int64_t)blockIdx.x >= jobs.j[i].block0) jsel = i;
+  int64_t tm = 0, tn = 0;
+  ExactProblem p;
+  bool ok = false;
+#pragma unroll
+  for (int i = 0; i < kMaxBatch; ++i)
+    if (i == jsel) {
+      p = jobs.j[i].p;
+      ok = exact_map_tile((int64_t)blockIdx.x - jobs.j[i].block0, jobs.j[i].tiles_m, jobs.j[i].tiles_n, tm, tn);
+    }
+  if (!ok) return;
+  exact_gemm_tile<LD, 128, 128, SM, 2, false>(p, tm * 128, tn * 128, lds0, lds1, lds2, lds3, ldsc);
+}
+
 // Group of a tile: the largest g with tile_prefix[g] <= tile (tile_prefix is non-decreasing
 // and tile < tile_prefix[groups]). Each wave narrows the range 64-fold per round with one
 // load per lane and a ballot (two rounds for up to 4096 groups).
@@ -1141,11 +1163,35 @@ hipError_t launch_gemm_batch(int fmt, int n, const int64_t* M, const int64_t* N,
                              const void* const* A, const void* const* sA, const float* const* tA, const int* tA_mode,
                              const void* const* B, const void* const* sB, const float* const* tB, const int* tB_mode,
                              float* const* C, const int64_t* ldc, hipStream_t st) {
-  const int ld = fmt == 1 ? 1 : fmt == 2 ? 2 : fmt == 4 ? 3 : 0;
+  const int ld = fmt == 1 ? 1 : fmt == 2 ? 2 : fmt == 4 ? 3 : fmt == 5 ? 4 : 0;
   int order[kMaxBatch];
   for (int i = 0; i < n; ++i) order[i] = i;
   for (int i = 1; i < n; ++i)                          // insertion sort, K descending (stable)
     for (int k = i; k > 0 && K[order[k]] > K[order[k - 1]]; --k) std::swap(order[k], order[k - 1]);
+  if (ld == 4) {
+    // blockwise FP8 (fmt 5, tB_mode = b_blocks): every problem on the single call's 128 x 128
+    // tiles at two workgroups per CU, so a long-K problem (a layer's dgrad) shares the CUs
+    // with the others instead of leaving half the slots idle
+    BatchJobs jobs;
+    jobs.n = 0;
+    int64_t blocks = 0;
+    for (int q = 0; q < n; ++q) {
+      const int i = order[q];
+      ExactProblem& p = jobs.j[jobs.n].p;
+      p.A = (const uint8_t*)A[i]; p.sA = (const uint8_t*)sA[i]; p.tA = nullptr; p.tA_mode = 0;
+      p.a_idx = nullptr; p.a_rows = M[i]; p.a_base = 0; p.m_valid = M[i]; p.lda = K[i];
+      p.B = (const uint8_t*)B[i]; p.sB = (const uint8_t*)sB[i]; p.tB = nullptr; p.tB_mode = tB_mode[i];
+      p.n_valid = N[i]; p.ldb = K[i];
+      p.k_begin = 0; p.k_end = K[i]; p.C = C[i]; p.ldc = ldc[i];
+      jobs.j[jobs.n].tiles_m = (M[i] + 127) / 128;
+      jobs.j[jobs.n].tiles_n = (N[i] + 127) / 128;
+      jobs.j[jobs.n].block0 = blocks;
+      blocks += (jobs.j[jobs.n].tiles_m * jobs.j[jobs.n].tiles_n + 7) / 8 * 8;
+      ++jobs.n;
+    }
+    if (blocks > 0) hipLaunchKernelGGL((exact_batch_occ2_kernel<4, 1>), dim3((unsigned)blocks), dim3(256), 0, st, jobs);
+    return hipGetLastError();
+  }
   int64_t t256 = 0;
   for (int i = 0; i < n; ++i) t256 += ((M[i] + 255) / 256) * ((N[i] + 255) / 256);
   const int bt = t256 >= 192 ? 256 : 128;

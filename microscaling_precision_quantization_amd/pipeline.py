@@ -122,10 +122,18 @@ class LinearFp8Block:
         else:
             B.gemm_fp8_blockwise(dc, dcs, xc, xcs, b_blocks=False, out=self.dw)
 
+    def gemm_all(self):
+        """fprop, dgrad and wgrad in one batched launch (bit-identical to the single calls)."""
+        xr, xs, xc, xcs = self.qx
+        wr, ws, wc, wcs = self.qw
+        dr, ds, dc, dcs = self.qdy
+        B.gemm_fp8_blockwise_batch([dict(A=xr, sA=xs, B=wr, sB=ws, b_blocks=True, out=self.y),
+                                    dict(A=dr, sA=ds, B=wc, sB=wcs, b_blocks=True, out=self.dx),
+                                    dict(A=dc, sA=dcs, B=xc, sB=xcs, b_blocks=False, out=self.dw)])
+
     def step(self, x, w, dy):
         self.quantize(x, w, dy)
-        for n in ("fprop", "dgrad", "wgrad"):
-            self.gemm(n)
+        self.gemm_all()
 
 
 # ---------------------------------------------------------------------------

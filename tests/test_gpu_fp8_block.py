@@ -158,3 +158,51 @@ def test_gemm_zero_and_strided_output():
     mxq.gemm_fp8_blockwise(qa, sa, qb, sb, b_blocks=True, out=out[:, :128])
     o = host(out)
     assert np.all(o[:, :128] == 0.0) and np.all(o[:, 128:] == 7.0)
+
+
+def test_gemm_batch_matches_single_calls():
+    """A layer's three GEMMs (dgrad with 4x the K of the others), a ragged problem with
+    per-row B scales, an empty one and a strided output in one launch: every output is
+    bit-identical to its own gemm_fp8_blockwise call, and the layer's are within 2e-5 of
+    the FP64 product of the oracle's dequantized operands."""
+    g = inputs.rng(147, 0)
+    T, Din, Dout = 256, 384, 1536
+    x = inputs.to_bf16_bits(g.standard_normal((T, Din)) * g.lognormal(0, 1, (T, 1)))
+    w = inputs.normal_bf16(g, (Dout, Din), 0.02)
+    dy = inputs.to_bf16_bits(g.standard_t(3.0, (T, Dout)) * 1e-3)
+    qx, sx, qxt, sxt = mxq.quantize_fp8_block_act(dev_bf16(x), colwise=True)
+    qw, sw, qwt, swt = mxq.quantize_fp8_block_weight(dev_bf16(w))
+    qd, sd, qdt, sdt = mxq.quantize_fp8_block_act(dev_bf16(dy), colwise=True)
+    ra = inputs.to_bf16_bits(g.standard_normal((300, 640)))
+    rb = inputs.to_bf16_bits(g.standard_normal((77, 640)))
+    qra, sra, _, _ = mxq.quantize_fp8_block_act(dev_bf16(ra))
+    qrb, srb, _, _ = mxq.quantize_fp8_block_act(dev_bf16(rb))
+    wide = torch.full((300, 96), 5.0, device="cuda")
+    probs = [dict(A=qx, sA=sx, B=qw, sB=sw, b_blocks=True, out=torch.full((T, Dout), float("nan"), device="cuda")),
+             dict(A=qd, sA=sd, B=qwt, sB=swt, b_blocks=True, out=torch.full((T, Din), float("nan"), device="cuda")),
+             dict(A=qdt, sA=sdt, B=qxt, sB=sxt, b_blocks=False,
+                  out=torch.full((Dout, Din), float("nan"), device="cuda")),
+             dict(A=qra, sA=sra, B=qrb, sB=srb, b_blocks=False, out=wide[:, :77]),
+             dict(A=qra[:0], sA=sra[:0], B=qrb, sB=srb, b_blocks=False, out=torch.empty((0, 77), device="cuda"))]
+    outs = mxq.gemm_fp8_blockwise_batch(probs)
+    for i, q in enumerate(probs[:4]):
+        single = mxq.gemm_fp8_blockwise(q["A"], q["sA"], q["B"], q["sB"], b_blocks=q["b_blocks"])
+        assert torch.equal(outs[i], single), f"problem {i}"
+    assert np.all(host(wide)[:, 77:] == 5.0)
+    xh, dh = ob.dequantize_act(host(qx), host(sx)), ob.dequantize_act(host(qd), host(sd))
+    assert_gemm_close(host(outs[0]), og.gemm_tn_fp64(xh, ob.dequantize_weight(host(qw), host(sw))), "fprop")
+    assert_gemm_close(host(outs[1]), og.gemm_tn_fp64(dh, ob.dequantize_weight(host(qwt), host(swt))), "dgrad")
+    assert_gemm_close(host(outs[2]), og.gemm_tn_fp64(ob.dequantize_act(host(qdt), host(sdt)),
+                                                     ob.dequantize_act(host(qxt), host(sxt))), "wgrad")
+
+
+def test_gemm_batch_rejects_bad_descriptors_before_launch():
+    g = inputs.rng(148, 0)
+    qa, sa, _, _ = mxq.quantize_fp8_block_act(dev_bf16(inputs.normal_bf16(g, (128, 256), 1.0)))
+    out = torch.full((128, 128), 3.0, device="cuda")
+    good = dict(A=qa, sA=sa, B=qa, sB=sa, b_blocks=False, out=out)
+    bad = dict(A=qa[:, :200], sA=sa, B=qa[:, :200], sB=sa, b_blocks=False, out=torch.empty((128, 128), device="cuda"))
+    with pytest.raises(mxq.MxqError):
+        mxq.gemm_fp8_blockwise_batch([good, bad])                 # K % 128 != 0
+    torch.cuda.synchronize()
+    assert np.all(host(out) == 3.0)                               # nothing ran

@@ -202,3 +202,30 @@ def test_scale_and_workspace_sizes():
     L = B.lib()
     assert L.mxq_workspace_bytes(B.OP_QUANTIZE_NVFP4, 0, 0, 3) >= 12
     assert L.mxq_workspace_bytes(B.OP_GROUPED_GEMM, 128, 0, 0) >= 129 * 8
+
+
+def test_fp8_block_batch_validation():
+    """Every descriptor is checked on the host before anything is launched (fake device
+    addresses: no case here reaches a launch)."""
+    f = B.lib().gemm_fp8_blockwise_batch
+
+    def prob(**kw):
+        d = dict(M=128, N=128, K=256, A=P, sA=P, B=P, sB=P, b_blocks=1, C=P, ldc=128)
+        d.update(kw)
+        return B._Fp8BlockProblem(**d)
+
+    def call(*probs, count=None):
+        arr = (B._Fp8BlockProblem * len(probs))(*probs)
+        return f(ctypes.cast(arr, ctypes.c_void_p), len(probs) if count is None else count, None)
+
+    assert call(prob(), count=0) == 2                                   # count < 1
+    assert call(*[prob(M=0) for _ in range(9)]) == 2                    # count > MXQ_GEMM_BATCH_MAX
+    assert f(None, 1, None) == 1                                        # NULL array
+    assert call(prob(), prob(K=200)) == 2                               # K % 128 in a later descriptor
+    assert call(prob(), prob(sB=None)) == 1
+    assert call(prob(b_blocks=2)) == 4
+    assert call(prob(A=MIS)) == 3
+    assert call(prob(sA=P + 2)) == 3                                    # scales 4-byte aligned
+    assert call(prob(ldc=64)) == 2                                      # ldc < N
+    assert call(prob(M=-1)) == 2
+    assert call(prob(M=0), prob(N=0, A=None)) == 0                      # only empty problems: no-op

@@ -40,10 +40,15 @@ def gemm_nvfp4_ref(pa, Sa, ta_rows, pb, Sb, tb_rows) -> np.ndarray:
 
 
 def normwise_rel_err(c, c_ref) -> float:
+    """||C - C_ref||_F / ||C_ref||_F in FP64; an all-zero C_ref gives 0 when C is exactly
+    zero (either sign) and +inf otherwise. Both norms are taken of the arrays divided by
+    one power of two near their largest magnitude (an exact step), so squares of tiny
+    or huge entries neither underflow nor overflow."""
     c = np.asarray(c, dtype=np.float64)
     c_ref = np.asarray(c_ref, dtype=np.float64)
-    den = np.linalg.norm(c_ref)
-    num = np.linalg.norm(c - c_ref)
-    if den == 0.0:
-        return 0.0 if num == 0.0 else float("inf")
-    return float(num / den)
+    d = c - c_ref
+    if not np.any(c_ref):
+        return 0.0 if not np.any(c) else float("inf")
+    big = max(float(np.max(np.abs(c_ref))), float(np.max(np.abs(d))) if d.size else 0.0)
+    scale = 2.0 ** np.floor(np.log2(big))
+    return float(np.linalg.norm(d / scale) / np.linalg.norm(c_ref / scale))

@@ -131,6 +131,20 @@ def test_f32_to_bf16_matches_torch():
     assert np.array_equal(F.f32_to_bf16_bits(v), ref)
 
 
+def test_f32_to_bf16_infinities_overflow_and_ties():
+    # IEEE binary32 bit patterns rounded to their top 16 bits, nearest-even:
+    #   +-Inf stay +-Inf (0x7F80 / 0xFF80); FLT_MAX 0x7F7FFFFF rounds up past the BF16
+    #   maximum 0x7F7F to Inf; 0x7F7F8000 is a tie whose lower neighbour 0x7F7F is odd, so
+    #   it goes up to Inf; 0x3F808000 is a tie between 0x3F80 (even) and 0x3F81, so it stays;
+    #   0x3F818000 is a tie between 0x3F81 (odd) and 0x3F82, so it goes up; 0x3F807FFF is
+    #   below the tie; the smallest FP32 subnormal 0x00000001 rounds to +0.
+    bits = np.array([0x7F800000, 0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x3F808000,
+                     0x3F818000, 0x3F807FFF, 0x00000001, 0x80000001], dtype=np.uint32)
+    got = F.f32_to_bf16_bits(bits.view(np.float32))
+    assert [int(b) for b in got] == [0x7F80, 0xFF80, 0x7F80, 0xFF80, 0x7F80, 0x3F80, 0x3F82, 0x3F80,
+                                     0x0000, 0x8000]
+
+
 def test_nonfinite_inputs_are_rejected():
     with pytest.raises(ValueError):
         F.encode_e4m3(np.array([np.nan]))

@@ -52,6 +52,65 @@ def test_swiglu_reference_special_points():
     assert F.bf16_bits_to_f32(hb)[0, 1] == 60.0
 
 
+def test_swiglu_correct_rounding_hand_worked():
+    # silu(1) * 1 = 1 / (1 + 1/e) = 0.7310585786...; the BF16 grid in [0.5, 1) has spacing
+    # 2^-8, 0.7310585786 * 256 = 187.151 -> 187 / 256 = 0.73046875 = 0x3F3B.
+    # g = 0: +0. g = 259, u = 1 and g = 37, u = 7: g u = 259 lies exactly between the BF16
+    # neighbours 258 (0x4381) and 260 (0x4382, the even one), but the real value is
+    # 259 / (1 + e^-g), strictly below 259, so it rounds down to 258 (for g = 37 the FP64
+    # 1 + e^-37 already rounds to 1). g = -1000: -1000 e^-1000 underflows to -0.
+    gu = np.zeros((1, 10), dtype=np.float32)
+    gu[0, :5] = [1.0, 0.0, 259.0, 37.0, -1000.0]
+    gu[0, 5:] = [1.0, 5.0, 1.0, 7.0, 1.0]
+    assert list(moe.swiglu_bf16_ref(gu)[0]) == [0x3F3B, 0x0000, 0x4381, 0x4381, 0x8000]
+
+
+def _bf16_rne_rational(v):
+    """Round a Fraction to the BF16 grid (RNE, 8 significant bits, smallest normal 2^-126)."""
+    from fractions import Fraction
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    q = Fraction(2) ** (e - 7)
+    n, rem = divmod(a, q)
+    n = int(n)
+    if rem * 2 > q or (rem * 2 == q and n % 2):
+        n += 1
+    return (n * q) if v > 0 else -(n * q)
+
+
+def test_swiglu_matches_arbitrary_precision_brute_force():
+    # an independent route: mpmath at 400 digits, then rational rounding to BF16; inputs span
+    # ordinary gates, large gates whose product g u sits exactly on a BF16 midpoint, and
+    # very negative gates whose result is a BF16 subnormal
+    import mpmath
+    from fractions import Fraction
+    mpmath.mp.dps = 400                         # sees e^-511 next to 1
+    g = np.random.default_rng(11)
+    n = 400
+    odd = 2 * g.integers(128, 256, 60) + 1                 # 257 .. 511
+    # g u on a BF16 midpoint: g = 32 or 64 with u = odd 2^-6 or 2^-7 (g u = odd / 2 in
+    # [128, 256), quantum 1), and odd g in [257, 511] with u = 1 (quantum 2)
+    gate = np.concatenate([g.standard_normal(n) * 4, np.full(20, 32.0), np.full(20, 64.0), odd[40:].astype(float),
+                           -g.uniform(80, 95, 50)])
+    up = np.concatenate([g.standard_normal(n) * 3, odd[:20] * 2.0 ** -6, odd[20:40] * 2.0 ** -7, np.ones(20),
+                         g.standard_normal(50) * 1e-3])
+    gu = np.concatenate([gate, up]).astype(np.float32).reshape(1, -1)
+    got = F.bf16_bits_to_f32(moe.swiglu_bf16_ref(gu))[0].astype(np.float64)
+    m = len(gate)
+    for j in range(m):
+        gj, uj = float(gu[0, j]), float(gu[0, m + j])
+        h = mpmath.mpf(gj) * mpmath.mpf(uj) / (1 + mpmath.exp(-mpmath.mpf(gj)))
+        sign, man, ex, _ = h._mpf_               # h = (-1)^sign man 2^ex exactly (400-digit value)
+        hv = Fraction(int(man)) * Fraction(2) ** int(ex) * (-1 if sign else 1) if man else Fraction(0)
+        ref = _bf16_rne_rational(hv)
+        assert Fraction(got[j]) == ref, (j, gj, uj, got[j], float(ref))
+
+
 def test_ulp_distance():
     a = inputs.to_bf16_bits(np.array([1.0, -1.0, 0.0, 1.0]))
     b = a.copy()

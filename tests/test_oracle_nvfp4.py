@@ -113,6 +113,49 @@ def test_outer_scale_closed_forms():
     assert nvfp4.unpack_codes(p)[0, 0] == 0 and nvfp4.unpack_codes(p)[0, 1] == 0x8
 
 
+def test_scope_scale_overflow_branch_hand_worked():
+    # A token of BF16 subnormals [2^-127, -2^-128, 3 * 2^-129, 0 x 13 | 16 zeros]:
+    #   A = 2^-127, 2688 / A = 2688 * 2^127 overflows binary32 -> s_enc = FLT_MAX;
+    #   t = fl(1 / FLT_MAX) = fl(2^-128 (1 + 2^-24 + ...)) = 2^-128 (FP32 subnormal 0x00200000).
+    #   Block 0: a_b = 2^-127, fl(a_b / 6) = 699051 * 2^-149 (2^22 / 6 = 699050.67 rounds up);
+    #   times FLT_MAX = (2^128 - 2^104): 699051 (2^-21 - 2^-45) = (11184816 - 0.667) 2^-25,
+    #   rounded to 11184815 * 2^-25 = 0.33333331; E4M3 neighbours 0.3125 and 0.34375 with
+    #   midpoint 0.328125 -> S_b = 0.34375 = 0x2B. r_b = FLT_MAX / 0.34375 overflows -> FLT_MAX.
+    #   Codes: 2^-127 * FLT_MAX = 2 - 2^-23 -> 2 (code 4); -2^-128 * FLT_MAX = -(1 - 2^-24) -> -1
+    #   (code 0xA); 3 * 2^-129 * FLT_MAX = 1.5 - 3 * 2^-25 -> 1.5 (code 3); zeros -> 0.
+    #   Block 1 (all zero): S_b = 0, codes 0.
+    row = np.zeros((1, 32), dtype=np.uint16)
+    row[0, :3] = [0x0040, 0x8020, 0x0030]           # 2^-127, -2^-128, 3 * 2^-129 as BF16 bits
+    p, S, t = nvfp4.quantize_per_token(row)
+    assert t.view(np.uint32)[0] == 0x00200000
+    assert list(S[0]) == [0x2B, 0x00]
+    assert list(p[0]) == [0xA4, 0x03] + [0] * 14
+    s_enc, t2 = nvfp4.scope_scales(np.array([2.0 ** -127], dtype=np.float32))
+    assert s_enc[0] == F.FLT_MAX and t2[0] == t[0]
+    # the smallest BF16 subnormal, 2^-133: fl(2^-133 / 6) = 10923 * 2^-149, times FLT_MAX
+    # = 10923 (2^-21 - 2^-45) -> 11185151 * 2^-31 = 0.0052085, E4M3 subnormal 3 * 2^-9
+    # (0.0052085 / 2^-9 = 2.67 -> 3, code 0x03); 2^-133 * FLT_MAX = (2 - 2^-23) 2^-6 -> 0
+    one = np.zeros((1, 16), dtype=np.uint16)
+    one[0, 5] = 0x0001
+    p, S, t = nvfp4.quantize_per_token(one)
+    assert t.view(np.uint32)[0] == 0x00200000 and S[0, 0] == 0x03 and not np.any(p)
+    # per-tensor scope: the same branch when the whole tensor holds only such values
+    pt, St, tt = nvfp4.quantize_per_tensor(np.concatenate([row, np.zeros((1, 32), np.uint16)]))
+    assert tt.view(np.uint32)[0] == 0x00200000
+    assert list(St[0]) == [0x2B, 0x00] and list(pt[0]) == [0xA4, 0x03] + [0] * 14 and not np.any(pt[1])
+
+
+def test_scope_amax_2688_hand_worked():
+    # A = a_b = 2688 gives s_enc = 1, d_b = fl(2688 / 6) = 448 exactly (code 0x7E, no clamp
+    # needed: d_b never exceeds 448 (1 + 3 * 2^-24), which rounds to 448), the element
+    # 2688 -> 6 (code 7), and 464 * fl(1 / 448) = 1.0357 -> 1 (code 2).
+    x = np.zeros((1, 16))
+    x[0, 0] = 2688.0
+    x[0, 1] = 464.0                # 464 * r_b = 464 * (1 / 448) = 1.0357 -> 1 (code 2)
+    p, S, t = nvfp4.quantize_per_token(bf16(x))
+    assert S[0, 0] == 0x7E and t[0] == 1.0 and p[0, 0] == (0x7 | (0x2 << 4))
+
+
 def test_nibble_order_low_first():
     x = np.zeros((1, 16))
     x[0, 0] = 6.0       # -> code 7 in the low nibble of byte 0

@@ -208,7 +208,8 @@ mxq_status quantize_fp8_block_weight(const void* x, int64_t rows, int64_t cols, 
  *   x       : BF16 (tokens, hidden), row stride ld_x elements (ld_x % 8 == 0).
  *   q_packed: uint8 (tokens, hidden/2);  s_block: E4M3 (tokens, hidden/16);
  *   s_token : float (tokens) -- the decode scale t (dequantized x = q * S * t).
- *   Requires hidden % 16 == 0.
+ *   Requires hidden % 16 == 0 and hidden <= 16384 (a row is held in the registers of
+ *   one wavefront); MXQ_ERR_SHAPE otherwise.
  * ------------------------------------------------------------------------- */
 mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidden, int64_t ld_x,
                                     void* q_packed, void* s_block, float* s_token,
@@ -228,7 +229,9 @@ mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidde
  *   transform in binary32 (stages 1, 2, 4, 8; (a, b) -> (a + b, a - b)); u = w / 4.
  *   Scope amax is taken over the transformed values.
  *
- *   x          : BF16 (rows, cols), row stride ld_x.
+ *   x          : BF16 (rows, cols), row stride ld_x. The input is BF16 only: the
+ *                tensors this path quantizes (activations, weights, gradients, the
+ *                SwiGLU output) are all BF16 on it, so no FP32-input variant exists.
  *   scope      : ROW / TENSOR / GROUP (group_rows consecutive rows share a scale;
  *                with transpose = 1 a group is group_rows consecutive COLUMNS of x,
  *                i.e. rows of the transposed output).
@@ -240,7 +243,8 @@ mxq_status quantize_nvfp4_per_token(const void* x, int64_t tokens, int64_t hidde
  *   workspace  : device scratch of mxq_workspace_bytes(MXQ_OP_QUANTIZE_NVFP4,
  *                rows, cols, scope-count) bytes (TENSOR and GROUP scopes; NULL
  *                allowed for ROW).
- *   Requires the blocked axis % 16 == 0; with transpose = 1 also cols % 8 == 0.
+ *   Requires the blocked axis % 16 == 0; with transpose = 1 also cols % 8 == 0;
+ *   with transpose = 0 and scope ROW, cols <= 16384 (as quantize_nvfp4_per_token).
  * ------------------------------------------------------------------------- */
 mxq_status quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                           mxq_scope scope, int64_t group_rows, int transpose,
@@ -357,10 +361,17 @@ mxq_status dequantize_transposed(mxq_format fmt, const void* q, const void* s, c
  *   (remio.ai, section "La Compatibilidad ..."; 7minutos.es, section "Que esta
  *   cuantificado y que no").
  *   MXQ_MXFP8: A (M, K) E4M3 + sA (M, K/32) E8M0; B (N, K) + sB (N, K/32); tA/tB unused.
- *              Every E4M3 * 2^(s-127) operand value is formed exactly and the
+ *              Every E4M3 * 2^(s-127) operand value is formed exactly in BF16 and the
  *              products are accumulated at FP32 precision (see
  *              gemm_mxfp8_matrix_core for the native scaled-FP8 MFMA variant).
- *              Dequantized magnitudes must stay below 2^128.
+ *              Range: a value is exact when its magnitude is below 2^128 and it is a
+ *              multiple of 2^-133 (BF16's smallest subnormal). Every operand that
+ *              quantize_mxfp8 makes from finite BF16 data below 2^128 meets both (its
+ *              codes times 2^(s-127) are multiples of the input's own 2^-133 grid).
+ *              Bytes made elsewhere can break the lower bound only with scale codes
+ *              s <= 2 and E4M3 subnormal codes (e.g. s = 0, code 0x01 = 2^-136): such
+ *              values are rounded to the BF16 grid before the products, and the
+ *              accuracy bound below does not cover them.
  *   MXQ_NVFP4: A (M, K/2) packed E2M1 + sA (M, K/16) E4M3 + tA (ROW: M, TENSOR: 1);
  *              B likewise with tB (ROW: N, TENSOR: 1);
  *              C = tA[m] tB[n] * sum_k (qA SA)(qB SB) -- the E4M3-per-16 block
@@ -522,14 +533,18 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
  *   ("Miles Blackwell RL", remio.ai, section "Un Cuantizador Compartido ..."), and
  *   per-token NVFP4 on the expert activations (same page, section "La
  *   Compatibilidad ..."). Each slot row (token, expert) is one scale scope.
- *   h = silu(g) * u = g / (1 + exp(-g)) * u in binary32 (g = row[0:inter],
- *   u = row[inter:2*inter]) with the hardware exponential, rounded to BF16: within one
- *   BF16 ulp of the exactly computed value; then the per-token quantizer above on the
- *   BF16 row (bit-exact on that h).
+ *   h = silu(g) * u = g u / (1 + e^(-g)) (g = row[0:inter], u = row[inter:2*inter]),
+ *   rounded once to BF16 (nearest, ties to even) from its exact value, so that no
+ *   approximate exponential reaches the FP4 quantizer (remio.ai, section "Un
+ *   Cuantizador Compartido ..."): computed in binary64 (relative error below 2^-50)
+ *   and rounded to BF16 through a round-to-odd binary32 step; then the per-token
+ *   quantizer above on the BF16 row. Both h and the quantized bytes are bit-exact
+ *   against the correctly rounded definition (a value within 2^-50 of a BF16 rounding
+ *   midpoint is the only case the binary64 evaluation could misplace).
  *
  *   gate_up : FP32 (rows, 2*inter); h_bf16 : optional BF16 (rows, inter) copy of h
  *   (NULL = not written); q (rows, inter/2), s (rows, inter/16), t (rows).
- *   Requires inter % 16 == 0.
+ *   Requires inter % 16 == 0 and inter <= 16384; MXQ_ERR_SHAPE otherwise.
  * ------------------------------------------------------------------------- */
 mxq_status moe_swiglu_quantize_nvfp4(const float* gate_up, int64_t rows, int64_t inter,
                                      void* h_bf16, void* q, void* s, float* t, void* stream);

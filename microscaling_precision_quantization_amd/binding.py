@@ -119,6 +119,73 @@ def _u8(shape, dev):
     return torch.empty(shape, dtype=torch.uint8, device=dev)
 
 
+class _Checks:
+    """Host-side checks of the tensors handed to one C-ABI call: dtype, exact shape, unit
+    inner stride and a dense layout (ld=True: rows may be padded, row stride >= the row
+    length) for each tensor as it is named, then, in done(), that all of them live on the
+    one GPU the call runs on. Every mismatch raises ValueError before anything reaches
+    the library, so a wrong buffer can never be read or written past its end."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.seen = []
+
+    def need(self, t, name: str, dtype, shape, ld: bool = False):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        shape = tuple(int(v) for v in shape)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
+        if t.numel():
+            if t.dim() and t.stride(-1) != 1:
+                raise ValueError(f"{name}: the innermost dimension must be contiguous")
+            if ld:
+                if t.dim() != 2 or t.stride(0) < t.shape[1]:
+                    raise ValueError(f"{name}: expected a 2-D tensor with row stride >= {t.shape[1]}")
+            elif not t.is_contiguous():
+                raise ValueError(f"{name}: expected a contiguous tensor")
+        self.seen.append((name, t))
+        return t
+
+    def opt(self, t, *a, **kw):
+        return None if t is None else self.need(t, *a, **kw)
+
+    def operand(self, fmt: int, name: str, t, rows: int, K: int, s=None):
+        """A K-contiguous GEMM operand of `rows` rows and K elements (+ its block scales)."""
+        width = K if fmt == BF16 else K // _elems_per_byte(fmt)
+        self.need(t, name, _operand_dtype(fmt), (rows, width))
+        if fmt != BF16:
+            if s is None:
+                raise ValueError(f"s{name}: block scales are required for this format")
+            self.need(s, "s" + name, torch.uint8, (rows, K // _scale_block(fmt)))
+
+    def outer_scale(self, name: str, t, scope: str, rows: int):
+        if t is None:
+            raise ValueError(f"{name}: NVFP4 needs its FP32 scale")
+        self.need(t, name, torch.float32, (rows if SCOPE[scope] == 0 else 1,))
+
+    def done(self):
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name}: expected a GPU tensor, got one on {t.device}")
+            if t.device != self.dev:
+                raise ValueError(f"{name}: on {t.device}, expected {self.dev}")
+
+
+def _elems_per_byte(fmt: int) -> int:
+    return 2 if fmt in _PACKED4 else 1
+
+
+def _operand_dtype(fmt: int):
+    return torch.bfloat16 if fmt == BF16 else torch.uint8
+
+
+def _scale_block(fmt: int) -> int:
+    return 16 if fmt == NVFP4 else 32
+
+
 # ---------------------------------------------------------------------------
 # Quantizers
 # ---------------------------------------------------------------------------
@@ -134,6 +201,7 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, 
     dev = x.device
     if out is not None:
         q_row, s_row, q_col, s_col = out
+        _mx_check_out("quantize_mxfp8", x, out, 1)
     else:
         q_row = _u8((R, C), dev) if rowwise else None
         s_row = _u8((R, C // 32), dev) if rowwise else None
@@ -154,6 +222,7 @@ def quantize_mxfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, 
     dev = x.device
     if out is not None:
         q_row, s_row, q_col, s_col = out
+        _mx_check_out("quantize_mxfp4", x, out, 2)
     else:
         q_row = _u8((R, C // 2), dev) if rowwise else None
         s_row = _u8((R, C // 32), dev) if rowwise else None
@@ -206,10 +275,28 @@ class _Mxfp8Tensor(ctypes.Structure):
                 ("s_row", _c_void_p), ("q_colT", _c_void_p), ("s_colT", _c_void_p)]
 
 
+def _mx_check_out(fn: str, x, out, per_byte: int):
+    """Output buffers of an MXFP8 / MXFP4 quantize: (R, C/per_byte) + (R, C/32) rowwise,
+    (C, R/per_byte) + (C, R/32) columnwise; a skipped copy is (None, None)."""
+    R, C = x.shape
+    q_row, s_row, q_col, s_col = out
+    if (q_row is None) != (s_row is None) or (q_col is None) != (s_col is None):
+        raise ValueError(f"{fn}: a copy needs both its element and its scale buffer")
+    c = _Checks(x.device)
+    c.opt(q_row, "q_row", torch.uint8, (R, C // per_byte))
+    c.opt(s_row, "s_row", torch.uint8, (R, C // 32))
+    c.opt(q_col, "q_colT", torch.uint8, (C, R // per_byte))
+    c.opt(s_col, "s_colT", torch.uint8, (C, R // 32))
+    c.done()
+
+
 def _mx_multi(fn: str, xs, outs):
     n = len(xs)
+    if len(outs) != n:
+        raise ValueError(f"{fn}: {n} inputs but {len(outs)} output tuples")
     arr = (_Mxfp8Tensor * n)()
     for i, (x, o) in enumerate(zip(xs, outs)):
+        _mx_check_out(fn, x, o, 2 if fn.startswith("quantize_mxfp4") else 1)
         _bf16(x)
         q_row, s_row, q_col, s_col = o
         arr[i] = _Mxfp8Tensor(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0),
@@ -323,6 +410,10 @@ def dequantize_transposed(fmt: int, q: torch.Tensor, s=None, t=None, t_scope: st
         out_cols = src_row.numel() if src_row is not None else group_rows
     if out is None:
         out = torch.empty((groups, cols, out_cols), dtype=torch.bfloat16, device=q.device)
+    elif (out.dtype != torch.bfloat16 or out.dim() != 3 or tuple(out.shape[:2]) != (groups, cols)
+          or out.shape[2] < out_cols or out.stride(-1) != 1 or out.stride(0) != cols * out.stride(1)
+          or out.device != q.device):
+        raise ValueError(f"out: expected BF16 (groups={groups}, cols={cols}, >= {out_cols}) rows on {q.device}")
     _check("dequantize_transposed", lib().dequantize_transposed(
         fmt, _ptr(q), _ptr(s), _ptr(t), SCOPE[t_scope], groups, group_rows, cols, _ptr(src_row), out_cols,
         _ptr(out), out.stride(-2), _stream(q.device)))
@@ -333,11 +424,29 @@ def dequantize_transposed(fmt: int, q: torch.Tensor, s=None, t=None, t_scope: st
 # GEMMs
 # ---------------------------------------------------------------------------
 
+def _gemm_args(fmt: int, A, sA, B, sB, tA, tB, tA_scope, tB_scope, out):
+    """Validate one TN GEMM's operands and output; returns (M, N, K)."""
+    if fmt not in (MXFP8, NVFP4, BF16, MXFP4):
+        raise ValueError(f"unknown format {fmt}")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D (rows, K-contiguous bytes or elements)")
+    M, N = A.shape[0], B.shape[0]
+    K = A.shape[1] * _elems_per_byte(fmt)
+    c = _Checks(A.device)
+    c.operand(fmt, "A", A, M, K, sA)
+    c.operand(fmt, "B", B, N, K, sB)
+    if fmt == NVFP4:
+        c.outer_scale("tA", tA, tA_scope, M)
+        c.outer_scale("tB", tB, tB_scope, N)
+    if out is not None:
+        c.need(out, "out", torch.float32, (M, N), ld=True)
+    c.done()
+    return M, N, K
+
+
 def gemm_block_scaled(fmt: int, A, sA, B, sB, tA=None, tB=None, tA_scope="row", tB_scope="tensor", out=None):
     """C = A_hat B_hat^T in FP32; A (M, K-bytes) and B (N, K-bytes) K-contiguous."""
-    M = A.shape[0]
-    N = B.shape[0]
-    K = A.shape[1] * (2 if fmt in _PACKED4 else 1)
+    M, N, K = _gemm_args(fmt, A, sA, B, sB, tA, tB, tA_scope, tB_scope, out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _check("gemm_block_scaled", lib().gemm_block_scaled(fmt, M, N, K, _ptr(A), _ptr(sA), _ptr(tA), SCOPE[tA_scope],
@@ -360,7 +469,10 @@ def gemm_block_scaled_batch(fmt: int, problems):
     dev = problems[0]["A"].device
     for i, q in enumerate(problems):
         A, B_, out = q["A"], q["B"], q["out"]
-        K = A.shape[1] * (2 if fmt in _PACKED4 else 1)
+        if A.device != dev:
+            raise ValueError(f"problem {i}: operands on {A.device}, the batch runs on {dev}")
+        _, _, K = _gemm_args(fmt, A, q.get("sA"), B_, q.get("sB"), q.get("tA"), q.get("tB"),
+                             q.get("tA_scope", "row"), q.get("tB_scope", "tensor"), out)
         ptr = lambda t: None if t is None else t.data_ptr()
         arr[i] = _GemmProblem(A.shape[0], B_.shape[0], K, A.data_ptr(), ptr(q.get("sA")), ptr(q.get("tA")),
                               SCOPE[q.get("tA_scope", "row")], B_.data_ptr(), ptr(q.get("sB")), ptr(q.get("tB")),
@@ -369,10 +481,24 @@ def gemm_block_scaled_batch(fmt: int, problems):
     return [q["out"] for q in problems]
 
 
-def gemm_fp8_blockwise(A, sA, B, sB, b_blocks: bool = True, out=None):
-    """Blockwise FP8 GEMM C = A_hat B_hat^T (FP32); sB per 128 x 128 block (b_blocks) or per row."""
+def _fp8_block_args(A, sA, B, sB, b_blocks: bool, out):
+    """Validate a blockwise-FP8 GEMM; returns (M, N, K)."""
     M, K = A.shape
     N = B.shape[0]
+    c = _Checks(A.device)
+    c.need(A, "A", torch.uint8, (M, K))
+    c.need(sA, "sA", torch.float32, (M, K // 128))
+    c.need(B, "B", torch.uint8, (N, K))
+    c.need(sB, "sB", torch.float32, ((N + 127) // 128, K // 128) if b_blocks else (N, K // 128))
+    if out is not None:
+        c.need(out, "out", torch.float32, (M, N), ld=True)
+    c.done()
+    return M, N, K
+
+
+def gemm_fp8_blockwise(A, sA, B, sB, b_blocks: bool = True, out=None):
+    """Blockwise FP8 GEMM C = A_hat B_hat^T (FP32); sB per 128 x 128 block (b_blocks) or per row."""
+    M, N, K = _fp8_block_args(A, sA, B, sB, b_blocks, out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _check("gemm_fp8_blockwise", lib().gemm_fp8_blockwise(M, N, K, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), int(b_blocks),
@@ -393,6 +519,9 @@ def gemm_fp8_blockwise_batch(problems):
     dev = problems[0]["A"].device
     for i, q in enumerate(problems):
         A, B_, out = q["A"], q["B"], q["out"]
+        if A.device != dev:
+            raise ValueError(f"problem {i}: operands on {A.device}, the batch runs on {dev}")
+        _fp8_block_args(A, q["sA"], B_, q["sB"], q["b_blocks"], out)
         arr[i] = _Fp8BlockProblem(A.shape[0], B_.shape[0], A.shape[1], A.data_ptr(), q["sA"].data_ptr(), B_.data_ptr(),
                                   q["sB"].data_ptr(), int(q["b_blocks"]), out.data_ptr(), out.stride(0))
     _check("gemm_fp8_blockwise_batch", lib().gemm_fp8_blockwise_batch(ctypes.cast(arr, _c_void_p), n, _stream(dev)))
@@ -401,13 +530,54 @@ def gemm_fp8_blockwise_batch(problems):
 
 def gemm_mxfp8_matrix_core(A, sA, B, sB, out=None):
     """MXFP8 GEMM on the native scaled-FP8 matrix core (see include/mxq.h for its accumulation)."""
-    M, K = A.shape
-    N = B.shape[0]
+    M, N, K = _gemm_args(MXFP8, A, sA, B, sB, None, None, "row", "tensor", out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _check("gemm_mxfp8_matrix_core", lib().gemm_mxfp8_matrix_core(M, N, K, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB),
                                                                   _ptr(out), out.stride(0), _stream(A.device)))
     return out
+
+
+def _grouped_args(fmt, offsets, A, B, N, K, sA, sB, tA, tB, tA_scope, tB_scope, a_row_index, vary_k, M, total,
+                  a_rows, out):
+    """Validate a grouped GEMM's host-visible shapes (the offsets' values are checked on
+    the device)."""
+    c = _Checks(A.device)
+    c.need(offsets, "offsets", torch.int64, (offsets.numel(),))
+    G = offsets.numel() - 1
+    if G < 0:
+        raise ValueError("offsets: needs groups + 1 entries")
+    if vary_k:
+        if a_row_index is not None:
+            raise ValueError("a_row_index is not supported with vary_k")
+        c.operand(fmt, "A", A, M, total, sA)
+        c.operand(fmt, "B", B, N, total, sB)
+        if out is not None:
+            c.need(out, "out", torch.float32, (G, M, N))
+        c.done()
+        return
+    rows = A.shape[0]
+    if a_row_index is not None:
+        c.need(a_row_index, "a_row_index", torch.int32, (total,))
+        if a_rows is not None and a_rows != rows:
+            raise ValueError(f"a_rows = {a_rows} but A has {rows} rows")
+    elif rows != total:
+        raise ValueError(f"A: {rows} rows, expected total = {total} (no gather)")
+    c.operand(fmt, "A", A, rows, K, sA)
+    width = K if fmt == BF16 else K // _elems_per_byte(fmt)
+    if B.shape[-1] != width or B.numel() != G * N * width:
+        raise ValueError(f"B: shape {tuple(B.shape)}, expected {G} stacked ({N}, {width}) operands")
+    if not B.is_contiguous():
+        raise ValueError("B: expected a contiguous tensor")
+    c.operand(fmt, "B", B.reshape(G * N, width), G * N, K, None if sB is None else sB.reshape(-1, sB.shape[-1]))
+    if fmt == NVFP4:
+        c.outer_scale("tA", tA, tA_scope, rows)
+        if tB is None:
+            raise ValueError("tB: NVFP4 needs its FP32 scale")
+        c.need(tB, "tB", torch.float32, (G if SCOPE[tB_scope] == 2 else G * N if SCOPE[tB_scope] == 0 else 1,))
+    if out is not None:
+        c.need(out, "out", torch.float32, (total, N))
+    c.done()
 
 
 def grouped_gemm_block_scaled(fmt: int, offsets, A, B, N: int, K: int, sA=None, sB=None, tA=None, tB=None,
@@ -421,12 +591,16 @@ def grouped_gemm_block_scaled(fmt: int, offsets, A, B, N: int, K: int, sA=None, 
     dev = A.device
     if total is None:
         total = int(offsets[-1].item())
+    _grouped_args(fmt, offsets, A, B, N, K, sA, sB, tA, tB, tA_scope, tB_scope, a_row_index, vary_k, M, total,
+                  a_rows, out)
     if out is None:
         shape = (groups, M, N) if vary_k else (total, N)
         out = torch.empty(shape, dtype=torch.float32, device=dev)
     ws_bytes = lib().mxq_workspace_bytes(OP_GROUPED_GEMM, groups, 0, 0)
     if workspace is None:
         workspace = _u8((max(ws_bytes, 1),), dev)
+    elif workspace.numel() < ws_bytes:
+        raise ValueError(f"workspace: {workspace.numel()} bytes, the call needs {ws_bytes}")
     _check("grouped_gemm_block_scaled", lib().grouped_gemm_block_scaled(
         fmt, groups, _ptr(offsets), int(vary_k), total, M, N, K, _ptr(a_row_index), a_rows if a_rows is not None
         else (A.shape[0] if a_row_index is not None else 0), _ptr(A), _ptr(sA), _ptr(tA),
@@ -444,6 +618,9 @@ def moe_swiglu_quantize_nvfp4(gate_up: torch.Tensor, keep_h: bool = True):
     rows, two_i = gate_up.shape
     inter = two_i // 2
     dev = gate_up.device
+    c = _Checks(dev)
+    c.need(gate_up, "gate_up", torch.float32, (rows, 2 * inter))
+    c.done()
     h = torch.empty((rows, inter), dtype=torch.bfloat16, device=dev) if keep_h else None
     q, s = _u8((rows, inter // 2), dev), _u8((rows, inter // 16), dev)
     t = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -455,6 +632,12 @@ def moe_swiglu_quantize_nvfp4(gate_up: torch.Tensor, keep_h: bool = True):
 def moe_combine(o_slots: torch.Tensor, slot_of: torch.Tensor, weights: torch.Tensor, out=None):
     T, k = slot_of.shape
     H = o_slots.shape[1]
+    c = _Checks(o_slots.device)
+    c.need(o_slots, "o_slots", torch.float32, tuple(o_slots.shape))
+    c.need(slot_of, "slot_of", torch.int64, (T, k))
+    c.need(weights, "weights", torch.float32, (T, k))
+    c.opt(out, "out", torch.float32, (T, H))
+    c.done()
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=o_slots.device)
     _check("moe_combine", lib().moe_combine(_ptr(o_slots), o_slots.shape[0], T, k, H, _ptr(slot_of), _ptr(weights),

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+
 #include "../../include/mxq.h"
 
 namespace mxq {
@@ -449,17 +450,22 @@ mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K, const void* A
                                   const void* sB, float* C, int64_t ldc, void* stream) {
   if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (!A || !sA || !B || !sB || !C) return MXQ_ERR_NULL;
-  if (K % 32 || ldc < N) return MXQ_ERR_SHAPE;
+  if (K % 32 || K > kMaxGemmK || ldc < N) return MXQ_ERR_SHAPE;
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   if (M == 0 || N == 0) return MXQ_OK;
   return hip_status(mxq::launch_gemm(6, M, N, K, A, sA, nullptr, 0, B, sB, nullptr, 0, C, ldc, S(stream)));
 }
 
-mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64_t* offsets, int vary_k,
-                                     int64_t total, int64_t M, int64_t N, int64_t K, const int32_t* a_row_index,
-                                     int64_t a_rows, const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
-                                     const void* B, const void* sB, const float* tB, mxq_scope tB_scope, float* C,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by both grouped entry points; on MXQ_OK, *empty says the call has
+// no work and *ta / *tb hold the decode-scale modes.
+mxq_status grouped_check(mxq_format fmt, int64_t groups, const int64_t* offsets, int vary_k, int64_t total,
+                         int64_t M, int64_t N, int64_t K, const int32_t* a_row_index, int64_t a_rows, const void* A,
+                         const void* sA, const float* tA, mxq_scope tA_scope, const void* B, const void* sB,
+                         const float* tB, mxq_scope tB_scope, const float* C, bool* empty, int* ta, int* tb) {
   if (groups < 0 || total < 0 || M < 0 || N < 0 || K < 0 || a_rows < 0) return MXQ_ERR_SHAPE;
   if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4) return MXQ_ERR_FORMAT;
   if (vary_k != 0 && vary_k != 1) return MXQ_ERR_FORMAT;
@@ -467,13 +473,14 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
   if (vary_k && a_row_index) return MXQ_ERR_FORMAT;
   if (!offsets || !A || !B || !C) return MXQ_ERR_NULL;
   if (fmt != MXQ_BF16 && (!sA || !sB)) return MXQ_ERR_NULL;
-  int ta = -1, tb = -1;
+  *ta = -1;
+  *tb = -1;
   if (fmt == MXQ_NVFP4) {
     if (!tA || !tB) return MXQ_ERR_NULL;
-    ta = scope_mode(tA_scope);
-    tb = scope_mode(tB_scope);
-    if (ta != 0 && ta != 1) return MXQ_ERR_FORMAT;
-    if (tb != 0 && tb != 2) return MXQ_ERR_FORMAT;    // per B row, or per group (expert)
+    *ta = scope_mode(tA_scope);
+    *tb = scope_mode(tB_scope);
+    if (*ta != 0 && *ta != 1) return MXQ_ERR_FORMAT;
+    if (*tb != 0 && *tb != 2) return MXQ_ERR_FORMAT;    // per B row, or per group (expert)
   }
   if (!vary_k) {
     if (fmt != MXQ_BF16 && K % 32) return MXQ_ERR_SHAPE;
@@ -485,7 +492,24 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
     if (total > kMaxGemmK) return MXQ_ERR_SHAPE;
   }
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
-  if (groups == 0 || N == 0 || (vary_k ? M == 0 : total == 0)) return MXQ_OK;
+  *empty = groups == 0 || N == 0 || (vary_k ? M == 0 : total == 0);
+  return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64_t* offsets, int vary_k,
+                                     int64_t total, int64_t M, int64_t N, int64_t K, const int32_t* a_row_index,
+                                     int64_t a_rows, const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
+                                     const void* B, const void* sB, const float* tB, mxq_scope tB_scope, float* C,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int ta = -1, tb = -1;
+  const mxq_status st = grouped_check(fmt, groups, offsets, vary_k, total, M, N, K, a_row_index, a_rows, A, sA, tA,
+                                      tA_scope, B, sB, tB, tB_scope, C, &empty, &ta, &tb);
+  if (st != MXQ_OK || empty) return st;
   if (!workspace || workspace_bytes < mxq::grouped_gemm_ws_bytes(groups)) return MXQ_ERR_WORKSPACE;
   if (!al16(workspace)) return MXQ_ERR_ALIGN;
   return hip_status(mxq::launch_grouped_gemm((int)fmt, groups, offsets, vary_k, total, M, N, K, a_row_index,

@@ -285,18 +285,63 @@ hipError_t launch_dequant_t(int fmt, const void* q, const void* s, const float* 
 
 // ---------------------------------------------------------------------------
 // SwiGLU + per-row NVFP4: one wave per slot row; the row stays in registers.
-// h = silu(g) * u = g / (1 + exp(-g)) * u in binary32, rounded to BF16, then the
-// per-token quantizer's arithmetic on the BF16 row.
+// h = silu(g) * u = g u / (1 + e^(-g)), rounded once to BF16 (nearest, ties to even)
+// from its exact value, then the per-token quantizer's arithmetic on the BF16 row.
 // ---------------------------------------------------------------------------
-// g >= -80: exp(-g) through the hardware base-2 exponential (relative error ~|g| 2^-24,
-// far below the BF16 rounding of h; for large g it underflows to 0, which leaves h = g u
-// as the exact value rounds), the division correctly rounded.
-// g < -80: exp(-g) nears the binary32 overflow (at g = -88.7) and exp(g) would lose its
-// precision as a denormal, so h = g e^g u (1 + e^g rounds to 1) is formed as
-// -sign(u) exp(g + ln|g| + ln|u|) with the accurate functions.
-__device__ __forceinline__ float swiglu1(float g, float u) {
-  if (g >= -80.0f) return g / (1.0f + __expf(-g)) * u;
-  return copysignf(expf(g + logf(-g) + logf(fabsf(u))), -u);
+// binary64 -> BF16 bits, one rounding: the binary32 conversion is turned into
+// round-to-odd (an inexact result is truncated toward zero and gets its last bit set),
+// and round-to-odd to 24 bits followed by nearest-even to 8 bits equals nearest-even
+// to 8 bits directly (24 >= 8 + 2). Values past the binary32 range come out as
+// FLT_MAX | 1 and then round to +-Inf, values below its subnormals as +-2^-149 and
+// then to a signed zero, as the direct rounding gives.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
+  float f = (float)d;
+  if ((double)f != d) {
+    uint32_t b = __float_as_uint(f);
+    if (fabs((double)f) > fabs(d)) b -= 1u;          // magnitude rounded up: step back
+    f = __uint_as_float(b | 1u);
+  }
+  return f32_to_bf16_rne(f);
+}
+
+// h in binary64 from P = g u (exact: two 24-bit significands):
+//   g >= 0: h = P - C with C = P e / (1 + e), e = e^(-g) <= 1 (so C <= P / 2);
+//   g <  0: h = P e / (1 + e) with e = e^g < 1 (a vanishing e gives a zero with the
+//           sign of P, which is how the exact value, below 1e-300 in magnitude, rounds).
+// Either way h is within a few binary64 ulps of the exact value, so its BF16 rounding is
+// the correctly rounded one, except when h itself lands on a BF16 rounding midpoint.
+// For g > 0 that happens systematically, not by accident: once C drops below half an
+// ulp of P (g above ~37), h = P, and a product of two binary32 values is often a BF16
+// midpoint. The exact value is P - C_exact with C_exact > 0, so its side of the midpoint
+// is the sign of (|P| - |h|) - |C| (the first difference is exact): the magnitude rounds
+// up only if that is positive, else toward zero -- also when C underflowed to 0, since
+// the exact value stays strictly inside |P|. For g <= 0 a midpoint can only be hit by
+// chance (about 2^-44 per element); it then rounds to even.
+__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+  const double gd = g, P = (double)g * (double)u;
+  double h, C = 0.0;
+  if (gd >= 0.0) {
+    const double e = exp(-gd);
+    C = P * (e / (1.0 + e));
+    h = C == 0.0 ? P : P - C;                          // keeps the sign of a zero P
+  } else {
+    const double e = exp(gd);
+    h = P * (e / (1.0 + e));
+  }
+  if (gd > 0.0 && h != 0.0) {
+    // is |h| a midpoint of the BF16 grid (quantum 2^(max(E, -126) - 7), |h| in [2^E, 2^(E+1)))?
+    const double a = fabs(h);
+    int E;
+    frexp(a, &E);                                      // a = f 2^E, f in [0.5, 1)
+    const double q = ldexp(1.0, (E - 1 > -126 ? E - 1 : -126) - 7);
+    const double t = a / q, lo = floor(t);             // both exact: q is a power of two
+    if (t - lo == 0.5) {
+      const bool up = (fabs(P) - a) > fabs(C);         // |P| - |h| is exact (Sterbenz)
+      const double r = (up ? lo + 1.0 : lo) * q;       // a BF16 value (or 2^128)
+      return f32_to_bf16_rne((float)copysign(r, h));   // exact conversions
+    }
+  }
+  return f64_to_bf16_rne(h);
 }
 
 template <int CH>
@@ -317,10 +362,10 @@ swiglu_nvfp4_kernel(const float* __restrict__ gu, int64_t rows, int64_t inter, u
     if (e < inter) {
       const float4 g0 = load_stream16f(g + e), g1 = load_stream16f(g + e + 4);
       const float4 u0 = load_stream16f(u + e), u1 = load_stream16f(u + e + 4);
-      p[0] = f32_to_bf16_rne(swiglu1(g0.x, u0.x)) | (f32_to_bf16_rne(swiglu1(g0.y, u0.y)) << 16);
-      p[1] = f32_to_bf16_rne(swiglu1(g0.z, u0.z)) | (f32_to_bf16_rne(swiglu1(g0.w, u0.w)) << 16);
-      p[2] = f32_to_bf16_rne(swiglu1(g1.x, u1.x)) | (f32_to_bf16_rne(swiglu1(g1.y, u1.y)) << 16);
-      p[3] = f32_to_bf16_rne(swiglu1(g1.z, u1.z)) | (f32_to_bf16_rne(swiglu1(g1.w, u1.w)) << 16);
+      p[0] = swiglu_bf16(g0.x, u0.x) | (swiglu_bf16(g0.y, u0.y) << 16);
+      p[1] = swiglu_bf16(g0.z, u0.z) | (swiglu_bf16(g0.w, u0.w) << 16);
+      p[2] = swiglu_bf16(g1.x, u1.x) | (swiglu_bf16(g1.y, u1.y) << 16);
+      p[3] = swiglu_bf16(g1.z, u1.z) | (swiglu_bf16(g1.w, u1.w) << 16);
       if (h_out) {                                               // outputs leave with non-temporal stores
         const u32x4_nt h4 = {p[0], p[1], p[2], p[3]};
         __builtin_nontemporal_store(h4, reinterpret_cast<u32x4_nt*>(h_out + row * inter + e));

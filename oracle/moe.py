@@ -72,7 +72,7 @@ def _swiglu_exact_above(g: float, u: float, mid: float) -> bool:
     |g u| times 1/(1 + e^(-g)) < 1, i.e. strictly below, so the answer is False."""
     gd, ud = Decimal(g), Decimal(u)
     h = _DEC.divide(_DEC.multiply(gd, ud), _DEC.add(Decimal(1), _DEC.exp(_DEC.minus(gd))))
-    return _DEC.compare(abs(h), Decimal(mid)) > 0
+    return _DEC.compare(h.copy_abs(), Decimal(mid)) > 0            # copy_abs: no rounding
 
 
 def swiglu_bf16_ref(gate_up_f32: np.ndarray) -> np.ndarray:

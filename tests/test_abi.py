@@ -229,3 +229,51 @@ def test_fp8_block_batch_validation():
     assert call(prob(ldc=64)) == 2                                      # ldc < N
     assert call(prob(M=-1)) == 2
     assert call(prob(M=0), prob(N=0, A=None)) == 0                      # only empty problems: no-op
+
+
+def test_matrix_core_rejects_k_beyond_32bit_offsets():
+    f = B.lib().gemm_mxfp8_matrix_core
+    assert f(32, 32, (1 << 22) + 32, P, P, P, P, P, 32, None) == 2      # K > 2^22
+    assert f(32, 32, 48, P, P, P, P, P, 32, None) == 2                  # K % 32
+
+
+def test_binding_rejects_mismatched_buffers_before_any_call():
+    """The Python binding checks every operand, scale and output shape, dtype and layout on
+    the host (CPU tensors here: the shape checks run before the device check, and no
+    library call is reached)."""
+    import torch
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    A, sA, Bq, sB = u8(64, 128), u8(64, 4), u8(32, 128), u8(32, 4)
+    with pytest.raises(ValueError, match="out: shape"):
+        B.gemm_block_scaled(B.MXFP8, A, sA, Bq, sB, out=f32(64, 16))          # undersized output
+    with pytest.raises(ValueError, match="B: shape"):
+        B.gemm_block_scaled(B.MXFP8, A, sA, u8(32, 96), u8(32, 3))            # B narrower than A's K
+    with pytest.raises(ValueError, match="sB: shape"):
+        B.gemm_block_scaled(B.MXFP8, A, sA, Bq, u8(32, 2))                    # short scale matrix
+    with pytest.raises(ValueError, match="contiguous"):
+        B.gemm_block_scaled(B.MXFP8, u8(128, 64).t(), sA, Bq, sB)             # strided operand
+    with pytest.raises(ValueError, match="dtype"):
+        B.gemm_block_scaled(B.BF16, A, None, Bq, None)                        # BF16 format, uint8 data
+    with pytest.raises(ValueError, match="tA"):
+        B.gemm_block_scaled(B.NVFP4, u8(64, 64), u8(64, 8), u8(32, 64), u8(32, 8), tA=f32(63), tB=f32(1))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.gemm_block_scaled(B.MXFP8, A, sA, Bq, sB, out=f32(64, 32))          # right shapes, host memory
+    with pytest.raises(ValueError, match="out: shape"):
+        B.gemm_block_scaled_batch(B.MXFP8, [dict(A=A, sA=sA, B=Bq, sB=sB, out=f32(32, 32)),
+                                            dict(A=A, sA=sA, B=Bq, sB=sB, out=f32(64, 32))])
+    with pytest.raises(ValueError, match="sB: shape"):
+        B.gemm_fp8_blockwise(u8(64, 256), f32(64, 2), u8(256, 256), f32(256, 2), b_blocks=True)
+    with pytest.raises(ValueError, match="out: shape"):
+        B.gemm_mxfp8_matrix_core(A, sA, Bq, sB, out=f32(64, 31))
+    off = torch.tensor([0, 32, 64], dtype=torch.int64)
+    with pytest.raises(ValueError, match="B: shape"):
+        B.grouped_gemm_block_scaled(B.BF16, off, torch.zeros(64, 128, dtype=torch.bfloat16),
+                                    torch.zeros(1, 16, 128, dtype=torch.bfloat16), N=16, K=128, total=64)
+    with pytest.raises(ValueError, match="out: shape"):
+        B.grouped_gemm_block_scaled(B.BF16, off, torch.zeros(64, 128, dtype=torch.bfloat16),
+                                    torch.zeros(2, 16, 128, dtype=torch.bfloat16), N=16, K=128, total=64,
+                                    out=f32(64, 8))
+    with pytest.raises(ValueError, match="q_colT: shape"):
+        B.quantize_mxfp8_multi([torch.zeros(64, 64, dtype=torch.bfloat16)], [(u8(64, 64), u8(64, 2), u8(32, 64),
+                                                                             u8(64, 2))])

@@ -64,3 +64,24 @@ def test_algorithmic_bytes_per_element():
     assert bench.FP8B_ACT == 4.0625                       # 2 read + 1 + 1 + 2 * 4/128
     assert bench.HBM_PEAK_GBPS == 8000.0
     assert bench.MFMA_PEAK_TFLOPS == {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
+def test_cpu_baseline_row_chunks_equal_the_whole_tensor_oracle():
+    """The thread-pool CPU baseline splits the oracle's work into row (or column) chunks;
+    the bytes must be those of one whole-tensor call."""
+    import numpy as np
+
+    import bench
+    from microscaling_precision_quantization_amd import inputs
+    from oracle import mxfp8 as omx
+    from oracle import nvfp4 as onv
+    g = np.random.default_rng(5)
+    x = inputs.to_bf16_bits(g.standard_normal((96, 64)) * np.exp(g.standard_normal((96, 1))))
+    for a, b in zip(bench.rows_parallel(omx.quantize_rowwise, x), omx.quantize_rowwise(x)):
+        assert np.array_equal(a, b)
+    for a, b in zip(bench.mx_colwise_parallel(omx, x), omx.quantize_colwise(x)):
+        assert np.array_equal(a, b)
+    for a, b in zip(bench.rows_parallel(onv.quantize_per_token, x), onv.quantize_per_token(x)):
+        assert np.array_equal(a, b)
+    for a, b in zip(bench.nv_group_parallel(onv, x, 32), onv.quantize_per_group(x, [0, 32, 64, 96])):
+        assert np.array_equal(a, b)

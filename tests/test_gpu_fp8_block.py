@@ -202,7 +202,16 @@ def test_gemm_batch_rejects_bad_descriptors_before_launch():
     out = torch.full((128, 128), 3.0, device="cuda")
     good = dict(A=qa, sA=sa, B=qa, sB=sa, b_blocks=False, out=out)
     bad = dict(A=qa[:, :200], sA=sa, B=qa[:, :200], sB=sa, b_blocks=False, out=torch.empty((128, 128), device="cuda"))
-    with pytest.raises(mxq.MxqError):
-        mxq.gemm_fp8_blockwise_batch([good, bad])                 # K % 128 != 0
+    with pytest.raises(ValueError):                               # the binding refuses it first
+        mxq.gemm_fp8_blockwise_batch([good, bad])
+    # the C ABI itself, handed the same descriptors directly: K % 128 != 0 in the second
+    # one fails the whole call before anything is launched
+    from microscaling_precision_quantization_amd import binding as B
+    arr = (B._Fp8BlockProblem * 2)()
+    for i, (q, K) in enumerate(((good, 256), (bad, 200))):
+        arr[i] = B._Fp8BlockProblem(128, 128, K, q["A"].data_ptr(), q["sA"].data_ptr(), q["B"].data_ptr(),
+                                    q["sB"].data_ptr(), 0, q["out"].data_ptr(), 128)
+    status = B.lib().gemm_fp8_blockwise_batch(B.ctypes.cast(arr, B.ctypes.c_void_p), 2, B._stream(qa.device))
+    assert status == 2                                            # MXQ_ERR_SHAPE
     torch.cuda.synchronize()
     assert np.all(host(out) == 3.0)                               # nothing ran

@@ -118,9 +118,9 @@ def test_moe_layer_forward_and_dequantized_backward(pad):
         if hi > lo:
             assert_gemm_close(gu[lo:hi], ref[lo:hi], f"gate_up expert {e}")
     assert np.all(gu[~live] == 0.0)
-    # A11: SwiGLU (<= 1 BF16 ulp) + per-row requant of the device's h (bit-exact)
-    h = host(m.h)
-    assert np.max(omoe.bf16_ulp_distance(h, omoe.swiglu_bf16_ref(gu))) <= 1
+    # A11: SwiGLU (correctly rounded BF16) + per-row requant, from the device's FP32 gate/up
+    h = omoe.swiglu_bf16_ref(gu)
+    assert_bytes_equal(host(m.h), h, "h")
     eq, es, et = onv.quantize_per_token(h)
     assert_bytes_equal(host(m.qh), eq, "h packed")
     assert_bytes_equal(host(m.th).view(np.uint32), et.view(np.uint32), "h scales")
@@ -189,7 +189,7 @@ def test_shared_expert_bf16_forward_backward():
     gu = host(sh.gu)
     assert_gemm_close(gu, f64(x) @ f64(w_sgu).T, "shared gate_up")
     h = host(sh.h)
-    assert np.max(omoe.bf16_ulp_distance(h, omoe.swiglu_bf16_ref(gu))) <= 1
+    assert_bytes_equal(h, omoe.swiglu_bf16_ref(gu), "shared h")
     assert_gemm_close(host(sh.o), f64(h) @ f64(w_sd).T, "shared down")
     assert_gemm_close(host(sh.dh), f64(d_o) @ f64(w_sd), "shared down dgrad")
     assert_gemm_close(host(sh.dw_sd), f64(d_o).T @ f64(h), "shared down wgrad")
@@ -229,9 +229,14 @@ def check_moe_sampled(m, r, x_bits, w_gu_bits_of, w_d_bits_of, experts, tokens, 
         a[rows >= 0] = xh[rows[rows >= 0]]
         gu = host(m.gu[lo:hi])
         assert_gemm_close(gu, a @ onv.dequantize_exact(gq, gs, np.repeat(gt, 2 * I)).T, f"{what} gate_up[{e}]")
+        h_ref = omoe.swiglu_bf16_ref(gu)                       # from the device's FP32 gate/up
         if m.h is not None:
-            assert np.max(omoe.bf16_ulp_distance(host(m.h[lo:hi]), omoe.swiglu_bf16_ref(gu))) <= 1
+            assert_bytes_equal(host(m.h[lo:hi]), h_ref, f"{what} h[{e}]")
         hq, hs, ht = host(m.qh[lo:hi]), host(m.sh[lo:hi]), host(m.th[lo:hi])
+        eq, es, et = onv.quantize_per_token(h_ref)
+        assert_bytes_equal(hq, eq, f"{what} h[{e}] packed")
+        assert_bytes_equal(hs, es, f"{what} h[{e}] block scales")
+        assert_bytes_equal(ht.view(np.uint32), et.view(np.uint32), f"{what} h[{e}] scales")
         o = host(m.o[lo:hi])
         assert_gemm_close(o, onv.dequantize_exact(hq, hs, ht) @ onv.dequantize_exact(dq, ds, np.repeat(dt, H)).T,
                           f"{what} down[{e}]")
@@ -306,7 +311,7 @@ def test_moe_deepseek_full_size_sampled():
     gu = host(sh.gu[torch.from_numpy(tokens).cuda()])
     assert_gemm_close(gu, f64(xb[tokens]) @ f64(wsgu).T, "shared gate_up (sampled rows)")
     h = host(sh.h)
-    assert np.max(omoe.bf16_ulp_distance(h[tokens], omoe.swiglu_bf16_ref(gu))) <= 1
+    assert_bytes_equal(h[tokens], omoe.swiglu_bf16_ref(gu), "shared h (sampled rows)")
     assert_gemm_close(host(sh.o[torch.from_numpy(tokens).cuda()]), f64(h[tokens]) @ f64(wsd).T, "shared down")
     d_os, d_gus = host(t["d_os"]), host(t["d_gus"])
     assert_gemm_close(host(sh.dw_sd), f64(d_os).T @ f64(h), "shared down wgrad")

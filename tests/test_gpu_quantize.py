@@ -394,3 +394,78 @@ def test_dequantize_mxfp8_and_nvfp4():
     b16 = host(mxq.dequantize(mxq.NVFP4, q, s, t, t_scope="group", group_rows=32))
     t_rows = np.repeat(host(t), 32)
     assert_bytes_equal(b16, onv.dequantize_bf16_bits(host(q), host(s), t_rows), "nvfp4 group -> bf16")
+
+
+# -------------------- scope-scale overflow (FLT_MAX) branches --------------------
+
+def subnormal_scope_rows(g, rows=32, cols=256):
+    """Rows whose every value is a BF16 subnormal (|x| <= 127 * 2^-133), so every scope
+    amax A is below 2688 / FLT_MAX: s_enc overflows to FLT_MAX and r_b clamps to FLT_MAX.
+    Row 0 is the hand-worked token [2^-127, -2^-128, 3 * 2^-129, 0 ...]."""
+    v = g.integers(-127, 128, (rows, cols))                  # value v * 2^-133: BF16 bits |v| (+ sign)
+    xb = (np.abs(v) | np.where(v < 0, 0x8000, 0)).astype(np.uint16)
+    xb[0] = 0
+    xb[0, :3] = [0x0040, 0x8020, 0x0030]
+    xb[1, :] = 0x0001                                        # the smallest subnormal everywhere
+    xb[2, 16:] = 0                                           # one subnormal block, zeros after
+    return xb
+
+
+def test_nvfp4_scope_overflow_branch_per_token():
+    xb = subnormal_scope_rows(inputs.rng(96, 0))
+    q, s, t = check_token(xb, what="subnormal tokens")
+    # the hand-worked values of the oracle pin, on the device
+    assert host(t).view(np.uint32)[0] == 0x00200000
+    assert list(host(s)[0, :2]) == [0x2B, 0x00] and list(host(q)[0, :2]) == [0xA4, 0x03]
+
+
+def test_nvfp4_scope_overflow_branch_tensor_group_and_2d():
+    xb = subnormal_scope_rows(inputs.rng(96, 1), rows=64, cols=512)
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="tensor")
+    eq, es, et = onv.quantize_per_tensor(xb)
+    assert host(t).view(np.uint32)[0] == 0x00200000 == et.view(np.uint32)[0]
+    assert_bytes_equal(host(q), eq, "subnormal tensor packed")
+    assert_bytes_equal(host(s), es, "subnormal tensor scales")
+    # group scope: one group of subnormals beside a group of ordinary values
+    wb = np.concatenate([xb[:32], inputs.normal_bf16(inputs.rng(96, 2), (32, 512), 0.02)])
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(wb), scope="group", group_rows=32)
+    eq, es, et = onv.quantize_per_group(wb, [0, 32, 64])
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "subnormal group t")
+    assert_bytes_equal(host(q), eq, "subnormal group packed")
+    assert_bytes_equal(host(s), es, "subnormal group scales")
+    # transposed (columnwise) blocking of the same subnormal tensor
+    q, s, t = mxq.quantize_nvfp4(dev_bf16(xb), scope="tensor", transpose=True)
+    eq, es, et = onv.quantize_per_tensor(np.ascontiguousarray(xb.T))
+    assert_bytes_equal(host(q), eq, "subnormal colwise packed")
+    assert_bytes_equal(host(t).view(np.uint32), et.view(np.uint32), "subnormal colwise t")
+    # 2D 16x16 blocks
+    qr, sr, qc, sc, t2 = mxq.quantize_nvfp4_2d(dev_bf16(xb), scope="tensor")
+    eq, es, eqT, esT, et2 = onv.quantize_2d(xb)
+    assert_bytes_equal(host(qr), eq, "subnormal 2d packed")
+    assert_bytes_equal(host(qc), eqT, "subnormal 2d transposed")
+    assert_bytes_equal(host(t2).view(np.uint32), et2.view(np.uint32), "subnormal 2d t")
+
+
+# --------------------- run-twice determinism of the atomics ---------------------
+
+def test_nvfp4_scope_maxima_are_deterministic_across_runs():
+    """The tensor / group / 2D quantizers reduce their scope maxima with device atomics;
+    a max is order-independent, so two runs (and a run on a freshly allocated
+    workspace) must give the same bytes."""
+    g = inputs.rng(97, 0)
+    G, N, K = 4, 256, 2048
+    wb = inputs.to_bf16_bits(g.standard_normal((G * N, K)) * np.exp2(g.integers(-6, 6, (G * N, 1))))
+    x = dev_bf16(wb)
+    runs = []
+    for _ in range(3):
+        runs.append([host(a) for a in mxq.quantize_nvfp4(x, scope="tensor")]
+                    + [host(a) for a in mxq.quantize_nvfp4(x, scope="group", group_rows=N)]
+                    + [host(a) for a in mxq.quantize_nvfp4_2d(x, scope="group", group_rows=N)]
+                    + [host(a) for a in mxq.quantize_nvfp4(x, scope="tensor", transpose=True,
+                                                           rht_signs=[1, -1] * 8)])
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    eq, es, et = onv.quantize_per_group(wb, np.arange(G + 1) * N)
+    assert_bytes_equal(runs[0][3], eq, "group packed")
+    assert_bytes_equal(runs[0][5].view(np.uint32), et.view(np.uint32), "group t")

@@ -59,10 +59,13 @@ def test_swiglu_correct_rounding_hand_worked():
     # neighbours 258 (0x4381) and 260 (0x4382, the even one), but the real value is
     # 259 / (1 + e^-g), strictly below 259, so it rounds down to 258 (for g = 37 the FP64
     # 1 + e^-37 already rounds to 1). g = -1000: -1000 e^-1000 underflows to -0.
-    gu = np.zeros((1, 10), dtype=np.float32)
-    gu[0, :5] = [1.0, 0.0, 259.0, 37.0, -1000.0]
-    gu[0, 5:] = [1.0, 5.0, 1.0, 7.0, 1.0]
-    assert list(moe.swiglu_bf16_ref(gu)[0]) == [0x3F3B, 0x0000, 0x4381, 0x4381, 0x8000]
+    # g = 790, u = 2^-38: g u = 790 2^-38 is the midpoint of 0x3145 and 0x3146 and e^-790
+    # underflows binary64, yet the exact value is below it: 0x3145. Zeros carry the sign of
+    # g u (g = 0, u = -5 and g = 1, u = -0 give -0).
+    gu = np.zeros((1, 16), dtype=np.float32)
+    gu[0, :8] = [1.0, 0.0, 259.0, 37.0, -1000.0, 790.0, 0.0, 1.0]
+    gu[0, 8:] = [1.0, 5.0, 1.0, 7.0, 1.0, 2.0 ** -38, -5.0, -0.0]
+    assert list(moe.swiglu_bf16_ref(gu)[0]) == [0x3F3B, 0x0000, 0x4381, 0x4381, 0x8000, 0x3145, 0x8000, 0x8000]
 
 
 def _bf16_rne_rational(v):
@@ -95,10 +98,12 @@ def test_swiglu_matches_arbitrary_precision_brute_force():
     odd = 2 * g.integers(128, 256, 60) + 1                 # 257 .. 511
     # g u on a BF16 midpoint: g = 32 or 64 with u = odd 2^-6 or 2^-7 (g u = odd / 2 in
     # [128, 256), quantum 1), and odd g in [257, 511] with u = 1 (quantum 2)
+    # (and integer g in [700, 880] with power-of-two u: g u on a midpoint, e^-g below binary64)
+    big = 4 * g.integers(175, 220, 30) + 2                 # 10-bit integers ending in 10: midpoints
     gate = np.concatenate([g.standard_normal(n) * 4, np.full(20, 32.0), np.full(20, 64.0), odd[40:].astype(float),
-                           -g.uniform(80, 95, 50)])
+                           -g.uniform(80, 95, 50), big.astype(float)])
     up = np.concatenate([g.standard_normal(n) * 3, odd[:20] * 2.0 ** -6, odd[20:40] * 2.0 ** -7, np.ones(20),
-                         g.standard_normal(50) * 1e-3])
+                         g.standard_normal(50) * 1e-3, np.exp2(g.integers(-40, 40, 30).astype(float))])
     gu = np.concatenate([gate, up]).astype(np.float32).reshape(1, -1)
     got = F.bf16_bits_to_f32(moe.swiglu_bf16_ref(gu))[0].astype(np.float64)
     m = len(gate)

@@ -317,7 +317,7 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
 // up only if that is positive, else toward zero -- also when C underflowed to 0, since
 // the exact value stays strictly inside |P|. For g <= 0 a midpoint can only be hit by
 // chance (about 2^-44 per element); it then rounds to even.
-__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+__device__ __noinline__ uint32_t swiglu_bf16_f64(float g, float u) {
   const double gd = g, P = (double)g * (double)u;
   double h, C = 0.0;
   if (gd >= 0.0) {
@@ -342,6 +342,26 @@ __device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
     }
   }
   return f64_to_bf16_rne(h);
+}
+
+// The same BF16 value, mostly from binary32: for |g| <= 80, h32 = (g / (1 + e^-g)) u
+// with the accurate expf and correctly rounded division is within 2^-21 of h relative
+// (a few roundings of 2^-24 each and the exponential's error), i.e. within 8 binary32
+// ulps. Where h32 is a normal number more than 64 ulps away from every BF16 rounding
+// midpoint (its 16 bits below the BF16 precision differ from 0x8000 by more than 64),
+// the exact h lies on the same side of every midpoint, so rounding h32 gives the
+// correctly rounded BF16 value; everything else (about 1 element in 500, plus the
+// large gates, infinities and tiny values) takes the binary64 path above.
+__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+  if (fabsf(g) <= 80.0f) {
+    const float h = g / (1.0f + expf(-g)) * u;
+    const uint32_t b = __float_as_uint(h);
+    const uint32_t mag = b & 0x7FFFFFFFu;
+    const int32_t lowd = (int32_t)(b & 0xFFFFu) - 0x8000;
+    if (mag >= 0x0D800000u && mag < 0x7F000000u && (lowd > 64 || lowd < -64))   // 2^-100 <= |h32| < 2^127
+      return f32_to_bf16_rne(h);
+  }
+  return swiglu_bf16_f64(g, u);
 }
 
 template <int CH>

@@ -527,6 +527,31 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
                                      float* C, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * grouped_gemm_block_scaled_noalloc -- grouped_gemm_block_scaled without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid allocation.
+ *   Same operation, arguments (minus workspace), checks and bytes of C as
+ *   grouped_gemm_block_scaled: the same kernels run; only the scratch of the device
+ *   tile scheduler ((groups + 1) int64 tile offsets, rewritten in full by every call)
+ *   lives in a static device array of the library, one per GPU, held until the
+ *   process ends (64 KiB).
+ *   groups <= MXQ_NOALLOC_MAX_GROUPS, else MXQ_ERR_WORKSPACE (nothing launched).
+ *   The array of the CURRENT device (hipGetDevice) is used: `stream` must belong to
+ *   it. Its address is looked up on the first call on each device (MXQ_ERR_HIP if
+ *   that fails). No call allocates or frees.
+ *   Every call on one GPU shares that GPU's array: calls that can overlap on one GPU
+ *   (different streams, or several host threads) race on it and must be ordered by
+ *   the caller; calls on one stream are ordered by the stream.
+ * ------------------------------------------------------------------------- */
+#define MXQ_NOALLOC_MAX_GROUPS 8191
+mxq_status grouped_gemm_block_scaled_noalloc(mxq_format fmt, int64_t groups, const int64_t* offsets,
+                                             int vary_k, int64_t total, int64_t M, int64_t N, int64_t K,
+                                             const int32_t* a_row_index, int64_t a_rows,
+                                             const void* A, const void* sA, const float* tA, mxq_scope tA_scope,
+                                             const void* B, const void* sB, const float* tB, mxq_scope tB_scope,
+                                             float* C, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_swiglu_quantize_nvfp4 -- SwiGLU of the gate_up GEMM output followed by
  * per-row NVFP4 quantization of the result (input of the down projection).
  *   Defined by: SwiGLU experts whose gate and up projections enter one fused GEMM

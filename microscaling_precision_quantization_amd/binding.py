@@ -56,6 +56,9 @@ _SIGS = {
     "grouped_gemm_block_scaled": [_int, _i64, _c_void_p, _int, _i64, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p,
                                   _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p,
                                   _c_void_p, _size, _c_void_p],
+    "grouped_gemm_block_scaled_noalloc": [_int, _i64, _c_void_p, _int, _i64, _i64, _i64, _i64, _c_void_p, _i64,
+                                          _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p,
+                                          _int, _c_void_p, _c_void_p],
     "moe_swiglu_quantize_nvfp4": [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "moe_combine": [_c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "mxq_scale_bytes": [_int, _i64, _i64],
@@ -606,6 +609,25 @@ def grouped_gemm_block_scaled(fmt: int, offsets, A, B, N: int, K: int, sA=None, 
         else (A.shape[0] if a_row_index is not None else 0), _ptr(A), _ptr(sA), _ptr(tA),
         SCOPE[tA_scope], _ptr(B), _ptr(sB), _ptr(tB), SCOPE[tB_scope], _ptr(out), _ptr(workspace),
         workspace.numel(), _stream(dev)))
+    return out
+
+
+def grouped_gemm_block_scaled_noalloc(fmt: int, offsets, A, B, N: int, K: int, sA=None, sB=None, tA=None, tB=None,
+                                      tA_scope="row", tB_scope="group", a_row_index=None, vary_k=False, M: int = 0,
+                                      total: int | None = None, a_rows: int | None = None, out=None):
+    """grouped_gemm_block_scaled with the scheduler scratch in the library's static device
+    array (no workspace): for callers that cannot allocate. `out` must be given (this
+    call allocates nothing)."""
+    if out is None:
+        raise ValueError("out: the no-allocation call needs a preallocated output")
+    if total is None:
+        raise ValueError("total: pass it explicitly (reading it from the device offsets would synchronize)")
+    _grouped_args(fmt, offsets, A, B, N, K, sA, sB, tA, tB, tA_scope, tB_scope, a_row_index, vary_k, M, total,
+                  a_rows, out)
+    _check("grouped_gemm_block_scaled_noalloc", lib().grouped_gemm_block_scaled_noalloc(
+        fmt, offsets.numel() - 1, _ptr(offsets), int(vary_k), total, M, N, K, _ptr(a_row_index),
+        a_rows if a_rows is not None else (A.shape[0] if a_row_index is not None else 0), _ptr(A), _ptr(sA), _ptr(tA),
+        SCOPE[tA_scope], _ptr(B), _ptr(sB), _ptr(tB), SCOPE[tB_scope], _ptr(out), _stream(A.device)))
     return out
 
 

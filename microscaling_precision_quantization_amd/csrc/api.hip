@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/mxq.h"
 
@@ -496,6 +497,33 @@ mxq_status grouped_check(mxq_format fmt, int64_t groups, const int64_t* offsets,
   return MXQ_OK;
 }
 
+// Scratch of grouped_gemm_block_scaled_noalloc: the device-side tile prefix ((groups + 1)
+// int64, fully rewritten by every call before any tile reads it) lives in this
+// file-scope device array instead of a caller workspace. Each GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is looked up once per device
+// (hipGetSymbolAddress with that device current) and only that address is passed on.
+constexpr int64_t kNoAllocMaxGroups = MXQ_NOALLOC_MAX_GROUPS;
+__device__ __align__(256) int64_t scratch[kNoAllocMaxGroups + 1];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+mxq_status current_device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXQ_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MXQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -515,6 +543,27 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
   return hip_status(mxq::launch_grouped_gemm((int)fmt, groups, offsets, vary_k, total, M, N, K, a_row_index,
                                              a_row_index ? a_rows : total, A, sA,
                                              tA, ta, B, sB, tB, tb, C, workspace, S(stream)));
+}
+
+mxq_status grouped_gemm_block_scaled_noalloc(mxq_format fmt, int64_t groups, const int64_t* offsets, int vary_k,
+                                             int64_t total, int64_t M, int64_t N, int64_t K,
+                                             const int32_t* a_row_index, int64_t a_rows, const void* A,
+                                             const void* sA, const float* tA, mxq_scope tA_scope, const void* B,
+                                             const void* sB, const float* tB, mxq_scope tB_scope, float* C,
+                                             void* stream) {
+  bool empty = false;
+  int ta = -1, tb = -1;
+  const mxq_status st = grouped_check(fmt, groups, offsets, vary_k, total, M, N, K, a_row_index, a_rows, A, sA, tA,
+                                      tA_scope, B, sB, tB, tB_scope, C, &empty, &ta, &tb);
+  if (st != MXQ_OK) return st;
+  if (groups > kNoAllocMaxGroups) return MXQ_ERR_WORKSPACE;      // beyond the static scratch
+  if (empty) return MXQ_OK;
+  void* ws = nullptr;
+  const mxq_status ss = current_device_scratch(&ws);
+  if (ss != MXQ_OK) return ss;
+  return hip_status(mxq::launch_grouped_gemm((int)fmt, groups, offsets, vary_k, total, M, N, K, a_row_index,
+                                             a_row_index ? a_rows : total, A, sA,
+                                             tA, ta, B, sB, tB, tb, C, ws, S(stream)));
 }
 
 mxq_status moe_swiglu_quantize_nvfp4(const float* gate_up, int64_t rows, int64_t inter, void* h_bf16, void* q,

@@ -6,8 +6,7 @@ layer, the largest configuration that fits one GPU -- 16384 tokens, hidden 7168,
 256 routed experts (intermediate 2048, SwiGLU, top-8 of softmax(N(0,1) logits))
 with NVFP4 weights (one FP32 scale per expert matrix) and per-token NVFP4
 activations, plus one BF16 shared expert. One step = expert-weight quantization,
-the BF16 dequantization of the quantized weights for the backward, per-token
-quantization, the grouped NVFP4 forward GEMMs with SwiGLU + requantization and
+per-token quantization, the grouped NVFP4 forward GEMMs with SwiGLU + requantization and
 the combine, the dequantized-backward BF16 grouped GEMMs (dgrad and wgrad of both
 projections), and the shared expert forward + backward. Seeded synthetic data,
 resident in HBM before the timed region.
@@ -364,9 +363,10 @@ import numpy as np  # noqa: E402  (used by the oracle baselines above)
 
 class MoeDeepseek:
     """Routed NVFP4 experts + BF16 shared expert, forward and dequantized backward.
-    One step = expert-weight quantization (the weights change every training step)
-    and their transposed BF16 dequantization, the routed forward, the routed
-    dequantized backward GEMMs, and the shared expert's forward and backward."""
+    One step = expert-weight quantization (the weights change every training step),
+    the routed forward, the routed dequantized backward GEMMs (the dgrads build the
+    BF16 dequantized weights in their loader from the NVFP4 weights), and the shared
+    expert's forward and backward."""
     name = "moe_deepseek"
 
     def __init__(self, torch, dev):
@@ -397,7 +397,6 @@ class MoeDeepseek:
         n_w = G * 3 * H * I
         st = [Stage("quantize_nvfp4_expert_weights", lambda: m.quantize_weights(d["w_gu"], d["w_d"]),
                     n_w * NV_TENSOR, "hbm"),
-              Stage("dequantize_transposed", b.dequantize_weights, n_w * (0.5 + 1 / 16 + 2), "hbm"),
               Stage("quantize_nvfp4_per_token", lambda: m.quantize_tokens(self.x), T * H * NV_TOKEN + 4 * T, "hbm"),
               Stage("grouped_gemm_nvfp4_fwd", m.gate_up, self.fl["gate_up"], "mfma", "fp4", "fp16"),
               Stage("swiglu_quantize_nvfp4", m.swiglu, S * 2 * I * 4 + S * I * (0.5 + 1 / 16) + 4 * S, "hbm"),

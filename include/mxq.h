@@ -59,7 +59,9 @@ typedef enum {
   MXQ_ERR_HIP = 6        /* a HIP launch failed                                */
 } mxq_status;
 
-typedef enum { MXQ_MXFP8 = 1, MXQ_NVFP4 = 2, MXQ_BF16 = 3, MXQ_MXFP4 = 4 } mxq_format;
+/* MXQ_BF16_NVFP4T: grouped GEMMs only -- BF16 activations times the stacked NVFP4 expert
+ * weights of the forward pass, read transposed (see grouped_gemm_block_scaled). */
+typedef enum { MXQ_MXFP8 = 1, MXQ_NVFP4 = 2, MXQ_BF16 = 3, MXQ_MXFP4 = 4, MXQ_BF16_NVFP4T = 5 } mxq_format;
 typedef enum { MXQ_OUT_BF16 = 0, MXQ_OUT_F32 = 1 } mxq_out_dtype;
 
 /* Scope of an NVFP4 FP32 (second-level) scale.
@@ -515,6 +517,16 @@ mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K,
  *              with vary_k = 1 every offset is a multiple of 32 (MXFP8, MXFP4) or 8 (BF16).
  *              The device checks this before any tile runs; offsets that break it
  *              make the call a no-op that leaves C unwritten.
+ *   fmt = MXQ_BF16_NVFP4T (vary_k = 0, no a_row_index): the dequantized-backward dgrad
+ *     straight from the forward's quantized expert weights. A : BF16 (total_slots, K);
+ *     B : the stacked NVFP4 weights W_g (K, N) exactly as quantize_nvfp4 (GROUP scope,
+ *     group_rows = K) stores them for the forward GEMM -- packed (groups * K, N/2), E4M3
+ *     sB (groups * K, N/16), tB (groups) with tB_scope GROUP -- and used transposed:
+ *       C[s, n] = sum_k A[s, k] * RNE_bf16(fl32(fl32(q S) t_g))[k, n],
+ *     the same BF16 operand values dequantize_transposed writes, built in the GEMM loader
+ *     instead of being stored (remio.ai, section "La Compatibilidad ...": backward GEMMs
+ *     in BF16 on BF16 dequantizations of the exact forward operands). sA / tA unused.
+ *     Requires K % 8 == 0, N % 16 == 0 and K * N / 2 < 2^31.
  *   Limits     : K <= 2^22 (vary_k = 1: total <= 2^22); with a_row_index, a_rows times
  *              the bytes of one A row must stay below 2^31. MXQ_ERR_SHAPE otherwise.
  *   workspace: device scratch of mxq_workspace_bytes(MXQ_OP_GROUPED_GEMM, groups, 0, 0).

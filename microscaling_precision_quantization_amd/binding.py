@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
 MXFP8, NVFP4, BF16, MXFP4 = 1, 2, 3, 4
+BF16_NVFP4T = 5                    # grouped only: BF16 A x stacked NVFP4 weights (K, N) read transposed
 _PACKED4 = (NVFP4, MXFP4)          # formats with two elements per byte
 OUT_BF16, OUT_F32 = 0, 1
 SCOPE = {"row": 0, "token": 0, "tensor": 1, "group": 2}
@@ -550,6 +551,19 @@ def _grouped_args(fmt, offsets, A, B, N, K, sA, sB, tA, tB, tA_scope, tB_scope, 
     G = offsets.numel() - 1
     if G < 0:
         raise ValueError("offsets: needs groups + 1 entries")
+    if fmt == BF16_NVFP4T:
+        if vary_k or a_row_index is not None:
+            raise ValueError("BF16_NVFP4T: row-grouped only, no gather")
+        c.need(A, "A", torch.bfloat16, (total, K))
+        c.need(B.reshape(-1, B.shape[-1]) if B.dim() == 3 else B, "B", torch.uint8, (G * K, N // 2))
+        if sB is None or tB is None:
+            raise ValueError("BF16_NVFP4T: sB and tB (one FP32 scale per group) are required")
+        c.need(sB.reshape(-1, sB.shape[-1]) if sB.dim() == 3 else sB, "sB", torch.uint8, (G * K, N // 16))
+        c.need(tB, "tB", torch.float32, (G,))
+        if out is not None:
+            c.need(out, "out", torch.float32, (total, N))
+        c.done()
+        return
     if vary_k:
         if a_row_index is not None:
             raise ValueError("a_row_index is not supported with vary_k")

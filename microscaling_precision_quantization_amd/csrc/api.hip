@@ -468,8 +468,23 @@ mxq_status grouped_check(mxq_format fmt, int64_t groups, const int64_t* offsets,
                          const void* sA, const float* tA, mxq_scope tA_scope, const void* B, const void* sB,
                          const float* tB, mxq_scope tB_scope, const float* C, bool* empty, int* ta, int* tb) {
   if (groups < 0 || total < 0 || M < 0 || N < 0 || K < 0 || a_rows < 0) return MXQ_ERR_SHAPE;
-  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4) return MXQ_ERR_FORMAT;
+  if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4 && fmt != MXQ_BF16_NVFP4T)
+    return MXQ_ERR_FORMAT;
   if (vary_k != 0 && vary_k != 1) return MXQ_ERR_FORMAT;
+  if (fmt == MXQ_BF16_NVFP4T) {
+    // BF16 A x the stacked NVFP4 weights (groups, K, N), read transposed, one scale per group
+    if (vary_k || a_row_index) return MXQ_ERR_FORMAT;
+    if (!offsets || !A || !B || !C) return MXQ_ERR_NULL;
+    if (!sB || !tB) return MXQ_ERR_NULL;
+    if (scope_mode(tB_scope) != 2) return MXQ_ERR_FORMAT;
+    if (K % 8 || N % 16 || K > kMaxGemmK) return MXQ_ERR_SHAPE;
+    if (K * (N / 2) > 0x7FFFFFFF) return MXQ_ERR_SHAPE;  // one weight's bytes: 32-bit buffer offsets
+    if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
+    *ta = -1;
+    *tb = 2;
+    *empty = groups == 0 || N == 0 || total == 0;
+    return MXQ_OK;
+  }
   if (vary_k && fmt == MXQ_NVFP4) return MXQ_ERR_FORMAT;
   if (vary_k && a_row_index) return MXQ_ERR_FORMAT;
   if (!offsets || !A || !B || !C) return MXQ_ERR_NULL;
@@ -540,8 +555,8 @@ mxq_status grouped_gemm_block_scaled(mxq_format fmt, int64_t groups, const int64
   if (st != MXQ_OK || empty) return st;
   if (!workspace || workspace_bytes < mxq::grouped_gemm_ws_bytes(groups)) return MXQ_ERR_WORKSPACE;
   if (!al16(workspace)) return MXQ_ERR_ALIGN;
-  return hip_status(mxq::launch_grouped_gemm((int)fmt, groups, offsets, vary_k, total, M, N, K, a_row_index,
-                                             a_row_index ? a_rows : total, A, sA,
+  return hip_status(mxq::launch_grouped_gemm(fmt == MXQ_BF16_NVFP4T ? 7 : (int)fmt, groups, offsets, vary_k, total,
+                                             M, N, K, a_row_index, a_row_index ? a_rows : total, A, sA,
                                              tA, ta, B, sB, tB, tb, C, workspace, S(stream)));
 }
 
@@ -561,8 +576,8 @@ mxq_status grouped_gemm_block_scaled_noalloc(mxq_format fmt, int64_t groups, con
   void* ws = nullptr;
   const mxq_status ss = current_device_scratch(&ws);
   if (ss != MXQ_OK) return ss;
-  return hip_status(mxq::launch_grouped_gemm((int)fmt, groups, offsets, vary_k, total, M, N, K, a_row_index,
-                                             a_row_index ? a_rows : total, A, sA,
+  return hip_status(mxq::launch_grouped_gemm(fmt == MXQ_BF16_NVFP4T ? 7 : (int)fmt, groups, offsets, vary_k, total,
+                                             M, N, K, a_row_index, a_row_index ? a_rows : total, A, sA,
                                              tA, ta, B, sB, tB, tb, C, ws, S(stream)));
 }
 

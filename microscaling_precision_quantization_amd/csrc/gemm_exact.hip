@@ -74,6 +74,7 @@ template <> struct RowBytes<2> { static constexpr int v = 32; };    // NVFP4
 template <> struct RowBytes<3> { static constexpr int v = 32; };    // MXFP4
 template <> struct RowBytes<4> { static constexpr int v = 128; };   // blockwise FP8: one 128-K block per stage
 template <> struct RowBytes<5> { static constexpr int v = 128; };   // MXFP8 on the scaled FP8 MFMA: 128 K per stage
+template <> struct RowBytes<6> { static constexpr int v = 128; };   // BF16 A x BF16 B built from NVFP4 weights (LDS rows BF16)
 
 // Scale modes (SM):
 //   0  general: K tiles may end early; per stage, one direct load per row and scale
@@ -88,7 +89,7 @@ template <> struct RowBytes<5> { static constexpr int v = 128; };   // MXFP8 on 
 // Blockwise FP8 (LD 4): one FP32 scale per row and 128-K block, one dword load per row
 // and stage (SU 1, SZ 4) whatever SM is.
 template <int LD, int SM> struct ScaleDma {
-  static constexpr int SU = LD == 4 ? 1 : (LD == 0 || SM == 2) ? 0 : (SM == 1 ? 1 : 2);
+  static constexpr int SU = LD == 4 ? 1 : (LD == 0 || LD == 6 || SM == 2) ? 0 : (SM == 1 ? 1 : 2);
   static constexpr int SZ = LD == 4 ? 4 : (LD == 1 || LD == 3) ? (SM >= 1 ? 2 : 1) : (SM >= 1 ? 4 : 2);
 };
 
@@ -99,12 +100,12 @@ template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false>
 struct Cfg {
   // BF16 128 x 256 tiles at two workgroups per CU take 64-byte stages to fit half the LDS
   static constexpr int RB = (WIDE && LD != 0) ? 128 : (LD == 0 && OCC == 2 && BM + BN == 384) ? 64 : RowBytes<LD>::v;
-  static constexpr int BK = LD == 0 ? RB / 2 : (LD == 1 || LD == 4 || LD == 5) ? RB : 2 * RB;   // K per stage
+  static constexpr int BK = (LD == 0 || LD == 6) ? RB / 2 : (LD == 1 || LD == 4 || LD == 5) ? RB : 2 * RB;   // K per stage
   static constexpr int SBS = LD == 5 ? RB / 64 : RB / 32;                 // sub-blocks per stage
   static_assert(!WIDE || SM == 2, "wide stages need chunked scales");
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int SU = ScaleDma<LD, SM>::SU, SZ = ScaleDma<LD, SM>::SZ;
-  static constexpr bool CH = SM == 2 && LD != 0 && LD != 4;      // chunked scales
+  static constexpr bool CH = SM == 2 && LD != 0 && LD != 4 && LD != 6;      // chunked scales
   // stages per 16-byte scale chunk (16 blocks)
   static constexpr int SPC = (LD == 1 || LD == 3 || LD == 5) ? 16 / (BK / 32) : LD == 2 ? 16 / (BK / 16) : 4;
   // chunk loads per wave: 64 rows of 16 bytes each; rows past BM + BN (a 128 x 256 tile
@@ -116,7 +117,8 @@ struct Cfg {
   static constexpr int FREE = kLdsBytes / OCC - 2 * CH_HALF;
   static constexpr int NS_LDS = (4 * STAGE <= FREE) ? 4 : (3 * STAGE <= FREE ? 3 : 2);
   static constexpr int NS = (CH && NS_LDS > SPC + 1) ? SPC + 1 : NS_LDS;
-  static constexpr int IA = A_BYTES / 4096, IB = B_BYTES / 4096;  // 1 KiB wave instructions per wave
+  // 1 KiB wave instructions per wave (LD 6 builds its B tile through registers instead)
+  static constexpr int IA = A_BYTES / 4096, IB = LD == 6 ? 0 : B_BYTES / 4096;
   static constexpr int IS = SU * (BM + BN) / 256;                 // 64-row scale loads per wave
   static_assert(SU == 0 || (BM + BN) % 256 == 0, "per-stage scale loads need BM + BN a multiple of 256");
   static constexpr int TI = BM / 64, TJ = BN / 64;                // 32x32 MFMA tiles per wave
@@ -229,7 +231,7 @@ __device__ __forceinline__ void buf_dma16_group(v4i rs, const uint32_t* vo, uint
 
 template <int LD>
 __device__ __forceinline__ int64_t k_bytes(int64_t k) {
-  return LD == 0 ? k * 2 : (LD == 1 || LD == 4 || LD == 5) ? k : k / 2;
+  return (LD == 0 || LD == 6) ? k * 2 : (LD == 1 || LD == 4 || LD == 5) ? k : k / 2;
 }
 
 typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
@@ -339,7 +341,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   constexpr int NF = TI + TJ;                             // fragments per lane and sub-block
   constexpr int BS = LD == 4 ? 128 : (LD == 1 || LD == 3 || LD == 5) ? 32 : 16;   // elements per scale block
   constexpr int SEB = LD == 4 ? 4 : 1;                    // bytes per scale entry
-  constexpr int EPC = LD == 0 ? 8 : (LD == 1 || LD == 4 || LD == 5) ? 16 : 32;   // elements per 16-byte chunk
+  constexpr int EPC = (LD == 0 || LD == 6) ? 8 : (LD == 1 || LD == 4 || LD == 5) ? 16 : 32;   // elements per 16-byte chunk
   constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave (chunks aside)
   constexpr int R = CH ? lcm_int(SPC, NS) : NS;           // stages per unrolled round
   static_assert(R % NS == 0 && (!CH || R % SPC == 0), "round must cover whole slot and chunk cycles");
@@ -358,8 +360,8 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // per-row offsets; rows outside the tile's valid range read zeros.
   const v4i rsA = p.a_idx ? make_rsrc(p.A, (uint32_t)min(p.a_rows * ldA, (int64_t)0x7FFFFFFF))
                           : make_rsrc(p.A + (p.a_base + m0) * ldA, (uint32_t)(a_rows_tile * ldA));
-  const v4i rsB = make_rsrc(p.B + n0 * ldB, (uint32_t)(b_rows_tile * ldB));
-  uint32_t voA[IA], voB[IB];
+  const v4i rsB = LD == 6 ? rsA : make_rsrc(p.B + n0 * ldB, (uint32_t)(b_rows_tile * ldB));
+  uint32_t voA[IA], voB[IB > 0 ? IB : 1];
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int pos = (wave * IA + j) * 1024 + lane * 16;   // byte in the A tile
@@ -442,6 +444,110 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 
   const uint32_t lbase[4] = {lds_addr(lds0), lds_addr(lds1), lds_addr(lds2), lds_addr(lds3)};
 
+  // LD 6: the B tile is made from NVFP4 weight rows W[k][n] (E2M1 pairs along n, one E4M3
+  // scale per 16 n, one FP32 decode scale t for the whole group): B[n][k] =
+  // RNE_bf16(fl32(fl32(q S) t)), the dequantized weight transposed. Lane (kg, ng) of the
+  // 256 threads loads an 8 (k) x 8 (n) block per stage -- 8 rows of 4 bytes and their 8
+  // scale bytes -- into registers, and at the end of the stage writes its 8 n-rows of 8 k
+  // (one 16-byte chunk each, at the swizzled position the BF16 fragment reads expect) into
+  // the B area of the slot being filled. A quarter-wave covers 8 k groups x 2 n groups, so
+  // each 16-byte LDS write meets at most one other lane on its banks.
+  const int kb_ = (int)p.k_begin;
+  const int nk_ = ((int)p.k_end - kb_ + C::BK - 1) / C::BK;
+  constexpr bool NVT = LD == 6;
+  static_assert(!NVT || (BN == 256 && C::BK == 64 && C::SBS == 4 && TJ / 2 - 1 == 1),
+                "the NVFP4-transposed B path is laid out for 256 x 64 stages of four sub-blocks");
+  __amdgpu_buffer_rsrc_t rsB6, rsS6;
+  uint32_t voB6[NVT ? 8 : 1], voS6[NVT ? 8 : 1];
+  float t6 = 0.0f;
+  int64_t rowB6 = 0, rowS6 = 0;
+  const int kg6 = lane & 7, ng6 = wave * 8 + (lane >> 3);
+  if constexpr (NVT) {
+    rowB6 = p.ldb / 2;                                    // bytes per W row (p.ldb = N elements)
+    rowS6 = p.ldb / 16;
+    rsB6 = __builtin_amdgcn_make_buffer_rsrc((void*)p.B, (short)0, (int)min(p.k_end * rowB6, (int64_t)0x7FFFFFFF),
+                                             0x00020000);
+    rsS6 = __builtin_amdgcn_make_buffer_rsrc((void*)p.sB, (short)0, (int)min(p.k_end * rowS6, (int64_t)0x7FFFFFFF),
+                                             0x00020000);
+    // Columns at or past n_valid (N % 16 == 0: a lane's 8 columns all exist or none) read
+    // whatever in-range bytes follow, or zeros past the buffer; they only feed accumulator
+    // columns the epilogue never stores.
+    const int64_t n = n0 + 8 * ng6;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      voB6[j] = (uint32_t)((8 * kg6 + j) * rowB6 + n / 2);
+      voS6[j] = (uint32_t)((8 * kg6 + j) * rowS6 + n / 16);
+    }
+    t6 = p.tB[0];
+  }
+  // Two register buffers: the loads of tile t + 2 are in flight while tile t + 1's block is
+  // converted (at the start of stage t) and written to its slot.
+  uint32_t bq6[2][NVT ? 8 : 1], bs6[2][NVT ? 8 : 1];
+  uint32_t out6[8][NVT ? 4 : 1];                          // converted block: [n][k pair]
+  // register loads of B tile t into buffer BUF (rows at or past k_end, and tiles past the
+  // end, read zeros)
+  auto nvt_issue = [&](int t, auto BUF) {
+    if constexpr (NVT) {
+      constexpr int bf = decltype(BUF)::value;
+      const int k0 = kb_ + t * C::BK;
+      const bool past = t >= nk_;
+      const int so = (int)(past ? kOutOfRange : (uint32_t)(k0 * rowB6));
+      const int ss = (int)(past ? kOutOfRange : (uint32_t)(k0 * rowS6));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bq6[bf][j] = __builtin_amdgcn_raw_buffer_load_b32(rsB6, (int)voB6[j], so, 0);
+        bs6[bf][j] = __builtin_amdgcn_raw_buffer_load_b8(rsS6, (int)voS6[j], ss, 0);
+      }
+    }
+  };
+  // row J of the block in buffer BUF -> v6[J % 2][n], the FP32 dequantized values
+  float v6[2][NVT ? 8 : 1];
+  auto nvt_row = [&](auto BUF, auto J) {
+    if constexpr (NVT) {
+      constexpr int bf = decltype(BUF)::value, j = decltype(J)::value, r = j % 2;
+      const uint32_t w = bq6[bf][j];
+      const float Sb = __builtin_amdgcn_cvt_f32_fp8((int)bs6[bf][j], 0);   // exact E4M3 decode, no branch
+      const v2f_t e0 = e2m1x2_to_f32<0>(w), e1 = e2m1x2_to_f32<1>(w);
+      const v2f_t e2 = e2m1x2_to_f32<2>(w), e3 = e2m1x2_to_f32<3>(w);
+      v6[r][0] = (e0.x * Sb) * t6; v6[r][1] = (e0.y * Sb) * t6;        // q S exact, then * t
+      v6[r][2] = (e1.x * Sb) * t6; v6[r][3] = (e1.y * Sb) * t6;
+      v6[r][4] = (e2.x * Sb) * t6; v6[r][5] = (e2.y * Sb) * t6;
+      v6[r][6] = (e3.x * Sb) * t6; v6[r][7] = (e3.y * Sb) * t6;
+    }
+  };
+  // rows 2 jp, 2 jp + 1 (in v6) -> BF16 pairs out6[n][jp]
+  auto nvt_pack = [&](auto JP) {
+    if constexpr (NVT) {
+      constexpr int jp = decltype(JP)::value;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) out6[n][jp] = bf16x2_rne(v6[0][n], v6[1][n]);
+    }
+  };
+  auto nvt_convert = [&](auto BUF, auto JP) {
+    constexpr int jp = decltype(JP)::value;
+    nvt_row(BUF, ic<2 * jp>{});
+    nvt_row(BUF, ic<2 * jp + 1>{});
+    nvt_pack(JP);
+  };
+  // write the converted block into the B area of slot S
+  auto nvt_write = [&](auto SLOT) {
+    if constexpr (NVT) {
+      constexpr int S = decltype(SLOT)::value;
+      const uint32_t base = lbase[S] + C::A_BYTES;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int nl = 8 * ng6 + n;                       // B tile row
+        const uint32_t a = base + (uint32_t)(nl * RB + ((kg6 ^ swz<RB>(nl)) << 4));
+        const u32x4 v4 = {out6[n][0], out6[n][1], out6[n][2], out6[n][3]};
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)a = v4;
+      }
+    }
+  };
+  auto nvt_store = [&](auto BUF, auto SLOT) {
+    static_for<0, 4>([&](auto JP) { nvt_convert(BUF, JP); });
+    nvt_write(SLOT);
+  };
+
   const int kb = (int)p.k_begin, ke = (int)p.k_end;       // K <= 2^22
   const int nk = (ke - kb + C::BK - 1) / C::BK;
 
@@ -453,7 +559,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     TileK r;
     r.k0 = kb + t * C::BK;
     const bool past = t >= nk;
-    r.sod = past ? kOutOfRange : (uint32_t)(LD == 0 ? 2 * r.k0 : (LD == 1 || LD == 4 || LD == 5) ? r.k0 : r.k0 / 2);
+    r.sod = past ? kOutOfRange : (uint32_t)((LD == 0 || LD == 6) ? 2 * r.k0 : (LD == 1 || LD == 4 || LD == 5) ? r.k0 : r.k0 / 2);
     r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS * SEB);
     r.tail = !AL && !past && r.k0 + C::BK > ke;
     return r;
@@ -578,7 +684,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           fr.sc[f] = (chr[f][tp * SBS + b] >> (16 * h)) & 0xFFFFu;
         }
       }
-    } else if constexpr (LD != 0 && LD != 4) {
+    } else if constexpr (LD != 0 && LD != 4 && LD != 6) {
       const lds_cptr sa = as_lds(lbase[S] + wsA + xs), sb = as_lds(lbase[S] + wsB + xs);
       // MXFP8: the byte of block b; NVFP4: the two bytes of blocks 2h, 2h+1; MXFP4 (one
       // sub-block per stage): the byte of block h
@@ -655,7 +761,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 
   // Convert + MFMA one sub-block; hook(jj) runs after the MFMAs of B fragment jj.
   auto mma_sub = [&](const Frag& fr, auto&& hook) {
-    if constexpr (LD == 0) {
+    if constexpr (LD == 0 || LD == 6) {
       v8bf fa[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) __builtin_memcpy(&fa[i], &fr.raw[i], 16);
@@ -761,7 +867,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // stages (issued ahead of their stage's data).
   auto allowed = [](auto RI) constexpr {
     constexpr int ri = decltype(RI)::value;
-    int n = (NS - 2) * OPS;
+    int n = (NS - 2) * OPS + (NVT ? 16 : 0);
     if constexpr (CH)
       for (int d = 0; d <= NS - 3; ++d)
         if (((ri - d) % R + R) % R % SPC == 0) n += XS;
@@ -792,13 +898,33 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           issue_chunk(kt / SPC + 1);                    // the next chunk, ahead of this stage's data loads
           __builtin_amdgcn_sched_barrier(0);
         }
+        // LD 6: the B block of tile kt + 1 was loaded during the previous stage; the stage
+        // starts by waiting for it (nothing else is in flight then, and the compiler sees
+        // the wait, so it adds none at the later uses), then sub-block b converts row pair
+        // b, interleaved with the matrix work, and the last sub-block writes the block to
+        // tile kt + 1's slot before the barrier. Tile kt + 1's A loads and the B register
+        // loads of tile kt + 2 go out during sub-block 0.
+        if constexpr (NVT && b == 0 && jj == 0) wait_vmcnt<0>();
         if constexpr (b == 0 && jj < PJ) {
           __builtin_amdgcn_sched_barrier(0);
           issue_range(tk, ic<SL>{}, ic<(UNITS * jj) / PJ>{}, ic<(UNITS * (jj + 1)) / PJ>{});
+          if constexpr (NVT && jj == PJ - 1) nvt_issue(kt + 2, ic<ri & 1>{});
           __builtin_amdgcn_sched_barrier(0);
+        }
+        // row 2b after fragment 0, row 2b + 1 and the packing after fragment 1 (no scheduling
+        // barrier: the scheduler interleaves them with the neighbouring MFMAs)
+        if constexpr (NVT && jj == 0) nvt_row(ic<(ri + 1) & 1>{}, ic<2 * b>{});
+        if constexpr (NVT && jj == 1) {
+          nvt_row(ic<(ri + 1) & 1>{}, ic<2 * b + 1>{});
+          nvt_pack(ic<b>{});
+          if constexpr (b + 1 == SBS) {
+            __builtin_amdgcn_sched_barrier(0);
+            nvt_write(ic<SL>{});
+          }
         }
         if constexpr (b + 1 == SBS && jj == BJ) {
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (NVT) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): B writes have landed
           wait_vmcnt<WAIT>();                           // tile kt + 1 has landed (this wave's loads)
           __builtin_amdgcn_s_barrier();                 // ... and every wave's; slot S fully read
           __builtin_amdgcn_sched_barrier(0);
@@ -813,7 +939,14 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // prologue: scale chunk 0, tiles 0 .. NS-2 in flight, then the first sub-block's fragments
   issue_chunk(0);
   static_for<0, NS - 1>([&](auto T) { issue_range(tile_k(T.value), T, ic<0>{}, ic<UNITS>{}); });
-  wait_vmcnt<(NS - 2) * OPS>();
+  if constexpr (NVT) {
+    static_assert(NS == 2, "the B register pipeline runs one stage ahead of two LDS slots");
+    nvt_issue(0, ic<0>{});
+    nvt_store(ic<0>{}, ic<0>{});                        // tile 0 into slot 0 (waits for everything)
+    nvt_issue(1, ic<1>{});                              // in flight into the first stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  }
+  wait_vmcnt<(NS - 2) * OPS + (NVT ? 16 : 0)>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_sub(0, ic<0>{}, ic<0>{}, ic<0>{}, F[0]);
@@ -1068,6 +1201,12 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.m_valid = offsets[g + 1] - offsets[g];
     const int64_t b_elems = g * N * base.ldb;
     p.B = base.B + k_bytes<LD>(b_elems);
+    if constexpr (LD == 6) {                      // group g's weight: K rows of N (= ldb) NVFP4 elements
+      const int64_t w_elems = g * base.k_end * base.ldb;
+      p.B = base.B + w_elems / 2;
+      p.sB = base.sB + w_elems / 16;
+      p.tB = base.tB + g;
+    }
     if (LD == 1 || LD == 3) p.sB = base.sB + b_elems / 32;
     if (LD == 2) {
       p.sB = base.sB + b_elems / 16;
@@ -1340,7 +1479,7 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   // group at least 64 of them. BF16 row groups averaging 384 rows or more also take
   // 256 x 256 tiles: their per-flop speed outweighs the extra row padding there (DeepSeek
   // expert dgrads, ~527 rows per expert: 7% faster). NVFP4 showed no gain.
-  const bool big_rows = fmt == 3 && !vary_k && groups > 0 && total / groups >= 384;
+  const bool big_rows = (fmt == 3 || fmt == 7) && !vary_k && groups > 0 && total / groups >= 384;
   // Row-grouped NVFP4 with chunked scales: 128 x 256 tiles (DeepSeek expert gate_up 12%
   // faster than 128 x 128, Qwen3 8%).
   const bool nv_rect = fmt == 2 && !vary_k && scale_mode(2, K, false) == 2;
@@ -1348,7 +1487,7 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   // BF16 weight gradients with large outputs: 128 x 256 tiles (DeepSeek expert wgrads 7-9%
   // faster than 256 x 256)
   const bool bf_wgrad = fmt == 3 && wide_out;
-  const int BT = bf_wgrad ? 128 : (wide_out || big_rows) ? 256 : 128;
+  const int BT = fmt == 7 ? 256 : bf_wgrad ? 128 : (wide_out || big_rows) ? 256 : 128;
   const int BTN = (nv_rect || bf_wgrad) ? 256 : BT;
   const int64_t tiles_n = (N + BTN - 1) / BTN;
   const int64_t tiles_m_fixed = vary_k ? (M + BT - 1) / BT : 0;
@@ -1365,6 +1504,15 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
     p.m_valid = 0; p.lda = K; p.n_valid = N; p.ldb = K; p.k_begin = 0; p.k_end = K;
   } else {
     p.m_valid = M; p.lda = total; p.n_valid = N; p.ldb = total; p.k_begin = 0; p.k_end = 0;
+  }
+  if (fmt == 7) {
+    // BF16 A x the stacked NVFP4 weights (K, N) per group, read transposed: B_g[n][k] is the
+    // BF16 dequantization of W_g[k][n], built in the loader (no BF16 weight copy in HBM)
+    p.ldb = N;
+    const int64_t tn = (N + 255) / 256;
+    hipLaunchKernelGGL((exact_grouped_kernel<6, 256, 256, 0, 1, false>), dim3((unsigned)max_tiles), dim3(256), 0, st, p,
+                       offsets, prefix, groups, 0, M, N, tn);
+    return hipGetLastError();
   }
   const int ld = fmt == 1 ? 1 : fmt == 2 ? 2 : fmt == 4 ? 3 : 0;
   const int sm = scale_mode(ld, p.lda, vary_k != 0);

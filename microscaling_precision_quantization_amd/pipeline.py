@@ -249,15 +249,20 @@ class MoeDequantBackward:
     outputs and dGU (S, 2I) of the gate_up outputs (padding slots zero):
         down:    dh = dO W_d,g          dW_d,g = dO_g^T h_hat_g
         gate_up: dX = dGU W_gu,g        dW_gu,g = dGU_g^T X_hat_g
-    dgrad GEMMs vary M per expert; wgrad GEMMs vary K (the slots). Operands that a TN
-    GEMM needs transposed come from dequantize_transposed."""
+    dgrad GEMMs vary M per expert; wgrad GEMMs vary K (the slots). The dgrads read the
+    forward's NVFP4 expert weights directly (fused_weights: the GEMM loader builds the
+    transposed BF16 dequantization, the BF16_NVFP4T format); with fused_weights=False
+    they read BF16 transposes written by dequantize_transposed first. Activation operands
+    that a TN wgrad needs transposed come from dequantize_transposed."""
 
-    def __init__(self, fwd: MoeNvfp4):
+    def __init__(self, fwd: MoeNvfp4, fused_weights: bool = True):
         f = fwd
         dev, G, H, I, S = f.dev, f.G, f.H, f.I, f.S
         self.f = f
-        self.w_dT = _bf16((G, I, H), dev)          # W_hat_d,g^T
-        self.w_guT = _bf16((G, H, 2 * I), dev)     # W_hat_gu,g^T
+        self.fused = fused_weights
+        if not fused_weights:
+            self.w_dT = _bf16((G, I, H), dev)      # W_hat_d,g^T
+            self.w_guT = _bf16((G, H, 2 * I), dev) # W_hat_gu,g^T
         self.hT = _bf16((1, I, S), dev)            # h_hat^T (slots along K)
         self.xT = _bf16((1, H, S), dev)            # X_hat gathered into slots, transposed
         self.d_oT = _bf16((1, H, S), dev)
@@ -268,6 +273,9 @@ class MoeDequantBackward:
         self.dw_gu = _f32((G, 2 * I, H), dev)
 
     def dequantize_weights(self):                                  # A6 (static per step)
+        """BF16 transposed weights for the two-step dgrads (nothing to do when fused)."""
+        if self.fused:
+            return
         f = self.f
         qw, sw, tw = f.wq["d"]
         B.dequantize_transposed(B.NVFP4, qw, sw, tw, t_scope="group", groups=f.G, group_rows=f.H, cols=f.I,
@@ -288,12 +296,22 @@ class MoeDequantBackward:
     def gemms(self, d_o, d_gu):                                    # A13
         f = self.f
         off = f.r.offsets
-        B.grouped_gemm_block_scaled(B.BF16, off, d_o, self.w_dT, N=f.I, K=f.H, total=f.S, out=self.dh,
-                                    workspace=f.ws)
+        if self.fused:
+            qw, sw, tw = f.wq["d"]
+            B.grouped_gemm_block_scaled(B.BF16_NVFP4T, off, d_o, qw, N=f.I, K=f.H, sB=sw, tB=tw, tB_scope="group",
+                                        total=f.S, out=self.dh, workspace=f.ws)
+        else:
+            B.grouped_gemm_block_scaled(B.BF16, off, d_o, self.w_dT, N=f.I, K=f.H, total=f.S, out=self.dh,
+                                        workspace=f.ws)
         B.grouped_gemm_block_scaled(B.BF16, off, self.d_oT[0], self.hT[0], N=f.I, K=0, vary_k=True, M=f.H,
                                     total=f.S, out=self.dw_d, workspace=f.ws)
-        B.grouped_gemm_block_scaled(B.BF16, off, d_gu, self.w_guT, N=f.H, K=2 * f.I, total=f.S, out=self.dx,
-                                    workspace=f.ws)
+        if self.fused:
+            qw, sw, tw = f.wq["gu"]
+            B.grouped_gemm_block_scaled(B.BF16_NVFP4T, off, d_gu, qw, N=f.H, K=2 * f.I, sB=sw, tB=tw,
+                                        tB_scope="group", total=f.S, out=self.dx, workspace=f.ws)
+        else:
+            B.grouped_gemm_block_scaled(B.BF16, off, d_gu, self.w_guT, N=f.H, K=2 * f.I, total=f.S, out=self.dx,
+                                        workspace=f.ws)
         B.grouped_gemm_block_scaled(B.BF16, off, self.d_guT[0], self.xT[0], N=f.H, K=0, vary_k=True, M=2 * f.I,
                                     total=f.S, out=self.dw_gu, workspace=f.ws)
 

@@ -552,3 +552,48 @@ def _oracle_operand(f, q, side):
         t = host(q["t" + side])
         return onv.dequantize_exact(x, sx, t if len(t) == x.shape[0] else np.repeat(t, x.shape[0]))
     return F.bf16_bits_to_f32(x).astype(np.float64)
+
+
+# ------------- dequantized-backward dgrad straight from NVFP4 weights -------------
+
+def _nvfp4t_case(seed, G, K, N, rows, zero_group=None):
+    g = inputs.rng(170, seed)
+    w = inputs.to_bf16_bits(g.standard_normal((G * K, N)) * 0.02 * np.exp2(g.integers(-3, 3, (G * K, 1))))
+    if zero_group is not None:                              # an all-zero expert with -0 entries
+        w[zero_group * K:(zero_group + 1) * K] = 0
+        w[zero_group * K, ::7] = 0x8000
+    offsets = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    S = int(offsets[-1])
+    a = inputs.to_bf16_bits(g.standard_normal((S, K)) * 1e-3)
+    qw, sw, tw = mxq.quantize_nvfp4(dev_bf16(w), scope="group", group_rows=K)
+    wb = onv.dequantize_bf16_bits(host(qw), host(sw), np.repeat(host(tw), K))      # (G K, N) BF16 bits
+    b_hat = F.bf16_bits_to_f32(wb).astype(np.float64).reshape(G, K, N).transpose(0, 2, 1)
+    ref = omoe.grouped_gemm_ref(F.bf16_bits_to_f32(a).astype(np.float64), offsets, b_hat)
+    return dict(a=a, qw=qw, sw=sw, tw=tw, off=offsets, ref=ref, S=S)
+
+
+@pytest.mark.parametrize("G,K,N,rows,zg", [
+    (6, 512, 768, [0, 400, 513, 256, 390, 1000], None),     # 256-row tiles on both paths: bit-identical
+    (4, 200, 400, [37, 0, 300, 129], 1),                     # K tail (200 % 64), N tail (400 % 256), zero expert
+    (3, 1024, 2048, [700, 64, 900], 2),
+])
+def test_bf16_nvfp4t_dgrad_from_quantized_weights(G, K, N, rows, zg):
+    """The BF16 x NVFP4-weights-transposed grouped GEMM (the weight dequantization done in
+    the GEMM loader) against the oracle's FP64 product of the BF16 dequantized weights,
+    per expert, and bit for bit against the two-step path (dequantize_transposed, then the
+    BF16 grouped GEMM) where both run the same tiles."""
+    c = _nvfp4t_case(G + K + N, G, K, N, rows, zg)
+    off = dev(c["off"])
+    got = host(mxq.grouped_gemm_block_scaled(mxq.BF16_NVFP4T, off, dev_bf16(c["a"]), c["qw"], N=N, K=K, sB=c["sw"],
+                                             tB=c["tw"], tB_scope="group", total=c["S"]))
+    for e in range(G):
+        lo, hi = c["off"][e], c["off"][e + 1]
+        if hi > lo:
+            assert_gemm_close(got[lo:hi], c["ref"][lo:hi], f"expert {e}")
+    wT = mxq.dequantize_transposed(mxq.NVFP4, c["qw"], c["sw"], c["tw"], t_scope="group", groups=G, group_rows=K,
+                                   cols=N)
+    two_step = host(mxq.grouped_gemm_block_scaled(mxq.BF16, off, dev_bf16(c["a"]), wT, N=N, K=K, total=c["S"]))
+    if c["S"] / G >= 384:
+        assert np.array_equal(got.view(np.uint32), two_step.view(np.uint32))
+    else:
+        assert_gemm_close(got, two_step.astype(np.float64), "against the two-step path")

@@ -145,14 +145,17 @@ def test_moe_layer_forward_and_dequantized_backward(pad):
     d_gu = inputs.normal_bf16(gg, (S, 2 * I), 1e-3)
     d_o[~live] = 0
     d_gu[~live] = 0
-    b = pipeline.MoeDequantBackward(m)
+    b = pipeline.MoeDequantBackward(m)                         # dgrads straight from the NVFP4 weights
     b.dequantize_weights()
     b.backward(dev_bf16(d_o), dev_bf16(d_gu))
+    b2 = pipeline.MoeDequantBackward(m, fused_weights=False)    # BF16 weight transposes first
+    b2.dequantize_weights()
+    b2.backward(dev_bf16(d_o), dev_bf16(d_gu))
     torch.cuda.synchronize()
     wd_b = onv.dequantize_bf16_bits(qd, sd, np.repeat(td, H)).reshape(G, H, I)
-    assert_bytes_equal(host(b.w_dT), np.ascontiguousarray(wd_b.transpose(0, 2, 1)), "W_d^T")
+    assert_bytes_equal(host(b2.w_dT), np.ascontiguousarray(wd_b.transpose(0, 2, 1)), "W_d^T")
     wgu_b = onv.dequantize_bf16_bits(qg, sg, np.repeat(tg, 2 * I)).reshape(G, 2 * I, H)
-    assert_bytes_equal(host(b.w_guT), np.ascontiguousarray(wgu_b.transpose(0, 2, 1)), "W_gu^T")
+    assert_bytes_equal(host(b2.w_guT), np.ascontiguousarray(wgu_b.transpose(0, 2, 1)), "W_gu^T")
     h_b = onv.dequantize_bf16_bits(host(m.qh), host(m.sh), host(m.th))
     assert_bytes_equal(host(b.hT)[0], np.ascontiguousarray(h_b.T), "h_hat^T")
     x_b = onv.dequantize_bf16_bits(host(m.qx), host(m.sx), host(m.tx))
@@ -167,8 +170,10 @@ def test_moe_layer_forward_and_dequantized_backward(pad):
             assert np.all(dw_d[e] == 0) and np.all(dw_gu[e] == 0)
             continue
         assert_gemm_close(dh[lo:hi], f64(d_o[lo:hi]) @ f64(wd_b[e]), f"down dgrad {e}")
+        assert_gemm_close(host(b2.dh[lo:hi]), f64(d_o[lo:hi]) @ f64(wd_b[e]), f"down dgrad {e} (two-step)")
         assert_gemm_close(dw_d[e], f64(d_o[lo:hi]).T @ f64(h_b[lo:hi]), f"down wgrad {e}")
         assert_gemm_close(dx[lo:hi], f64(d_gu[lo:hi]) @ f64(wgu_b[e]), f"gate_up dgrad {e}")
+        assert_gemm_close(host(b2.dx[lo:hi]), f64(d_gu[lo:hi]) @ f64(wgu_b[e]), f"gate_up dgrad {e} (two-step)")
         assert_gemm_close(dw_gu[e], f64(d_gu[lo:hi]).T @ f64(xs[lo:hi]), f"gate_up wgrad {e}")
 
 
@@ -294,7 +299,10 @@ def test_moe_deepseek_full_size_sampled():
         lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
         wgu_b = onv.dequantize_bf16_bits(qg[e * 2 * I:(e + 1) * 2 * I], sg[e * 2 * I:(e + 1) * 2 * I],
                                          np.repeat(tg[e:e + 1], 2 * I))
-        assert_bytes_equal(host(b.w_guT[e]), np.ascontiguousarray(wgu_b.T), f"W_gu^T[{e}]")
+        wguT = mxq.dequantize_transposed(mxq.NVFP4, m.wq["gu"][0][e * 2 * I:(e + 1) * 2 * I],
+                                         m.wq["gu"][1][e * 2 * I:(e + 1) * 2 * I], m.wq["gu"][2][e:e + 1],
+                                         t_scope="group", groups=1, group_rows=2 * I, cols=H)
+        assert_bytes_equal(host(wguT[0]), np.ascontiguousarray(wgu_b.T), f"W_gu^T[{e}]")
         qd, sd, td = (host(a[e * H:(e + 1) * H]) if a.dim() == 2 else host(a) for a in m.wq["d"])
         wd_b = onv.dequantize_bf16_bits(qd, sd, np.repeat(td[e:e + 1], H))
         d_o, d_gu = host(t["d_o"][lo:hi]), host(t["d_gu"][lo:hi])

@@ -98,8 +98,7 @@ template <int LD, int SM> struct ScaleDma {
 // NVFP4 256 K per stage), i.e. fewer barriers and larger loads per stage.
 template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false>
 struct Cfg {
-  // BF16 128 x 256 tiles at two workgroups per CU take 64-byte stages to fit half the LDS
-  static constexpr int RB = (WIDE && LD != 0) ? 128 : (LD == 0 && OCC == 2 && BM + BN == 384) ? 64 : RowBytes<LD>::v;
+  static constexpr int RB = (WIDE && LD != 0) ? 128 : RowBytes<LD>::v;
   static constexpr int BK = (LD == 0 || LD == 6) ? RB / 2 : (LD == 1 || LD == 4 || LD == 5) ? RB : 2 * RB;   // K per stage
   static constexpr int SBS = LD == 5 ? RB / 64 : RB / 32;                 // sub-blocks per stage
   static_assert(!WIDE || SM == 2, "wide stages need chunked scales");
@@ -1016,6 +1015,18 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);           // reads done before the next strip overwrites
     }
+  } else if (m0 + BM <= p.m_valid && n0 + BN <= p.n_valid) {
+    // interior tile (the common case): no per-element bounds checks, one row pointer per
+    // accumulator row and the TJ column blocks at fixed offsets from it
+    float* cw = p.C + (m0 + wm * (BM / 2) + h * 4) * p.ldc + n0 + wn * (BN / 2) + lr;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float* cr = cw + (int64_t)(i * 32 + (r / 4) * 8 + (r % 4)) * p.ldc;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) __builtin_nontemporal_store(acc[i][j][r], cr + j * 32);
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -1450,15 +1461,6 @@ static void launch_grouped_t(const ExactProblem& p, const int64_t* offsets, cons
                      offsets, prefix, groups, vary_k, M, N, tn);
 }
 
-// BF16 weight gradients (vary_k): 128 x 256 tiles, two workgroups per CU, so one's
-// prologue and FP32 epilogue overlap the other's main loop (short K per group).
-static void launch_grouped_bf16_wgrad(const ExactProblem& p, const int64_t* offsets, const int64_t* prefix,
-                                      int64_t max_tiles, int64_t groups, int64_t M, int64_t N, hipStream_t st) {
-  const int64_t tn = (N + 255) / 256;
-  hipLaunchKernelGGL((exact_grouped_kernel<0, 128, 256, 0, 2, false>), dim3((unsigned)max_tiles), dim3(256), 0, st, p,
-                     offsets, prefix, groups, 1, M, N, tn);
-}
-
 // Row-grouped NVFP4 with chunked scales: 128-row tiles keep the expert padding small,
 // 256 columns halve the A re-reads, two workgroups per CU.
 template <int SM>
@@ -1483,12 +1485,12 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   // Row-grouped NVFP4 with chunked scales: 128 x 256 tiles (DeepSeek expert gate_up 12%
   // faster than 128 x 128, Qwen3 8%).
   const bool nv_rect = fmt == 2 && !vary_k && scale_mode(2, K, false) == 2;
+  // Weight gradients (vary_k) with large outputs: 256 x 256 tiles. (With the unguarded
+  // interior-tile epilogue the DeepSeek expert wgrads run 5% faster on them than on 128 x 256
+  // tiles at two workgroups per CU; with per-element guarded stores it was the reverse.)
   const bool wide_out = vary_k && ((M + 255) / 256) * ((N + 255) / 256) >= 64;
-  // BF16 weight gradients with large outputs: 128 x 256 tiles (DeepSeek expert wgrads 7-9%
-  // faster than 256 x 256)
-  const bool bf_wgrad = fmt == 3 && wide_out;
-  const int BT = fmt == 7 ? 256 : bf_wgrad ? 128 : (wide_out || big_rows) ? 256 : 128;
-  const int BTN = (nv_rect || bf_wgrad) ? 256 : BT;
+  const int BT = fmt == 7 ? 256 : (wide_out || big_rows) ? 256 : 128;
+  const int BTN = nv_rect ? 256 : BT;
   const int64_t tiles_n = (N + BTN - 1) / BTN;
   const int64_t tiles_m_fixed = vary_k ? (M + BT - 1) / BT : 0;
   const int64_t align = (fmt == 1 || fmt == 4) ? 32 : fmt == 2 ? 16 : 8;
@@ -1536,7 +1538,6 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   };
   if (ld == 1) by_sm(ic<1>{});
   else if (ld == 2 && nv_rect) launch_grouped_nv_rect<2>(p, offsets, prefix, max_tiles, groups, M, N, st);
-  else if (ld == 0 && bf_wgrad) launch_grouped_bf16_wgrad(p, offsets, prefix, max_tiles, groups, M, N, st);
   else if (ld == 2) by_sm(ic<2>{});
   else if (ld == 3) by_sm(ic<3>{});
   else by_sm(ic<0>{});

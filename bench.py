@@ -418,31 +418,50 @@ class MoeDeepseek:
                       lambda: self.moe.quantize_weights_2d(self.d["w_gu"], self.d["w_d"]), n_el * NV_2D_BOTH, "hbm")]
 
     def cpu_baseline(self):
+        """Whole experts, one after another (evenly spaced over the 256) until about 10 s
+        of CPU work: weight quantize of W_gu and W_d, per-token quantize of the expert's
+        tokens, gate_up GEMM, SwiGLU, requantize, down GEMM, then the four backward GEMMs
+        of the dequantized operands. The device-to-host copies of each expert's weights
+        and upstream gradients are outside the timed sections."""
+        from oracle import moe as omoe
         from oracle import nvfp4 as onv
-        w, r = self.host, self.host["routing"]
-        H, I = self.H, self.I
-        lo, hi = r.offsets[0], r.offsets[1]
-        rows = r.row_index[lo:hi]
-        rows = rows[rows >= 0]
-        wgu_bits = self.d["w_gu"][:2 * I].view(torch_int16()).cpu().numpy().view(np.uint16)   # expert 0
-        t0 = time.perf_counter()
-        qx, sx, tx = rows_parallel(onv.quantize_per_token, w["x"][rows])
-        xh = onv.dequantize_exact(qx, sx, tx)
-        q, s, t = nv_group_parallel(onv, wgu_bits, 2 * I)
-        wh = onv.dequantize_exact(q, s, np.repeat(t, 2 * I))
-        gu = xh @ wh.T                    # fprop gate_up of expert 0
-        gu @ wh                           # dgrad-shaped product (rows x H)
-        gu.T @ xh                         # wgrad-shaped product (2I x H)
-        dt = time.perf_counter() - t0
-        m = len(rows)
-        flop = 3 * 2 * m * 2 * I * H
-        return flop / dt, (f"expert 0 of 256: per-token quantize of its {m} tokens, gate_up weight quantize, and "
-                           f"the fprop/dgrad/wgrad-shaped FP64 GEMMs ({m} x {2 * I} x {H}) -- {dt:.1f} s")
-
-
-def torch_int16():
-    import torch
-    return torch.int16
+        import torch
+        w, r, d = self.host, self.host["routing"], self.d
+        G, H, I = self.G, self.H, self.I
+        bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        busy, flop, done, tokens = 0.0, 0, 0, 0
+        for e in range(0, G, 8):
+            lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+            rows = r.row_index[lo:hi]
+            live = np.nonzero(rows >= 0)[0]
+            rows = rows[live]
+            wgu = bits(d["w_gu"][e * 2 * I:(e + 1) * 2 * I])
+            wd = bits(d["w_d"][e * H:(e + 1) * H])
+            d_o = omoe.bf16_to_f64(bits(d["d_o"][lo:hi])[live])
+            d_gu = omoe.bf16_to_f64(bits(d["d_gu"][lo:hi])[live])
+            t0 = time.perf_counter()
+            q, s, t = nv_group_parallel(onv, wgu, 2 * I)
+            w_gu = onv.dequantize_exact(q, s, np.repeat(t, 2 * I))
+            q, s, t = nv_group_parallel(onv, wd, H)
+            w_d = onv.dequantize_exact(q, s, np.repeat(t, H))
+            qx, sx, tx = rows_parallel(onv.quantize_per_token, w["x"][rows])
+            x_hat = onv.dequantize_exact(qx, sx, tx)
+            h = omoe.swiglu_bf16_ref((x_hat @ w_gu.T).astype(np.float32))     # gate_up + SwiGLU
+            qh, sh, th = rows_parallel(onv.quantize_per_token, h)
+            h_hat = onv.dequantize_exact(qh, sh, th)
+            h_hat @ w_d.T                                                       # down
+            d_o @ w_d, d_o.T @ h_hat                                            # down dgrad, wgrad
+            d_gu @ w_gu, d_gu.T @ x_hat                                         # gate_up dgrad, wgrad
+            busy += time.perf_counter() - t0
+            m = len(rows)
+            flop += 3 * (2 * m * 2 * I * H + 2 * m * H * I)
+            done += 1
+            tokens += m
+            if busy >= 10.0:
+                break
+        return flop / busy, (f"{done} of the {G} routed experts ({tokens} routed tokens), each end to end: NVFP4 "
+                             f"quantize of W_gu and W_d, per-token quantize of its tokens, gate_up, SwiGLU, "
+                             f"requantize, down, and the four backward GEMMs (FP64) -- {busy:.1f} s")
 
 
 class Stress:

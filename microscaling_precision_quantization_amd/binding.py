@@ -4,7 +4,9 @@ Argument marshalling only: every function here allocates its outputs with torch
 on the input's device, passes raw device pointers and torch's current HIP stream
 to the C ABI in include/mxq.h, and raises MxqError on a non-zero status. No
 step of the quantize / GEMM path runs in Python, and there is no fallback: if
-libmxq.so is missing the first call raises.
+libmxq.so is missing the first call raises. MXQ_LIBRARY, when set, names another
+build of the same library to load instead (the host-sanitizer build that the ABI
+tests run under).
 """
 
 from __future__ import annotations
@@ -15,7 +17,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxq.so")
+LIB_PATH = os.environ.get("MXQ_LIBRARY") or os.path.join(_HERE, "libmxq.so")
 
 MXFP8, NVFP4, BF16, MXFP4 = 1, 2, 3, 4
 BF16_NVFP4T = 5                    # grouped only: BF16 A x stacked NVFP4 weights (K, N) read transposed

@@ -5,6 +5,11 @@
 Every source is compiled with IEEE binary32 semantics (no fast math, no FP
 contraction, correctly rounded division, denormals kept), which the bit-exact
 quantizers rely on, and with packed-FP32 instructions disabled.
+
+build_asan() links a second copy, _build/libmxq_asan.so, whose host code in
+api.hip (argument validation, workspace sizing, launch set-up) is built with
+AddressSanitizer; the device code is the same as in libmxq.so. It is meant for the
+CPU ABI tests, run with the sanitizer runtime preloaded (ASAN_RUNTIME).
 """
 
 from __future__ import annotations
@@ -44,6 +49,36 @@ def _compile(src: str) -> str:
     if out:
         print(out, file=sys.stderr)
     return obj
+
+
+ASAN_RUNTIME = "/opt/rocm/llvm/lib/clang/{}/lib/linux/libclang_rt.asan-x86_64.so"
+# host-only instrumentation: each sanitizer flag applies to the host compilation alone
+ASAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str | None:
+    """Path of the clang AddressSanitizer runtime that matches hipcc, or None."""
+    import glob
+    hits = sorted(glob.glob(ASAN_RUNTIME.format("*")))
+    return hits[-1] if hits else None
+
+
+def build_asan() -> str:
+    """_build/libmxq_asan.so: api.hip with host AddressSanitizer, the kernels as built."""
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES if s != "api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=False)
+    obj = os.path.join(BUILD, "api_asan.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ASAN_FLAGS
+    r = subprocess.run([HIPCC, *flags, "-c", os.path.join(CSRC, "api.hip"), "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for api.hip (host sanitizer build):\n" + r.stdout + r.stderr)
+    lib = os.path.join(BUILD, "libmxq_asan.so")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", obj, *objs, "-o", lib],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed (host sanitizer build):\n" + r.stdout + r.stderr)
+    return lib
 
 
 def build(jobs: int = 6, verbose: bool = True) -> str:

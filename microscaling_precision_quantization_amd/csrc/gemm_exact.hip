@@ -1195,17 +1195,40 @@ __device__ __forceinline__ int64_t find_group(const int64_t* __restrict__ prefix
 //   vary_k = 1: group g reduces over k in [off[g], off[g+1]) into C_g = C + g*M*N.
 // OCC = 2 gives each workgroup half the LDS, so two share a CU and one's prologue and
 // epilogue overlap the other's main loop (expert tiles are short in K or in rows).
+//
+// Row groups (vary_k = 0) are walked XCD by XCD: dispatch order b goes to XCD b % 8, and
+// each XCD takes a contiguous run of the logical tile list, so an expert's tiles share
+// one L2. Inside a group the tiles go in column bands of kRowGroupBand row tiles: the row
+// tiles that read one weight column slab run side by side (Qwen3-shaped gate_up: L2
+// misses 1110 -> 275 MB per launch and 9% faster; DeepSeek-shaped fused dgrads 3-4%
+// faster). Weight gradients (vary_k = 1) keep the plain order: there the XCD runs made
+// the kernels 2-14% slower (their time goes to the FP32 output stores, not to reads).
+constexpr int kRowGroupBand = 4;
 template <int LD, int BM, int BN, int SM, int OCC, bool WIDE>
 __global__ void __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, const int64_t* __restrict__ tile_prefix,
                      int64_t groups, int vary_k, int64_t M, int64_t N, int64_t tiles_n) {
   using C = gx::Cfg<LD, BM, BN, SM, OCC, WIDE>;
   MXQ_EXACT_LDS(C)
-  const int64_t tile = blockIdx.x;
-  if (tile >= tile_prefix[groups]) return;
+  const int64_t total = tile_prefix[groups];
+  int64_t tile = blockIdx.x;
+  if (!vary_k) {
+    const int64_t T8 = (total + 7) / 8;
+    if (tile >= 8 * T8) return;                     // the grid may exceed the tile count
+    tile = (tile % 8) * T8 + tile / 8;
+  }
+  if (tile >= total) return;
   const int64_t g = find_group(tile_prefix, groups, tile);
   const int64_t local = tile - tile_prefix[g];
-  const int64_t tm = local / tiles_n, tn = local % tiles_n;
+  int64_t tm = local / tiles_n, tn = local % tiles_n;
+  if (!vary_k) {
+    const int64_t tiles_m = (tile_prefix[g + 1] - tile_prefix[g]) / tiles_n;
+    const int64_t band = local / (kRowGroupBand * tiles_n);
+    const int64_t rows_in_band = min((int64_t)kRowGroupBand, tiles_m - band * kRowGroupBand);
+    const int64_t idx = local - band * kRowGroupBand * tiles_n;
+    tm = band * kRowGroupBand + idx % rows_in_band;
+    tn = idx / rows_in_band;
+  }
   ExactProblem p = base;
   if (!vary_k) {
     p.a_base = offsets[g];

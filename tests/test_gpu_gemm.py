@@ -523,6 +523,8 @@ def _batch_case(fmt, shapes, seed):
     ("nvfp4", [(300, 200, 256), (256, 512, 2048)]),
     ("mxfp4", [(4196, 3112, 512), (64, 1000, 1024), (32, 32, 32)]),
     ("bf16", [(300, 200, 96), (128, 256, 1024)]),
+    ("mxfp8", [(300, 200, 4096), (64, 1000, 1024), (2048, 2048, 8192)]),         # long-K, few-tile members
+    ("bf16", [(384, 640, 8192), (130, 70, 4224), (300, 200, 96)]),
 ])
 def test_gemm_batch_matches_single_calls(fmt, shapes):
     f = {"mxfp8": mxq.MXFP8, "nvfp4": mxq.NVFP4, "mxfp4": mxq.MXFP4, "bf16": mxq.BF16}[fmt]
@@ -597,3 +599,32 @@ def test_bf16_nvfp4t_dgrad_from_quantized_weights(G, K, N, rows, zg):
         assert np.array_equal(got.view(np.uint32), two_step.view(np.uint32))
     else:
         assert_gemm_close(got, two_step.astype(np.float64), "against the two-step path")
+
+
+@pytest.mark.parametrize("fmt,mnk", [("mxfp8", (300, 200, 4096)), ("mxfp8", (64, 64, 8192)),
+                                     ("bf16", (384, 640, 8192)), ("bf16", (130, 70, 4224))])
+def test_long_k_few_tiles_gemm_oracle_and_deterministic(fmt, mnk):
+    """Long-K problems with few output tiles (ragged ones included): within the bound of
+    the oracle, the same bits on a second run, and the columns past N of a strided output
+    untouched."""
+    M, N, K = mnk
+    g = inputs.rng(151, M + N + K)
+    a = inputs.to_bf16_bits(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))
+    b = inputs.normal_bf16(g, (N, K), 0.05)
+    if fmt == "mxfp8":
+        qa, sa, ah = mx_operands(a)
+        qb, sb, bh = mx_operands(b)
+        f = mxq.MXFP8
+    else:
+        qa, sa, ah = dev_bf16(a), None, F.bf16_bits_to_f32(a)
+        qb, sb, bh = dev_bf16(b), None, F.bf16_bits_to_f32(b)
+        f = mxq.BF16
+    outs = []
+    for _ in range(2):
+        out = torch.full((M, N + 5), 3.0, device="cuda")
+        mxq.gemm_block_scaled(f, qa, sa, qb, sb, out=out[:, :N])
+        o = host(out)
+        assert np.all(o[:, N:] == 3.0)
+        outs.append(o[:, :N].copy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert_gemm_close(outs[0], og.gemm_tn_fp64(ah, bh), f"long K {fmt} {mnk}")

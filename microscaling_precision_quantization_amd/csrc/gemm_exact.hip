@@ -1519,7 +1519,11 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   const int64_t align = (fmt == 1 || fmt == 4) ? 32 : fmt == 2 ? 16 : 8;
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, st, offsets, groups, total, vary_k, align, (int64_t)BT,
                      tiles_m_fixed, tiles_n, prefix);
-  const int64_t max_tiles = vary_k ? groups * tiles_m_fixed * tiles_n : ((total + BT - 1) / BT + groups) * tiles_n;
+  // Row groups: an upper bound on the tiles (the device prefix holds the count), rounded
+  // up to a multiple of 8 so that the XCD-contiguous order reaches every logical tile
+  // below 8 ceil(tiles / 8) (the kernel maps dispatch index b to (b % 8) ceil(tiles / 8) + b / 8).
+  const int64_t max_tiles = vary_k ? groups * tiles_m_fixed * tiles_n
+                                   : ((((total + BT - 1) / BT + groups) * tiles_n + 7) / 8) * 8;
   if (max_tiles <= 0) return hipGetLastError();
   ExactProblem p;
   p.A = (const uint8_t*)A; p.sA = (const uint8_t*)sA; p.tA = tA; p.tA_mode = tA_mode;

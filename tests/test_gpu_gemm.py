@@ -345,6 +345,49 @@ def test_grouped_bf16_vary_m_large_groups():
     assert_gemm_close(host(c), ref, "bf16 grouped, large groups")
 
 
+
+@pytest.mark.parametrize("fmt,sizes,N,K", [
+    ("bf16", [2304], 128, 64),           # one group of nine 256-row tiles, one column tile
+    ("bf16", [2304, 0, 256], 100, 64),
+    ("nvfp4", [1152], 256, 256),         # nine 128-row tiles on the 128 x 256 NVFP4 tiles
+    ("mxfp8", [1152], 128, 64),          # nine 128 x 128 tiles
+    ("mxfp8", [640, 128, 384], 64, 96),
+])
+def test_grouped_row_groups_with_few_column_tiles(fmt, sizes, N, K):
+    """Row groups whose tile count is not a multiple of 8 with one column tile: the
+    XCD-contiguous tile order has to reach every tile (a grid too small for it left row
+    tiles unwritten). Every output row is checked against the oracle."""
+    g = inputs.rng(152, sum(sizes) + N + K)
+    sizes = np.array(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    S, G = int(off[-1]), len(sizes)
+    a = inputs.to_bf16_bits(g.standard_normal((S, K)) * g.lognormal(0, 1, (S, 1)))
+    w = inputs.normal_bf16(g, (G * N, K), 0.05)
+    c = torch.full((S, N), float("nan"), device="cuda")  # an unwritten tile stays NaN
+    if fmt == "bf16":
+        mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a), dev_bf16(w), N=N, K=K, out=c)
+        ah, wh = F.bf16_bits_to_f32(a).astype(np.float64), F.bf16_bits_to_f32(w).astype(np.float64)
+    elif fmt == "mxfp8":
+        qa, sa, ah = mx_operands(a)
+        qw, sw, wh = mx_operands(w)
+        mxq.grouped_gemm_block_scaled(mxq.MXFP8, dev(off), qa, qw, N=N, K=K, sA=sa, sB=sw, out=c)
+    else:
+        qa, sa, ta = mxq.quantize_nvfp4_per_token(dev_bf16(a))
+        qw, sw, tw = mxq.quantize_nvfp4(dev_bf16(w), scope="group", group_rows=N)
+        mxq.grouped_gemm_block_scaled(mxq.NVFP4, dev(off), qa, qw, N=N, K=K, sA=sa, sB=sw, tA=ta, tB=tw,
+                                      tA_scope="row", tB_scope="group", out=c)
+        ah = onv.dequantize_exact(host(qa), host(sa), host(ta))
+        wh = onv.dequantize_exact(host(qw), host(sw), np.repeat(host(tw), N))
+    ref = omoe.grouped_gemm_ref(ah, off, wh.reshape(G, N, -1))
+    ch = host(c)
+    assert not np.isnan(ch).any(), f"{np.isnan(ch).any(axis=1).sum()} output rows never written"
+    for e in range(G):
+        lo, hi = off[e], off[e + 1]
+        for r0 in range(lo, hi, 128):                     # every 128-row band on its own
+            r1 = min(r0 + 128, hi)
+            assert_gemm_close(ch[r0:r1], ref[r0:r1], f"{fmt} group {e} rows {r0}:{r1}")
+
+
 # --------------------------------- MoE glue ---------------------------------
 
 def test_swiglu_extreme_gates():

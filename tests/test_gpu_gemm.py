@@ -319,6 +319,30 @@ def test_grouped_bf16_vary_k_wide_output():
             assert_gemm_close(c[e], ah[:, off[e]:off[e + 1]] @ bh[:, off[e]:off[e + 1]].T, f"wide wgrad group {e}")
 
 
+
+def test_grouped_bf16_vary_k_wide_output_many_tiles():
+    """A wide BF16 weight gradient with more output tiles than CUs: ragged M (2100) and
+    N (2050), per-group K of 600 (ten 64-K stages), 0, 520 and 64 (one stage), an empty
+    group in between. The output is prefilled with NaN, so an element that no tile
+    writes fails the check."""
+    g = inputs.rng(92, 0)
+    M, N = 2100, 2050
+    sizes = np.array([600, 0, 520, 64])
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    S = int(off[-1])
+    a = inputs.normal_bf16(g, (M, S), 1.0)
+    b = inputs.normal_bf16(g, (N, S), 1.0)
+    out = torch.full((len(sizes), M, N), float("nan"), device="cuda")
+    mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a), dev_bf16(b), N=N, K=0, vary_k=True, M=M, out=out)
+    c = host(out)
+    assert not np.isnan(c).any()
+    ah, bh = F.bf16_bits_to_f32(a).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64)
+    for e in range(len(sizes)):
+        if sizes[e] == 0:
+            assert np.all(c[e] == 0.0)
+        else:
+            assert_gemm_close(c[e], ah[:, off[e]:off[e + 1]] @ bh[:, off[e]:off[e + 1]].T, f"wide wgrad group {e}")
+
 def test_grouped_bf16_vary_m():
     x, r, w = small_moe(seed=2)
     G, N = 8, 192

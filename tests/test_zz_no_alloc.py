@@ -2,7 +2,8 @@
 scheduler scratch lives in the library's static device array (for callers that cannot
 allocate): called through the C ABI, its output must equal grouped_gemm_block_scaled's
 bit for bit (the same kernels run) and meet the 2e-5 bound against the oracle, on two
-calls in a row, the second smaller, so stale scratch from the first would show."""
+calls in a row, the second smaller, so stale scratch from the first would show; and
+captured in a HIP graph, each replay with new data equal to the workspace entry point."""
 
 import ctypes
 
@@ -80,3 +81,32 @@ def test_noalloc_rejects_more_groups_than_its_scratch_holds():
     assert _call_noalloc(c, out, groups=8192) == 5                # MXQ_ERR_WORKSPACE: nothing launched
     torch.cuda.synchronize()
     assert np.all(host(out) == 9.0)
+
+
+def test_noalloc_grouped_gemm_in_a_captured_hip_graph():
+    """The use the entry point exists for: captured in a HIP graph (no allocation, no
+    workspace argument) and replayed with new token data copied into its operands, with
+    eager work and synchronizations between replays; every replay equals the workspace
+    entry point on the same data, bit for bit."""
+    c = _moe_case(3, tokens=300, groups=24, N=256, K=512)
+    out = torch.full((c["total"], c["N"]), 9.0, device="cuda")
+    assert _call_noalloc(c, out) == 0                             # first use outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert _call_noalloc(c, out) == 0
+    torch.cuda.synchronize()
+    for trial in range(3):
+        g = inputs.rng(161, trial)
+        x = inputs.to_bf16_bits(g.standard_normal((c["tokens"], c["K"])) * g.lognormal(0, 1, (c["tokens"], 1)))
+        qx, sx, tx = mxq.quantize_nvfp4_per_token(dev_bf16(x))
+        c["qx"].copy_(qx)
+        c["sx"].copy_(sx)
+        c["tx"].copy_(tx)
+        out.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(out)
+        ref_ws = host(_call_workspace(c))                         # eager call between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(got.view(np.uint32), ref_ws.view(np.uint32)), f"replay {trial}"

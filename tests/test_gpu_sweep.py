@@ -1,0 +1,91 @@
+"""Seeded random-shape sweeps through the C ABI against the oracle: MXFP8 row + column
+copies and NVFP4 per-token / per-tensor quantization on strided BF16 inputs (bit-exact),
+and MXFP8 / NVFP4 / BF16 GEMMs on ragged M, N and K (2e-5). Shapes are drawn within each
+entry point's documented limits, values are N(0, 1) times a log-normal row scale with a
+few large outliers and exact zeros."""
+
+import numpy as np
+import pytest
+import torch
+
+import microscaling_precision_quantization_amd as mxq
+from microscaling_precision_quantization_amd import inputs
+from oracle import formats as F
+from oracle import gemm as og
+from oracle import mxfp8 as omx
+from oracle import nvfp4 as onv
+from tests.gpu_util import assert_bytes_equal, assert_gemm_close, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _values(g, rows, cols):
+    x = g.standard_normal((rows, cols)) * g.lognormal(0, 1.5, (rows, 1))
+    n = max(1, rows * cols // 500)
+    x.flat[g.integers(0, x.size, n)] *= 1e3
+    x.flat[g.integers(0, x.size, n)] = 0.0
+    return inputs.to_bf16_bits(x)
+
+
+def _strided(bits, pad):
+    """The BF16 tensor as a row-strided device view (row stride cols + pad)."""
+    rows, cols = bits.shape
+    wide = np.zeros((rows, cols + pad), dtype=np.uint16)
+    wide[:, :cols] = bits
+    return dev_bf16(wide)[:, :cols]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_mxfp8_row_and_column_copies(seed):
+    g = inputs.rng(170, seed)
+    rows, cols, pad = 32 * int(g.integers(1, 24)), 32 * int(g.integers(1, 48)), 8 * int(g.integers(0, 4))
+    xb = _values(g, rows, cols)
+    qr, sr, qc, sc = mxq.quantize_mxfp8(_strided(xb, pad))
+    eq, es = omx.quantize_rowwise(xb)
+    assert_bytes_equal(host(qr), eq, f"rowwise q {rows}x{cols}")
+    assert_bytes_equal(host(sr), es, f"rowwise s {rows}x{cols}")
+    eq, es = omx.quantize_colwise(xb)
+    assert_bytes_equal(host(qc), eq, f"colwise q {rows}x{cols}")
+    assert_bytes_equal(host(sc), es, f"colwise s {rows}x{cols}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_nvfp4_per_token_and_per_tensor(seed):
+    g = inputs.rng(171, seed)
+    rows, cols, pad = int(g.integers(1, 700)), 16 * int(g.integers(1, 200)), 8 * int(g.integers(0, 4))
+    xb = _values(g, rows, cols)
+    q, s, t = mxq.quantize_nvfp4_per_token(_strided(xb, pad))
+    eq, es, et = onv.quantize_per_token(xb)
+    assert_bytes_equal(host(q), eq, f"per-token q {rows}x{cols}")
+    assert_bytes_equal(host(s), es, f"per-token s {rows}x{cols}")
+    assert_bytes_equal(host(t).view(np.uint32), np.asarray(et, dtype=np.float32).view(np.uint32), "per-token t")
+    q, s, t = mxq.quantize_nvfp4(_strided(xb, pad), scope="tensor")
+    eq, es, et = onv.quantize_per_tensor(xb)
+    assert_bytes_equal(host(q), eq, f"per-tensor q {rows}x{cols}")
+    assert_bytes_equal(host(s), es, f"per-tensor s {rows}x{cols}")
+    assert host(t).view(np.uint32)[0] == np.asarray(et, dtype=np.float32).reshape(-1).view(np.uint32)[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_gemms_ragged(seed):
+    g = inputs.rng(172, seed)
+    M, N = int(g.integers(1, 600)), int(g.integers(1, 600))
+    K = 32 * int(g.integers(1, 48))
+    a, b = _values(g, M, K), inputs.normal_bf16(g, (N, K), 0.05)
+    # MXFP8: rowwise copies of both (blocks along K)
+    qa, sa, _, _ = mxq.quantize_mxfp8(dev_bf16(a), True, False)
+    qb, sb, _, _ = mxq.quantize_mxfp8(dev_bf16(b), True, False)
+    c = mxq.gemm_block_scaled(mxq.MXFP8, qa, sa, qb, sb)
+    ref = og.gemm_tn_fp64(omx.dequantize_exact(host(qa), host(sa)), omx.dequantize_exact(host(qb), host(sb)))
+    assert_gemm_close(host(c), ref, f"MXFP8 {M}x{N}x{K}")
+    # NVFP4: per-token A, per-tensor B
+    qa, sa, ta = mxq.quantize_nvfp4_per_token(dev_bf16(a))
+    qb, sb, tb = mxq.quantize_nvfp4(dev_bf16(b), scope="tensor")
+    c = mxq.gemm_block_scaled(mxq.NVFP4, qa, sa, qb, sb, tA=ta, tB=tb, tA_scope="row", tB_scope="tensor")
+    ref = og.gemm_tn_fp64(onv.dequantize_exact(host(qa), host(sa), host(ta)),
+                          onv.dequantize_exact(host(qb), host(sb), np.repeat(host(tb), N)))
+    assert_gemm_close(host(c), ref, f"NVFP4 {M}x{N}x{K}")
+    # BF16
+    c = mxq.gemm_block_scaled(mxq.BF16, dev_bf16(a), None, dev_bf16(b), None)
+    ref = og.gemm_tn_fp64(F.bf16_bits_to_f32(a).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64))
+    assert_gemm_close(host(c), ref, f"BF16 {M}x{N}x{K}")

@@ -532,8 +532,9 @@ class Stress:
 
 WORKLOADS = {c.name: c for c in (Linear, Small, MoeQwen3, MoeDeepseek, Stress)}
 # (timed steps, warmup steps): the warmup keeps the GPU busy for 0.2-0.3 s so that the clock
-# has ramped up before the timed region, which then spans 0.5-0.8 s of work
-DEFAULT_STEPS = {"linear": (2000, 1000), "small": (2000, 500), "moe_qwen3": (1000, 300), "moe_deepseek": (10, 3),
+# has ramped up before the timed region, which then spans 0.5-1.2 s of work and at least 20
+# steps
+DEFAULT_STEPS = {"linear": (2000, 1000), "small": (2000, 500), "moe_qwen3": (1000, 300), "moe_deepseek": (20, 5),
                  "stress": (200, 50)}
 
 

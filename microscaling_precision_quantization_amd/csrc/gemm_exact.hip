@@ -304,6 +304,27 @@ __device__ __forceinline__ void e4m3_split(uint32_t codes, float& p2, v2h& m2) {
   __builtin_memcpy(&m2, &pair, 4);
 }
 
+// Both bytes of a scale pair at once: p0 / p1 carry 2^e of bytes 0 / 1 as above, and mm holds
+// their mantissa factors 1.mmm as packed FP16 (byte 0 low). The E4M3 codes convert to FP16
+// exactly (subnormal codes become normal FP16), and forcing the FP16 exponent field to 15
+// keeps just the factor S / 2^e -- the same values as the FP32 route.
+__device__ __forceinline__ void e4m3_split2(uint32_t codes, float& p0, float& p1, v2h& mm) {
+  p0 = __builtin_amdgcn_cvt_f32_fp8((int)codes, 0);
+  p1 = __builtin_amdgcn_cvt_f32_fp8((int)codes, 1);
+  const v2h s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false);
+  uint32_t b;
+  __builtin_memcpy(&b, &s, 4);
+  b = (b & 0x03FF03FFu) | 0x3C003C00u;
+  __builtin_memcpy(&mm, &b, 4);
+}
+
+// nv_to_f16 with half H of a packed mantissa pair broadcast to both lanes of the multiply.
+template <int H>
+__device__ __forceinline__ v8h nv_to_f16_h(uint32_t w, float p2, v2h mm) {
+  const v2h m2 = __builtin_shufflevector(mm, mm, H, H);
+  return nv_to_f16(w, p2, m2);
+}
+
 template <int I> using ic = std::integral_constant<int, I>;
 
 constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
@@ -828,24 +849,24 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 #pragma unroll
       for (int i = 0; i < TI; ++i)
       {
-        float p2;
-        v2h m2;
-        e4m3_split<0>(fr.sc[i], p2, m2);
-        fa[0][0][i] = nv_to_f16(fr.raw[i].x, p2, m2);
-        fa[0][1][i] = nv_to_f16(fr.raw[i].y, p2, m2);
-        e4m3_split<1>(fr.sc[i], p2, m2);
-        fa[1][0][i] = nv_to_f16(fr.raw[i].z, p2, m2);
-        fa[1][1][i] = nv_to_f16(fr.raw[i].w, p2, m2);
+        float p0, p1;
+        v2h mm;
+        e4m3_split2(fr.sc[i], p0, p1, mm);
+        fa[0][0][i] = nv_to_f16_h<0>(fr.raw[i].x, p0, mm);
+        fa[0][1][i] = nv_to_f16_h<0>(fr.raw[i].y, p0, mm);
+        fa[1][0][i] = nv_to_f16_h<1>(fr.raw[i].z, p1, mm);
+        fa[1][1][i] = nv_to_f16_h<1>(fr.raw[i].w, p1, mm);
       }
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
+        float pb0, pb1;
+        v2h mb;
+        e4m3_split2(fr.sc[TI + j], pb0, pb1, mb);
         static_for<0, 2>([&](auto HF) {
           constexpr int hf = decltype(HF)::value;
-          float p2;
-          v2h m2;
-          e4m3_split<hf>(fr.sc[TI + j], p2, m2);
-          const v8h fb0 = nv_to_f16(hf ? fr.raw[TI + j].z : fr.raw[TI + j].x, p2, m2);
-          const v8h fb1 = nv_to_f16(hf ? fr.raw[TI + j].w : fr.raw[TI + j].y, p2, m2);
+          const float p2 = hf ? pb1 : pb0;
+          const v8h fb0 = nv_to_f16_h<hf>(hf ? fr.raw[TI + j].z : fr.raw[TI + j].x, p2, mb);
+          const v8h fb1 = nv_to_f16_h<hf>(hf ? fr.raw[TI + j].w : fr.raw[TI + j].y, p2, mb);
 #pragma unroll
           for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][0][i], fb0, acc[i][j], 0, 0, 0);
 #pragma unroll
@@ -897,13 +918,16 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           issue_chunk(kt / SPC + 1);                    // the next chunk, ahead of this stage's data loads
           __builtin_amdgcn_sched_barrier(0);
         }
-        // LD 6: the B block of tile kt + 1 was loaded during the previous stage; the stage
-        // starts by waiting for it (nothing else is in flight then, and the compiler sees
-        // the wait, so it adds none at the later uses), then sub-block b converts row pair
-        // b, interleaved with the matrix work, and the last sub-block writes the block to
-        // tile kt + 1's slot before the barrier. Tile kt + 1's A loads and the B register
-        // loads of tile kt + 2 go out during sub-block 0.
-        if constexpr (NVT && b == 0 && jj == 0) wait_vmcnt<0>();
+        // LD 6: the B block of tile kt + 1 was loaded during the previous stage (8 rows, two
+        // loads each; nothing older is in flight when the stage starts). Sub-block b converts
+        // row pair b, interleaved with the matrix work, after waiting for just those rows:
+        // loads return in order, so they have landed once no more than the later rows' loads
+        // (and, from sub-block 1 on, the 8 A loads and 16 B loads issued in sub-block 0) are
+        // outstanding; the compiler sees the waits and adds none at the uses. The last
+        // sub-block writes the block to tile kt + 1's slot before the barrier. Tile kt + 1's
+        // A loads and the B register loads of tile kt + 2 go out during sub-block 0.
+        static_assert(!NVT || (C::IA == 8 && SBS == 4), "the wait counts assume 8 A loads per stage");
+        if constexpr (NVT && jj == 0) wait_vmcnt<b == 0 ? 12 : 8 + 16 + 4 * (3 - b)>();
         if constexpr (b == 0 && jj < PJ) {
           __builtin_amdgcn_sched_barrier(0);
           issue_range(tk, ic<SL>{}, ic<(UNITS * jj) / PJ>{}, ic<(UNITS * (jj + 1)) / PJ>{});
@@ -982,35 +1006,59 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       tbj[j] = col < p.n_valid ? (p.tB_mode == 0 ? p.tB[col] : p.tB[0]) : 0.0f;
     }
     const bool vec_ok = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
+    // tA of the lane's 16 rows of each strip, all loads issued before the first is used
+    float ta[TI][16];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * (BM / 2) + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+        const int64_t arow = row < p.m_valid ? exact_src_row(p, row) : -1;
+        ta[i][r] = arow < 0 ? 0.0f : p.tA_mode == 0 ? p.tA[arow] : p.tA[0];
+      }
+    // interior tile with 16-byte aligned rows: no per-chunk checks; each store instruction
+    // covers whole staged rows, lane l taking chunk l % CPR of row l / CPR
+    const bool interior = vec_ok && m0 + BM <= p.m_valid && n0 + BN <= p.n_valid;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int64_t rbase = m0 + wm * (BM / 2) + i * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = (r / 4) * 8 + h * 4 + (r % 4);
-        const int64_t arow = rbase + rl < p.m_valid ? exact_src_row(p, rbase + rl) : -1;
-        const float ta = arow < 0 ? 0.0f : p.tA_mode == 0 ? p.tA[arow] : p.tA[0];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) stg[rl * P + j * 32 + lr] = (acc[i][j][r] * ta) * tbj[j];
+        for (int j = 0; j < TJ; ++j) stg[rl * P + j * 32 + lr] = (acc[i][j][r] * ta[i][r]) * tbj[j];
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's LDS writes landed
       constexpr int CPR = BN / 8;                    // 16-byte chunks per staged row
+      constexpr int RPI = 64 / CPR;                  // staged rows per store instruction
+      if (interior) {
+        const int lrow = lane / CPR, lch = lane % CPR;
+        float* dst = p.C + (rbase + lrow) * p.ldc + col0 + 4 * lch;
+        const float* src = stg + lrow * P + 4 * lch;
 #pragma unroll
-      for (int k = 0; k < 32 * CPR / 64; ++k) {
-        const int idx = k * 64 + lane;
-        const int rl = idx / CPR, ch = idx % CPR;
-        const int64_t row = rbase + rl, col = col0 + ch * 4;
-        if (row >= p.m_valid) continue;
-        const float4 v = *reinterpret_cast<const float4*>(stg + rl * P + ch * 4);
-        float* dstp = p.C + row * p.ldc + col;
-        if (vec_ok && col + 4 <= p.n_valid) {
+        for (int k = 0; k < 32 / RPI; ++k) {
+          const float4 v = *reinterpret_cast<const float4*>(src + k * RPI * P);
           const f32x4_nt vv = {v.x, v.y, v.z, v.w};
-          __builtin_nontemporal_store(vv, reinterpret_cast<f32x4_nt*>(dstp));
-        } else {
-          if (col < p.n_valid) dstp[0] = v.x;
-          if (col + 1 < p.n_valid) dstp[1] = v.y;
-          if (col + 2 < p.n_valid) dstp[2] = v.z;
-          if (col + 3 < p.n_valid) dstp[3] = v.w;
+          __builtin_nontemporal_store(vv, reinterpret_cast<f32x4_nt*>(dst + k * RPI * p.ldc));
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 32 * CPR / 64; ++k) {
+          const int idx = k * 64 + lane;
+          const int rl = idx / CPR, ch = idx % CPR;
+          const int64_t row = rbase + rl, col = col0 + ch * 4;
+          if (row >= p.m_valid) continue;
+          const float4 v = *reinterpret_cast<const float4*>(stg + rl * P + ch * 4);
+          float* dstp = p.C + row * p.ldc + col;
+          if (vec_ok && col + 4 <= p.n_valid) {
+            const f32x4_nt vv = {v.x, v.y, v.z, v.w};
+            __builtin_nontemporal_store(vv, reinterpret_cast<f32x4_nt*>(dstp));
+          } else {
+            if (col < p.n_valid) dstp[0] = v.x;
+            if (col + 1 < p.n_valid) dstp[1] = v.y;
+            if (col + 2 < p.n_valid) dstp[2] = v.z;
+            if (col + 3 < p.n_valid) dstp[3] = v.w;
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);           // reads done before the next strip overwrites
@@ -1218,8 +1266,11 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     tile = (tile % 8) * T8 + tile / 8;
   }
   if (tile >= total) return;
-  const int64_t g = find_group(tile_prefix, groups, tile);
-  const int64_t local = tile - tile_prefix[g];
+  // weight gradients: every group has the same tiles_m x tiles_n tiles (the prefix is g times
+  // that, or all zero when the offsets were rejected), so the group needs no search
+  const int64_t per_group = (M + BM - 1) / BM * tiles_n;
+  const int64_t g = vary_k ? tile / per_group : find_group(tile_prefix, groups, tile);
+  const int64_t local = vary_k ? tile - g * per_group : tile - tile_prefix[g];
   int64_t tm = local / tiles_n, tn = local % tiles_n;
   if (!vary_k) {
     const int64_t tiles_m = (tile_prefix[g + 1] - tile_prefix[g]) / tiles_n;

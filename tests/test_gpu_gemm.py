@@ -463,6 +463,31 @@ def test_swiglu_requant_and_combine():
     assert_gemm_close(host(y), omoe.combine_ref(o, slot_of, wts), "combine")
 
 
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 6, 8, 9])
+def test_combine_every_topk_with_skipped_slots(k):
+    """Combine for each top-k the launcher distinguishes (compile-time k or the generic
+    loop), with slot indices below zero and past the end (they contribute nothing) and a
+    hidden size that leaves a partial last pass: within 2e-5 of the oracle, and bit-equal
+    to the FP32 sum in ascending j with a separate multiply and add per term."""
+    g = inputs.rng(88, k)
+    T, H = 70, 1028
+    S = T * k + 5
+    o = g.standard_normal((S, H)).astype(np.float32)
+    slot_of = g.permutation(S)[:T * k].reshape(T, k).astype(np.int64)
+    slot_of[g.random((T, k)) < 0.1] = -1
+    slot_of[g.random((T, k)) < 0.05] = S + 3
+    wts = g.random((T, k)).astype(np.float32)
+    y = host(mxq.moe_combine(dev(o), dev(slot_of), dev(wts)))
+    valid = (slot_of >= 0) & (slot_of < S)
+    ref = omoe.combine_ref(o, np.where(valid, slot_of, 0), np.where(valid, wts, 0.0).astype(np.float32))
+    assert_gemm_close(y, ref, f"combine k={k}")
+    acc = np.zeros((T, H), dtype=np.float32)
+    for j in range(k):
+        m = valid[:, j]
+        acc[m] = acc[m] + wts[m, j:j + 1] * o[slot_of[m, j]]
+    assert np.array_equal(y.view(np.uint32), acc.view(np.uint32)), f"combine k={k} differs from the FP32 ascending sum"
+
+
 # --------------------- native scaled-FP8 matrix-core path ---------------------
 
 def matrix_core_bound(ah, bh, c_ref):

@@ -244,6 +244,8 @@ class Linear:
 
 class Small:
     name = "small"
+    ROOFLINE_NOTE = ("launch-latency bound, not bandwidth-measurable: 1.06 MB of quantizer traffic and 67 MFLOP "
+                     "take well under a microsecond at the HBM and MFMA peaks, below the cost of a launch")
 
     def __init__(self, torch, dev):
         from microscaling_precision_quantization_amd import inputs
@@ -710,6 +712,8 @@ def main():
                 "frac_datapath": round(ach / MFMA_PEAK_TFLOPS[c["datapath"]], 4)}
     roof.update({"traffic": recorded_traffic(args.workload, dom), "kernel_group": dom,
                  "work_per_launch": int(per_launch), "avg_launch_ms": round(launch_ms, 4)})
+    if getattr(wl, "ROOFLINE_NOTE", None):
+        roof["note"] = wl.ROOFLINE_NOTE
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -501,7 +501,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     t6 = p.tB[0];
   }
   // Two register buffers: the loads of tile t + 2 are in flight while tile t + 1's block is
-  // converted (at the start of stage t) and written to its slot.
+  // converted (row pair b in sub-block b of stage t) and written to its slot.
   uint32_t bq6[2][NVT ? 8 : 1], bs6[2][NVT ? 8 : 1];
   uint32_t out6[8][NVT ? 4 : 1];                          // converted block: [n][k pair]
   // register loads of B tile t into buffer BUF (rows at or past k_end, and tiles past the

@@ -720,3 +720,64 @@ def test_long_k_few_tiles_gemm_oracle_and_deterministic(fmt, mnk):
         outs.append(o[:, :N].copy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
     assert_gemm_close(outs[0], og.gemm_tn_fp64(ah, bh), f"long K {fmt} {mnk}")
+
+
+# ------------- the documented K limit (2^22): 32-bit operand offsets -------------
+
+def _small_int_operand(g, shape):
+    """Integers in [-2, 2]: exact in BF16, and after the block scaling exact in E4M3 and
+    E2M1 too (a block maximum of 1 or 2 scales to a power of two of the element format)."""
+    v = g.integers(-2, 3, shape).astype(np.float32)
+    return v, inputs.to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8", "mxfp4", "nvfp4"])
+def test_dense_gemm_at_the_k_limit_is_exact(fmt):
+    """K = 2^22, the largest K the GEMM entry points accept. Small integer operands make
+    every product exact and keep every partial sum an integer far below 2^24, so the FP32
+    result must equal the exact product bit for bit: a K chunk dropped, repeated or read
+    from the wrong place by the 32-bit offset arithmetic would change it. M and N leave
+    ragged tiles. NVFP4 (both operands per-tensor, quantized from their transposes with
+    16-blocks along K, the only NVFP4 quantizer without a row-length limit): A and B have
+    amax 2, so s_enc = 1344 and every q S = 1344 x (S = 448, q = 3x in blocks of amax 2;
+    S = 224, q = 6x in blocks of amax 1); the accumulator holds 1344^2 = 2^12 441 times an
+    integer sum, exact in FP32, and the epilogue's two FP32 products by tA and tB follow."""
+    g = inputs.rng(175, ["bf16", "mxfp8", "mxfp4", "nvfp4"].index(fmt))
+    M, N, K = 40, (48 if fmt == "nvfp4" else 36), 1 << 22
+    a, ab = _small_int_operand(g, (M, K))
+    b, bb = _small_int_operand(g, (N, K))
+    exact = a.astype(np.float64) @ b.astype(np.float64).T                # integers
+    if fmt == "nvfp4":
+        qa, sa, ta = mxq.quantize_nvfp4(dev_bf16(np.ascontiguousarray(ab.T)), scope="tensor", transpose=True)
+        qb, sb, tb = mxq.quantize_nvfp4(dev_bf16(np.ascontiguousarray(bb.T)), scope="tensor", transpose=True)
+        c = mxq.gemm_block_scaled(mxq.NVFP4, qa, sa, qb, sb, tA=ta, tB=tb, tA_scope="tensor", tB_scope="tensor")
+        ta, tb = host(ta), host(tb)
+        assert ta[0].view(np.uint32) == np.float32(1.0 / 1344.0).view(np.uint32) and tb[0] == ta[0]
+        acc = (exact * 1344.0 * 1344.0).astype(np.float32)                 # exact: 441 |sum| < 2^24
+        ref = (acc * ta[0]) * tb[0]
+        assert np.array_equal(host(c), ref), "nvfp4 at K = 2^22"
+        return
+    if fmt == "bf16":
+        c = mxq.gemm_block_scaled(mxq.BF16, dev_bf16(ab), None, dev_bf16(bb), None)
+    else:
+        quant, f = (mxq.quantize_mxfp8, mxq.MXFP8) if fmt == "mxfp8" else (mxq.quantize_mxfp4, mxq.MXFP4)
+        qa, sa, _, _ = quant(dev_bf16(ab), True, False)
+        qb, sb, _, _ = quant(dev_bf16(bb), True, False)
+        c = mxq.gemm_block_scaled(f, qa, sa, qb, sb)
+    assert np.array_equal(host(c), exact.astype(np.float32)), f"{fmt} at K = 2^22"
+
+
+def test_grouped_weight_gradient_at_the_k_limit_is_exact():
+    """The BF16 weight-gradient grouped GEMM with the reduction total at its limit, 2^22,
+    over three groups (one empty, boundaries multiples of 8): exact per group as above."""
+    g = inputs.rng(176, 0)
+    M, N, total = 48, 40, 1 << 22
+    offsets = np.array([0, 1_500_000, 1_500_000, total], dtype=np.int64)
+    a, ab = _small_int_operand(g, (M, total))
+    b, bb = _small_int_operand(g, (N, total))
+    c = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(offsets), dev_bf16(ab), dev_bf16(bb), N=N, K=0,
+                                           vary_k=True, M=M, total=total))
+    for e in range(3):
+        lo, hi = offsets[e], offsets[e + 1]
+        ref = (a[:, lo:hi].astype(np.float64) @ b[:, lo:hi].astype(np.float64).T).astype(np.float32)
+        assert np.array_equal(c[e], ref), f"group {e}"

@@ -781,3 +781,46 @@ def test_grouped_weight_gradient_at_the_k_limit_is_exact():
         lo, hi = offsets[e], offsets[e + 1]
         ref = (a[:, lo:hi].astype(np.float64) @ b[:, lo:hi].astype(np.float64).T).astype(np.float32)
         assert np.array_equal(c[e], ref), f"group {e}"
+
+
+# ------------- more groups than two rounds of the 64-ary group search reach -------------
+
+@pytest.mark.parametrize("G", [4097, 5000])
+def test_grouped_rows_with_more_than_4096_groups(G):
+    """Row-grouped BF16 GEMM over more groups than two rounds of the tile->group search
+    cover (64^2 = 4096): most groups empty or a few rows long, every group's rows within
+    2e-5 of the oracle, the padding rows of each group's last tile never written."""
+    g = inputs.rng(177, G)
+    N, K = 40, 64
+    sizes = g.geometric(0.25, G) - 1                          # many zeros, a few rows each
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    S = int(off[-1])
+    a = inputs.normal_bf16(g, (S, K))
+    w = inputs.normal_bf16(g, (G * N, K), 0.05)
+    out = torch.full((S, N), float("nan"), device="cuda")
+    mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a), dev_bf16(w), N=N, K=K, total=S, out=out)
+    got = host(out)
+    ref = omoe.grouped_gemm_ref(F.bf16_bits_to_f32(a).astype(np.float64), off,
+                                F.bf16_bits_to_f32(w).astype(np.float64).reshape(G, N, K))
+    assert_gemm_close(got, ref, f"{G} groups")
+
+
+def test_grouped_weight_gradient_with_more_than_4096_groups():
+    """Weight-gradient (vary-K) grouped BF16 GEMM over 5000 groups, group boundaries
+    multiples of 8 and many empty groups (their outputs are zero)."""
+    g = inputs.rng(178, 0)
+    G, M, N = 5000, 32, 40
+    sizes = 8 * (g.geometric(0.3, G) - 1)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    total = int(off[-1])
+    a = inputs.normal_bf16(g, (M, total))
+    b = inputs.normal_bf16(g, (N, total))
+    got = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a), dev_bf16(b), N=N, K=0, vary_k=True,
+                                             M=M, total=total))
+    af, bf = F.bf16_bits_to_f32(a).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64)
+    for e in range(G):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            assert np.all(got[e] == 0.0), f"empty group {e}"
+        else:
+            assert_gemm_close(got[e], af[:, lo:hi] @ bf[:, lo:hi].T, f"group {e}")

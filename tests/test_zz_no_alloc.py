@@ -110,3 +110,32 @@ def test_noalloc_grouped_gemm_in_a_captured_hip_graph():
         ref_ws = host(_call_workspace(c))                         # eager call between replays
         torch.cuda.synchronize()
         assert np.array_equal(got.view(np.uint32), ref_ws.view(np.uint32)), f"replay {trial}"
+
+
+def test_noalloc_at_its_group_limit():
+    """MXQ_NOALLOC_MAX_GROUPS groups (8191), the most the static scratch holds: mostly
+    empty experts, bit-identical to the workspace entry point and within 2e-5 per expert."""
+    g = inputs.rng(162, 0)
+    groups, N, K, tokens = 8191, 64, 256, 600
+    x = inputs.to_bf16_bits(g.standard_normal((tokens, K)))
+    w = inputs.normal_bf16(g, (groups * N, K), 0.02)
+    choice = g.integers(0, groups, (tokens, 2))
+    choice[:, 1] = (choice[:, 0] + 1 + g.integers(0, groups - 1, tokens)) % groups     # two distinct experts
+    order = np.argsort(choice.ravel(), kind="stable")
+    row_index = (order // 2).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(np.bincount(choice.ravel(), minlength=groups))]).astype(np.int64)
+    qx, sx, tx = mxq.quantize_nvfp4_per_token(dev_bf16(x))
+    qw, sw, tw = mxq.quantize_nvfp4(dev_bf16(w), scope="group", group_rows=N)
+    c = dict(qx=qx, sx=sx, tx=tx, qw=qw, sw=sw, tw=tw, off=dev(offsets), idx=dev(row_index), total=len(row_index),
+             groups=groups, N=N, K=K, tokens=tokens)
+    out = torch.full((c["total"], N), 9.0, device="cuda")
+    assert _call_noalloc(c, out) == 0
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.array_equal(got.view(np.uint32), host(_call_workspace(c)).view(np.uint32))
+    xh = onv.dequantize_exact(host(qx), host(sx), host(tx))[row_index]
+    qwh, swh, twh = host(qw), host(sw), host(tw)
+    for e in np.nonzero(np.diff(offsets))[0]:                    # the experts that got tokens
+        lo, hi = offsets[e], offsets[e + 1]
+        we = onv.dequantize_exact(qwh[e * N:(e + 1) * N], swh[e * N:(e + 1) * N], np.repeat(twh[e], N))
+        assert_gemm_close(got[lo:hi], xh[lo:hi] @ we.T, f"expert {e}")

@@ -445,6 +445,24 @@ def test_swiglu_extreme_gates():
     assert_bytes_equal(host(t)[finite].view(np.uint32), et.view(np.uint32), "h scales")
 
 
+@pytest.mark.parametrize("inter", [16, 528, 2064, 4112, 8208, 16384])
+def test_swiglu_requant_every_row_width(inter):
+    """SwiGLU + per-row NVFP4 for row widths that reach every register-blocked instance of
+    the kernel (1 to 32 chunks of 512), ragged last chunks and the 16384 maximum: h, the
+    packed codes, the block scales and t bit for bit against the oracle from the FP32
+    gate/up values."""
+    g = inputs.rng(89, inter)
+    rows = 24
+    gu = (g.standard_normal((rows, 2 * inter)) * 4 * np.exp2(g.integers(-8, 8, (rows, 1)))).astype(np.float32)
+    h, q, s, t = mxq.moe_swiglu_quantize_nvfp4(dev(gu))
+    hh = omoe.swiglu_bf16_ref(gu)
+    assert_bytes_equal(host(h), hh, f"h (inter {inter})")
+    eq, es, et = onv.quantize_per_token(hh)
+    assert_bytes_equal(host(q), eq, f"packed (inter {inter})")
+    assert_bytes_equal(host(s), es, f"block scales (inter {inter})")
+    assert np.array_equal(host(t).view(np.uint32), et.view(np.uint32))
+
+
 def test_swiglu_requant_and_combine():
     g = inputs.rng(87, 0)
     rows, inter = 300, 768

@@ -12,6 +12,7 @@ import microscaling_precision_quantization_amd as mxq
 from microscaling_precision_quantization_amd import inputs
 from oracle import formats as F
 from oracle import gemm as og
+from oracle import mxfp4 as om4
 from oracle import mxfp8 as omx
 from oracle import nvfp4 as onv
 from tests.gpu_util import assert_bytes_equal, assert_gemm_close, dev_bf16, host
@@ -89,3 +90,39 @@ def test_sweep_gemms_ragged(seed):
     c = mxq.gemm_block_scaled(mxq.BF16, dev_bf16(a), None, dev_bf16(b), None)
     ref = og.gemm_tn_fp64(F.bf16_bits_to_f32(a).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64))
     assert_gemm_close(host(c), ref, f"BF16 {M}x{N}x{K}")
+
+
+_KS = {("bf16", 0): 1000, ("bf16", 1): 1024, ("mxfp8", 0): 1056, ("mxfp8", 1): 1088, ("mxfp8", 2): 1024,
+       ("mxfp4", 0): 1056, ("mxfp4", 1): 1088, ("mxfp4", 2): 1024, ("nvfp4", 0): 1056, ("nvfp4", 1): 1088,
+       ("nvfp4", 2): 1024}
+
+
+@pytest.mark.parametrize("big", [False, True])
+@pytest.mark.parametrize("fmt,mode", sorted(_KS))
+def test_dense_gemm_every_tile_and_scale_mode(fmt, mode, big):
+    """Every dense launch configuration: 128- or 256-tiles (the latter once the output holds
+    192 256-tiles: M = N = 3584) times each K class the scale loader distinguishes (K not a
+    multiple of 64; a multiple of 64 but not of the 16-byte scale chunk; chunk-aligned),
+    within 2e-5 of the oracle on every row (small) or 192 sampled rows (large)."""
+    K = _KS[(fmt, mode)]
+    M, N = (3584, 3584) if big else (300, 200)
+    g = inputs.rng(173, 2 * sorted(_KS).index((fmt, mode)) + int(big))
+    a, b = _values(g, M, K), inputs.normal_bf16(g, (N, K), 0.05)
+    rows = np.sort(g.choice(M, 192, replace=False)) if big else np.arange(M)
+    if fmt == "bf16":
+        c = mxq.gemm_block_scaled(mxq.BF16, dev_bf16(a), None, dev_bf16(b), None)
+        ah, bh = F.bf16_bits_to_f32(a[rows]).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64)
+    elif fmt == "nvfp4":
+        qa, sa, ta = mxq.quantize_nvfp4_per_token(dev_bf16(a))
+        qb, sb, tb = mxq.quantize_nvfp4(dev_bf16(b), scope="tensor")
+        c = mxq.gemm_block_scaled(mxq.NVFP4, qa, sa, qb, sb, tA=ta, tB=tb, tA_scope="row", tB_scope="tensor")
+        ah = onv.dequantize_exact(host(qa)[rows], host(sa)[rows], host(ta)[rows])
+        bh = onv.dequantize_exact(host(qb), host(sb), np.repeat(host(tb), N))
+    else:
+        quant, f, deq = ((mxq.quantize_mxfp8, mxq.MXFP8, omx.dequantize_exact) if fmt == "mxfp8"
+                         else (mxq.quantize_mxfp4, mxq.MXFP4, om4.dequantize_exact))
+        qa, sa, _, _ = quant(dev_bf16(a), True, False)
+        qb, sb, _, _ = quant(dev_bf16(b), True, False)
+        c = mxq.gemm_block_scaled(f, qa, sa, qb, sb)
+        ah, bh = deq(host(qa)[rows], host(sa)[rows]), deq(host(qb), host(sb))
+    assert_gemm_close(host(c)[rows], og.gemm_tn_fp64(ah, bh), f"{fmt} K={K} {'256' if big else '128'}-tiles")

@@ -407,7 +407,7 @@ class MoeDeepseek:
               Stage("grouped_gemm_nvfp4_fwd", m.down, self.fl["down"], "mfma", "fp4", "fp16"),
               Stage("combine", m.combine, T * k * H * 4 + T * H * 4 + T * k * 12, "hbm"),
               Stage("dequantize_transposed", lambda: b.dequantize_activations(d["d_o"], d["d_gu"]),
-                    S * I * (0.5 + 1 / 16 + 2) + S * H * (0.5 + 1 / 16 + 2) + S * H * 4 + S * 2 * I * 4, "hbm"),
+                    S * I * (0.5 + 1 / 16 + 2) + S * H * (0.5 + 1 / 16 + 2), "hbm"),
               Stage("grouped_gemm_bf16_bwd", lambda: b.gemms(d["d_o"], d["d_gu"]),
                     sum(v for kk, v in self.fl.items() if kk.endswith("grad")), "mfma", "bf16"),
               Stage("shared_expert_bf16", lambda: sh.forward(self.x, d["w_sgu"], d["w_sd"]), self.sfl["fwd"], "mfma",

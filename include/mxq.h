@@ -512,6 +512,10 @@ mxq_status gemm_mxfp8_matrix_core(int64_t M, int64_t N, int64_t K,
  *     A : (M, total_k) K-contiguous; B : (N, total_k); C : (groups, M, N).
  *     Group boundaries must be multiples of 32 (MXFP8, MXFP4) or 8 (BF16); MXQ_NVFP4
  *     is not supported with vary_k = 1 in ABI version 1.
+ *   vary_k = 2 (wgrad, MXQ_BF16 only): as vary_k = 1, with A given K-major: A is the
+ *     (total_k, M) row-major tensor whose transpose vary_k = 1 takes -- the slot-major
+ *     output gradient of the expert layer itself, so no transposed copy is needed. M % 8
+ *     == 0. Same values bit for bit as vary_k = 1 on the transposed A.
  *   offsets  : DEVICE int64 (groups + 1), non-decreasing, offsets[0] = 0,
  *              offsets[groups] = total (total_slots or total_k, passed as `total`);
  *              with vary_k = 1 every offset is a multiple of 32 (MXFP8, MXFP4) or 8 (BF16).

@@ -569,7 +569,12 @@ def _grouped_args(fmt, offsets, A, B, N, K, sA, sB, tA, tB, tA_scope, tB_scope, 
     if vary_k:
         if a_row_index is not None:
             raise ValueError("a_row_index is not supported with vary_k")
-        c.operand(fmt, "A", A, M, total, sA)
+        if vary_k == 2:                                     # K-major A: (total, M), BF16 only
+            if fmt != BF16:
+                raise ValueError("vary_k=2 (K-major A) is BF16 only")
+            c.operand(fmt, "A", A, total, M, None)
+        else:
+            c.operand(fmt, "A", A, M, total, sA)
         c.operand(fmt, "B", B, N, total, sB)
         if out is not None:
             c.need(out, "out", torch.float32, (G, M, N))
@@ -604,7 +609,8 @@ def grouped_gemm_block_scaled(fmt: int, offsets, A, B, N: int, K: int, sA=None, 
                               total: int | None = None, a_rows: int | None = None, out=None, workspace=None):
     """One GEMM per group; see include/mxq.h for the two modes.
 
-    vary_k=False: out (total_slots, N); vary_k=True: out (groups, M, N).
+    vary_k=False: out (total_slots, N); vary_k=True: out (groups, M, N); vary_k=2: as True
+    with A given K-major, (total, M).
     """
     groups = offsets.numel() - 1
     dev = A.device

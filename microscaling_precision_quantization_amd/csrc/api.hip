@@ -470,7 +470,8 @@ mxq_status grouped_check(mxq_format fmt, int64_t groups, const int64_t* offsets,
   if (groups < 0 || total < 0 || M < 0 || N < 0 || K < 0 || a_rows < 0) return MXQ_ERR_SHAPE;
   if (fmt != MXQ_MXFP8 && fmt != MXQ_NVFP4 && fmt != MXQ_BF16 && fmt != MXQ_MXFP4 && fmt != MXQ_BF16_NVFP4T)
     return MXQ_ERR_FORMAT;
-  if (vary_k != 0 && vary_k != 1) return MXQ_ERR_FORMAT;
+  if (vary_k != 0 && vary_k != 1 && vary_k != 2) return MXQ_ERR_FORMAT;
+  if (vary_k == 2 && fmt != MXQ_BF16) return MXQ_ERR_FORMAT;   // K-major A: BF16 only
   if (fmt == MXQ_BF16_NVFP4T) {
     // BF16 A x the stacked NVFP4 weights (groups, K, N), read transposed, one scale per group
     if (vary_k || a_row_index) return MXQ_ERR_FORMAT;
@@ -506,6 +507,7 @@ mxq_status grouped_check(mxq_format fmt, int64_t groups, const int64_t* offsets,
   } else {
     if (total % ((fmt == MXQ_MXFP8 || fmt == MXQ_MXFP4) ? 32 : 8)) return MXQ_ERR_SHAPE;
     if (total > kMaxGemmK) return MXQ_ERR_SHAPE;
+    if (vary_k == 2 && M % 8) return MXQ_ERR_SHAPE;            // 16-byte rows of the K-major A
   }
   if (!al16(A) || !al16(B) || !al4(C)) return MXQ_ERR_ALIGN;
   *empty = groups == 0 || N == 0 || (vary_k ? M == 0 : total == 0);

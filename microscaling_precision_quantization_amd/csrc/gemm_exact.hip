@@ -349,7 +349,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the loads of the stage NS - 1 ahead are interleaved with the first sub-block's
 // MFMAs, and the barrier that publishes the next stage sits halfway through the
 // last sub-block.
-template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false>
+// AKM: A is given K-major -- (k, m) row-major, p.lda = m per row -- as the slot-major
+// gradients of a weight-gradient GEMM are; BF16 with per-chunk K tails (SM 0) only.
+template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false, bool AKM = false>
 __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0,
                                                 uint8_t* lds1, uint8_t* lds2, uint8_t* lds3, uint8_t* ldsc) {
   using C = gx::Cfg<LD, BM, BN, SM, OCC, WIDE>;
@@ -382,15 +384,27 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
                           : make_rsrc(p.A + (p.a_base + m0) * ldA, (uint32_t)(a_rows_tile * ldA));
   const v4i rsB = LD == 6 ? rsA : make_rsrc(p.B + n0 * ldB, (uint32_t)(b_rows_tile * ldB));
   uint32_t voA[IA], voB[IB > 0 ? IB : 1];
+  static_assert(!AKM || (LD == 0 && SM == 0 && C::BK == 64), "K-major A: BF16 weight gradients");
+  // K-major A: LDS row k of a stage holds the tile's BM values of operand row k0 + k (2 BM
+  // bytes), 16-byte chunk c at position c ^ 2 (k % 4) -- so that the transpose reads of one
+  // 16-lane group (4 rows x 32 bytes) hit 8 different bank groups.
+  constexpr int AROW = 2 * BM;
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int pos = (wave * IA + j) * 1024 + lane * 16;   // byte in the A tile
-    const int row = pos / RB;
-    const int lc = ((pos % RB) / 16) ^ swz<RB>(row);      // logical chunk stored at this position
-    uint32_t o = (uint32_t)(row * ldA + lc * 16);
-    if (p.a_idx) {
-      const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
-      o = src >= 0 ? (uint32_t)(src * ldA + lc * 16) : kOutOfRange;
+    uint32_t o;
+    if constexpr (AKM) {
+      const int row = pos / AROW;
+      const int lc = ((pos % AROW) / 16) ^ (2 * (row % 4));
+      o = (uint32_t)(row * ldA + lc * 16);
+    } else {
+      const int row = pos / RB;
+      const int lc = ((pos % RB) / 16) ^ swz<RB>(row);    // logical chunk stored at this position
+      o = (uint32_t)(row * ldA + lc * 16);
+      if (p.a_idx) {
+        const int64_t src = row < a_rows_tile ? exact_src_row(p, m0 + row) : -1;
+        o = src >= 0 ? (uint32_t)(src * ldA + lc * 16) : kOutOfRange;
+      }
     }
     voA[j] = o - 1024u * (uint32_t)(j % 4);                // see buf_dma16_group
   }
@@ -574,11 +588,18 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // Uniform load parameters of tile t. Tiles past the end read zeros (out-of-range
   // SGPR offset); in the last tile, chunks and scale units at or beyond k_end are
   // turned out of range per lane.
-  struct TileK { uint32_t sod, sos; int k0; bool tail; };
+  struct TileK { uint32_t sod, sos; int k0; bool tail; v4i rsa; };
   auto tile_k = [&](int t) {
     TileK r;
     r.k0 = kb + t * C::BK;
     const bool past = t >= nk;
+    if constexpr (AKM) {
+      // the stage's rows of the K-major A, clipped at k_end (rows past it read zeros; the
+      // columns past m_valid of the last row read bytes that only feed unstored outputs)
+      const int64_t rows = past ? 0 : min((int64_t)C::BK, (int64_t)(ke - r.k0));
+      const int64_t bytes = rows > 0 ? rows * ldA - m0 * 2 : 0;
+      r.rsa = make_rsrc(p.A + (int64_t)r.k0 * ldA + m0 * 2, (uint32_t)min(bytes, (int64_t)0x7FFFFFFF));
+    }
     r.sod = past ? kOutOfRange : (uint32_t)((LD == 0 || LD == 6) ? 2 * r.k0 : (LD == 1 || LD == 4 || LD == 5) ? r.k0 : r.k0 / 2);
     r.sos = past ? kOutOfRange : (uint32_t)(r.k0 / BS * SEB);
     r.tail = !AL && !past && r.k0 + C::BK > ke;
@@ -600,7 +621,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       for (int n = 0; n < N; ++n) {
         const int j = 4 * g + n;
         vo[n] = isA ? voA[j] : voB[j];
-        if constexpr (!AL) {
+        if constexpr (!AL && !(AKM && isA)) {
           if (tk.tail) {
             const int pos = (wave * NI + j) * 1024 + lane * 16;
             const int lc = ((pos % RB) / 16) ^ swz<RB>(pos / RB);
@@ -609,7 +630,8 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         }
       }
       const uint32_t m0v = lb + (isA ? 0 : C::A_BYTES) + (uint32_t)(wave * NI + 4 * g) * 1024u;
-      buf_dma16_group<N>(isA ? rsA : rsB, vo, tk.sod, m0v);
+      if constexpr (AKM && isA) buf_dma16_group<N>(tk.rsa, vo, 0u, m0v);
+      else buf_dma16_group<N>(isA ? rsA : rsB, vo, tk.sod, m0v);
     } else if constexpr (IS > 0) {
       constexpr int q = d - GA - GB;
       uint32_t vo = voS[q];
@@ -668,13 +690,43 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // 16-byte-strided rows would each take several conflicting passes.)
   const uint32_t wcA = (uint32_t)(wm * (BM / 2) * 16), wcB = (uint32_t)((BM + wn * (BN / 2)) * 16);
   u32x4 chr[CH ? NF : 1];
+  // K-major A fragments: two LDS transpose reads (ds_read_b64_tr_b16) per 32 x 16 fragment.
+  // In a 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed by
+  // lanes i / 4 + 4 j (measured); lane (gq, l16) therefore addresses row 4 q + l16 / 4 of
+  // the group's k block (q: first or second 4 k of the lane half) at the 4 m values
+  // 4 (l16 % 4) onward, and receives 4 consecutive k of its own m -- the 16-bit MFMA
+  // operand. akm_lane[e]: the lane's offset for fragments whose first chunk is 4 e mod 8.
+  uint32_t akm_lane[2] = {0u, 0u};
+  if constexpr (AKM) {
+    const int gq = lane >> 4, l16 = lane & 15;
+    const int xa = 2 * (gq & 1) + ((l16 & 3) >> 1), ya = 2 * (l16 >> 2);
+    const uint32_t rowoff = (uint32_t)((8 * (gq >> 1) + (l16 >> 2)) * AROW) + (uint32_t)((l16 & 1) * 8) +
+                            (uint32_t)(wm * (BM / 16) * 16);
+    akm_lane[0] = rowoff + (uint32_t)((xa ^ ya) * 16);
+    akm_lane[1] = rowoff + (uint32_t)(((4 | xa) ^ ya) * 16);
+  }
   // TP = t % SPC, known at compile time in the unrolled rounds (R is a multiple of SPC)
   auto read_sub = [&](int t, auto SLOT, auto SB, auto TP, Frag& fr) {
     constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value, tp = decltype(TP)::value;
     const lds_cptr pa = as_lds(lbase[S] + wA + xo[b]);
     const lds_cptr pb = as_lds(lbase[S] + wB + xo[b]);
+    if constexpr (AKM) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
+      for (int i = 0; i < TI; ++i) {
+        const uint32_t a = lbase[S] + akm_lane[i & 1] + (uint32_t)(8 * (i / 2) * 16 + 16 * b * AROW);
+        typedef short v4s16 __attribute__((ext_vector_type(4)));
+        const v4s16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16*)(uintptr_t)a);
+        const v4s16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s16*)(uintptr_t)(a + 4 * AROW));
+        uint32_t w[4];
+        __builtin_memcpy(&w[0], &r0, 8);
+        __builtin_memcpy(&w[2], &r1, 8);
+        fr.raw[i] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) fr.raw[TI + j] = lds_ld16(pb + j * 32 * RB);
     if constexpr (LD == 5) {
@@ -1252,7 +1304,7 @@ __device__ __forceinline__ int64_t find_group(const int64_t* __restrict__ prefix
 // faster). Weight gradients (vary_k = 1) keep the plain order: there the XCD runs made
 // the kernels 2-14% slower (their time goes to the FP32 output stores, not to reads).
 constexpr int kRowGroupBand = 4;
-template <int LD, int BM, int BN, int SM, int OCC, bool WIDE>
+template <int LD, int BM, int BN, int SM, int OCC, bool WIDE, bool AKM = false>
 __global__ void __launch_bounds__(256, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, const int64_t* __restrict__ tile_prefix,
                      int64_t groups, int vary_k, int64_t M, int64_t N, int64_t tiles_n) {
@@ -1304,7 +1356,7 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.k_end = offsets[g + 1];
     p.C = base.C + g * M * N;
   }
-  exact_gemm_tile<LD, BM, BN, SM, OCC, WIDE>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
+  exact_gemm_tile<LD, BM, BN, SM, OCC, WIDE, AKM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1524,15 +1576,15 @@ __global__ void __launch_bounds__(64) tile_prefix_kernel(const int64_t* __restri
 
 size_t grouped_gemm_ws_bytes(int64_t groups) { return (size_t)(((groups + 1) * 8 + 255) / 256 * 256); }
 
-template <int LD, int BT, int SM>
+template <int LD, int BT, int SM, bool AKM = false>
 static void launch_grouped_t(const ExactProblem& p, const int64_t* offsets, const int64_t* prefix, int64_t max_tiles,
                              int64_t groups, int vary_k, int64_t M, int64_t N, hipStream_t st) {
   const int64_t tn = (N + BT - 1) / BT;
   // expert tiles keep the narrow stages: wide NVFP4 stages leave two LDS stages at half LDS.
   // 128 x 128 tiles run two workgroups per CU, 256 x 256 tiles one.
   constexpr int OCC = BT == 256 ? 1 : 2;
-  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, OCC, false>), dim3((unsigned)max_tiles), dim3(256), 0, st, p,
-                     offsets, prefix, groups, vary_k, M, N, tn);
+  hipLaunchKernelGGL((exact_grouped_kernel<LD, BT, BT, SM, OCC, false, AKM>), dim3((unsigned)max_tiles), dim3(256), 0, st,
+                     p, offsets, prefix, groups, vary_k, M, N, tn);
 }
 
 // Row-grouped NVFP4 with chunked scales: 128-row tiles keep the expert padding small,
@@ -1583,7 +1635,13 @@ hipError_t launch_grouped_gemm(int fmt, int64_t groups, const int64_t* offsets, 
   if (!vary_k) {
     p.m_valid = 0; p.lda = K; p.n_valid = N; p.ldb = K; p.k_begin = 0; p.k_end = K;
   } else {
-    p.m_valid = M; p.lda = total; p.n_valid = N; p.ldb = total; p.k_begin = 0; p.k_end = 0;
+    // vary_k 2: A is given K-major, (total, M) row-major (the slot-major gradient itself)
+    p.m_valid = M; p.lda = vary_k == 2 ? M : total; p.n_valid = N; p.ldb = total; p.k_begin = 0; p.k_end = 0;
+  }
+  if (vary_k == 2) {
+    if (BT == 256) launch_grouped_t<0, 256, 0, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+    else launch_grouped_t<0, 128, 0, true>(p, offsets, prefix, max_tiles, groups, vary_k, M, N, st);
+    return hipGetLastError();
   }
   if (fmt == 7) {
     // BF16 A x the stacked NVFP4 weights (K, N) per group, read transposed: B_g[n][k] is the

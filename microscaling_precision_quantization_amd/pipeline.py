@@ -252,8 +252,9 @@ class MoeDequantBackward:
     dgrad GEMMs vary M per expert; wgrad GEMMs vary K (the slots). The dgrads read the
     forward's NVFP4 expert weights directly (fused_weights: the GEMM loader builds the
     transposed BF16 dequantization, the BF16_NVFP4T format); with fused_weights=False
-    they read BF16 transposes written by dequantize_transposed first. Activation operands
-    that a TN wgrad needs transposed come from dequantize_transposed."""
+    they read BF16 transposes written by dequantize_transposed first. The wgrads read dO and
+    dGU as they are (slot-major, K-major A, vary_k=2); their other operands, the NVFP4
+    activations, are dequantized into K-contiguous BF16 transposes by dequantize_transposed."""
 
     def __init__(self, fwd: MoeNvfp4, fused_weights: bool = True):
         f = fwd
@@ -265,8 +266,6 @@ class MoeDequantBackward:
             self.w_guT = _bf16((G, H, 2 * I), dev) # W_hat_gu,g^T
         self.hT = _bf16((1, I, S), dev)            # h_hat^T (slots along K)
         self.xT = _bf16((1, H, S), dev)            # X_hat gathered into slots, transposed
-        self.d_oT = _bf16((1, H, S), dev)
-        self.d_guT = _bf16((1, 2 * I, S), dev)
         self.dh = _f32((S, I), dev)
         self.dx = _f32((S, H), dev)
         self.dw_d = _f32((G, H, I), dev)
@@ -290,8 +289,6 @@ class MoeDequantBackward:
                                 out=self.hT)
         B.dequantize_transposed(B.NVFP4, f.qx, f.sx, f.tx, t_scope="row", groups=1, group_rows=f.T, cols=f.H,
                                 src_row=f.r.row_index, out_cols=f.S, out=self.xT)
-        B.dequantize_transposed(B.BF16, d_o, groups=1, group_rows=f.S, cols=f.H, out=self.d_oT)
-        B.dequantize_transposed(B.BF16, d_gu, groups=1, group_rows=f.S, cols=2 * f.I, out=self.d_guT)
 
     def gemms(self, d_o, d_gu):                                    # A13
         f = self.f
@@ -303,7 +300,7 @@ class MoeDequantBackward:
         else:
             B.grouped_gemm_block_scaled(B.BF16, off, d_o, self.w_dT, N=f.I, K=f.H, total=f.S, out=self.dh,
                                         workspace=f.ws)
-        B.grouped_gemm_block_scaled(B.BF16, off, self.d_oT[0], self.hT[0], N=f.I, K=0, vary_k=True, M=f.H,
+        B.grouped_gemm_block_scaled(B.BF16, off, d_o, self.hT[0], N=f.I, K=0, vary_k=2, M=f.H,
                                     total=f.S, out=self.dw_d, workspace=f.ws)
         if self.fused:
             qw, sw, tw = f.wq["gu"]
@@ -312,7 +309,7 @@ class MoeDequantBackward:
         else:
             B.grouped_gemm_block_scaled(B.BF16, off, d_gu, self.w_guT, N=f.H, K=2 * f.I, total=f.S, out=self.dx,
                                         workspace=f.ws)
-        B.grouped_gemm_block_scaled(B.BF16, off, self.d_guT[0], self.xT[0], N=f.H, K=0, vary_k=True, M=2 * f.I,
+        B.grouped_gemm_block_scaled(B.BF16, off, d_gu, self.xT[0], N=f.H, K=0, vary_k=2, M=2 * f.I,
                                     total=f.S, out=self.dw_gu, workspace=f.ws)
 
     def backward(self, d_o, d_gu):

@@ -170,6 +170,11 @@ def test_gemm_validation():
     assert gg(1, 4, None, 0, 64, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, P, 4096, None) == 1
     assert gg(1, 0, P, 0, 0, 0, 32, 64, None, 0, P, P, None, 0, P, P, None, 0, P, None, 0, None) == 0
     assert gg(4, 4, P, 1, 48, 32, 32, 0, None, 0, P, P, None, 0, P, P, None, 0, P, P, 4096, None) == 2   # MXFP4 total % 32
+    # vary_k = 2 (K-major A): BF16 only, M % 8 == 0; other mode values are unknown
+    assert gg(1, 4, P, 2, 64, 32, 32, 0, None, 0, P, P, None, 0, P, P, None, 0, P, P, 4096, None) == 4
+    assert gg(3, 4, P, 2, 64, 36, 32, 0, None, 0, P, None, None, 0, P, None, None, 0, P, P, 4096, None) == 2
+    assert gg(3, 4, P, 3, 64, 40, 32, 0, None, 0, P, None, None, 0, P, None, None, 0, P, P, 4096, None) == 4
+    assert gg(3, 0, P, 2, 0, 40, 32, 0, None, 0, P, None, None, 0, P, None, None, 0, P, P, 4096, None) == 0
 
 
 def test_dequant_and_moe_validation():

@@ -842,3 +842,33 @@ def test_grouped_weight_gradient_with_more_than_4096_groups():
             assert np.all(got[e] == 0.0), f"empty group {e}"
         else:
             assert_gemm_close(got[e], af[:, lo:hi] @ bf[:, lo:hi].T, f"group {e}")
+
+
+# ------------- weight gradients from the K-major (slot-major) gradient -------------
+
+@pytest.mark.parametrize("M,N,sizes", [
+    (296, 260, [96, 0, 40, 416, 8]),                    # 128x128 tiles, ragged M and N, K tails of 8
+    (2048, 2048, [520, 0, 64, 1000]),                   # 256x256 tiles (64 per group)
+    (776, 1032, [0, 0, 136]),                           # empty leading groups, one group
+])
+def test_weight_gradient_from_k_major_a(M, N, sizes):
+    """vary_k = 2 reads A as the (total, M) slot-major tensor through LDS transpose reads:
+    bit-identical to vary_k = 1 on the transposed copy (same operand values, same K order)
+    and within 2e-5 of the oracle per group; empty groups give zeros."""
+    g = inputs.rng(181, M)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    total = int(off[-1])
+    a_km = inputs.normal_bf16(g, (total, M))                 # slot-major: row k holds the M values
+    b = inputs.normal_bf16(g, (N, total), 0.05)
+    got2 = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a_km), dev_bf16(b), N=N, K=0, vary_k=2,
+                                              M=M, total=total))
+    got1 = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(np.ascontiguousarray(a_km.T)), dev_bf16(b),
+                                              N=N, K=0, vary_k=True, M=M, total=total))
+    assert np.array_equal(got2.view(np.uint32), got1.view(np.uint32)), "vary_k 2 differs from vary_k 1"
+    af, bf = F.bf16_bits_to_f32(a_km).astype(np.float64), F.bf16_bits_to_f32(b).astype(np.float64)
+    for e in range(len(sizes)):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            assert np.all(got2[e] == 0.0)
+        else:
+            assert_gemm_close(got2[e], af[lo:hi].T @ bf[:, lo:hi].T, f"group {e}")

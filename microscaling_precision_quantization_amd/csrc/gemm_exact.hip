@@ -386,16 +386,17 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   uint32_t voA[IA], voB[IB > 0 ? IB : 1];
   static_assert(!AKM || (LD == 0 && SM == 0 && C::BK == 64), "K-major A: BF16 weight gradients");
   // K-major A: LDS row k of a stage holds the tile's BM values of operand row k0 + k (2 BM
-  // bytes), 16-byte chunk c at position c ^ 2 (k % 4) -- so that the transpose reads of one
-  // 16-lane group (4 rows x 32 bytes) hit 8 different bank groups.
+  // bytes), 16-byte chunk c at position c ^ 4 (k % 4) -- so that the transpose reads of one
+  // 32-lane half (4 rows x 64 bytes) cover all 64 banks once.
   constexpr int AROW = 2 * BM;
+  static_assert(!AKM || AROW >= 256, "K-major A swizzle spans 16 chunks of a row");
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int pos = (wave * IA + j) * 1024 + lane * 16;   // byte in the A tile
     uint32_t o;
     if constexpr (AKM) {
       const int row = pos / AROW;
-      const int lc = ((pos % AROW) / 16) ^ (2 * (row % 4));
+      const int lc = ((pos % AROW) / 16) ^ (4 * (row % 4));
       o = (uint32_t)(row * ldA + lc * 16);
     } else {
       const int row = pos / RB;
@@ -695,15 +696,15 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // lanes i / 4 + 4 j (measured); lane (gq, l16) therefore addresses row 4 q + l16 / 4 of
   // the group's k block (q: first or second 4 k of the lane half) at the 4 m values
   // 4 (l16 % 4) onward, and receives 4 consecutive k of its own m -- the 16-bit MFMA
-  // operand. akm_lane[e]: the lane's offset for fragments whose first chunk is 4 e mod 8.
-  uint32_t akm_lane[2] = {0u, 0u};
+  // operand. akm_lane[i]: the lane's offset for fragment i, whose 4 chunks are the row's
+  // chunk group q = wm TI + i, stored at group q ^ (k % 4).
+  uint32_t akm_lane[AKM ? TI : 1] = {};
   if constexpr (AKM) {
-    const int gq = lane >> 4, l16 = lane & 15;
-    const int xa = 2 * (gq & 1) + ((l16 & 3) >> 1), ya = 2 * (l16 >> 2);
-    const uint32_t rowoff = (uint32_t)((8 * (gq >> 1) + (l16 >> 2)) * AROW) + (uint32_t)((l16 & 1) * 8) +
-                            (uint32_t)(wm * (BM / 16) * 16);
-    akm_lane[0] = rowoff + (uint32_t)((xa ^ ya) * 16);
-    akm_lane[1] = rowoff + (uint32_t)(((4 | xa) ^ ya) * 16);
+    const int gq = lane >> 4, l16 = lane & 15, r = l16 >> 2;
+    const int xa = 2 * (gq & 1) + ((l16 & 3) >> 1);
+    const uint32_t rowoff = (uint32_t)((8 * (gq >> 1) + r) * AROW) + (uint32_t)((l16 & 1) * 8);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) akm_lane[i] = rowoff + (uint32_t)((4 * ((wm * TI + i) ^ r) + xa) * 16);
   }
   // TP = t % SPC, known at compile time in the unrolled rounds (R is a multiple of SPC)
   auto read_sub = [&](int t, auto SLOT, auto SB, auto TP, Frag& fr) {
@@ -713,7 +714,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     if constexpr (AKM) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const uint32_t a = lbase[S] + akm_lane[i & 1] + (uint32_t)(8 * (i / 2) * 16 + 16 * b * AROW);
+        const uint32_t a = lbase[S] + akm_lane[i] + (uint32_t)(16 * b * AROW);
         typedef short v4s16 __attribute__((ext_vector_type(4)));
         const v4s16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16*)(uintptr_t)a);
         const v4s16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

@@ -481,106 +481,106 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 
   // LD 6: the B tile is made from NVFP4 weight rows W[k][n] (E2M1 pairs along n, one E4M3
   // scale per 16 n, one FP32 decode scale t for the whole group): B[n][k] =
-  // RNE_bf16(fl32(fl32(q S) t)), the dequantized weight transposed. Lane (kg, ng) of the
-  // 256 threads loads an 8 (k) x 8 (n) block per stage -- 8 rows of 4 bytes and their 8
-  // scale bytes -- into registers, and at the end of the stage writes its 8 n-rows of 8 k
-  // (one 16-byte chunk each, at the swizzled position the BF16 fragment reads expect) into
-  // the B area of the slot being filled. A quarter-wave covers 8 k groups x 2 n groups, so
-  // each 16-byte LDS write meets at most one other lane on its banks.
+  // RNE_bf16(fl32(fl32(q S) t)), the dequantized weight transposed. It is kept K-major in
+  // LDS -- row k of a stage holds the tile's 256 BF16 values of W row k0 + k, 16-byte chunk
+  // c at position c ^ 5 (k % 4) -- and the MFMA fragments come out through transpose reads,
+  // like a K-major A. Lane (w, l) of the 256 threads owns stage row kr = 16 w + 4 (l / 16) +
+  // (l / 2) % 4 and, with q = 2 ((l / 8) % 2) + l % 2, the 32-n pieces q and q + 4 of it: two
+  // 16-byte loads of packed E2M1 and four scale bytes per stage (six loads; narrow 8 x 8
+  // blocks took sixteen and ran the DeepSeek-shaped dgrads 5-6% slower). Sub-block b
+  // converts 16 values (two chunks); the last one writes the block's eight chunks (1% faster
+  // than writing each sub-block's pair as it is made). The LDS takes 16-byte writes 8 lanes
+  // (128 bytes) at a time: each such group holds 4 rows x 2 adjacent pieces, which the
+  // rotation puts on 32 different banks (4 pieces of 2 rows per group, the first lane order,
+  // cost 25% of the LDS cycles in bank conflicts); each 32-lane pass of the transpose reads
+  // covers all 64 banks.
   const int kb_ = (int)p.k_begin;
   const int nk_ = ((int)p.k_end - kb_ + C::BK - 1) / C::BK;
   constexpr bool NVT = LD == 6;
-  static_assert(!NVT || (BN == 256 && C::BK == 64 && C::SBS == 4 && TJ / 2 - 1 == 1),
+  static_assert(!NVT || (BN == 256 && C::BK == 64 && C::SBS == 4 && TJ / 2 - 1 == 1 && C::IA == 8),
                 "the NVFP4-transposed B path is laid out for 256 x 64 stages of four sub-blocks");
+  constexpr int BROW6 = 2 * BN;                           // bytes of one K-major B row in LDS
+  constexpr int NB6 = 6;                                  // B loads per lane and stage
   __amdgpu_buffer_rsrc_t rsB6, rsS6;
-  uint32_t voB6[NVT ? 8 : 1], voS6[NVT ? 8 : 1];
+  uint32_t voB6 = 0, voS6 = 0;
+  uint32_t wo6[NVT ? 4 : 1] = {};                         // LDS offset of the lane's chunk c of piece q
   float t6 = 0.0f;
   int64_t rowB6 = 0, rowS6 = 0;
-  const int kg6 = lane & 7, ng6 = wave * 8 + (lane >> 3);
   if constexpr (NVT) {
+    const int kr6 = 16 * wave + 4 * (lane >> 4) + ((lane >> 1) & 3), q6 = 2 * ((lane >> 3) & 1) + (lane & 1);
+    const int a6 = kr6 & 3;
     rowB6 = p.ldb / 2;                                    // bytes per W row (p.ldb = N elements)
     rowS6 = p.ldb / 16;
     rsB6 = __builtin_amdgcn_make_buffer_rsrc((void*)p.B, (short)0, (int)min(p.k_end * rowB6, (int64_t)0x7FFFFFFF),
                                              0x00020000);
     rsS6 = __builtin_amdgcn_make_buffer_rsrc((void*)p.sB, (short)0, (int)min(p.k_end * rowS6, (int64_t)0x7FFFFFFF),
                                              0x00020000);
-    // Columns at or past n_valid (N % 16 == 0: a lane's 8 columns all exist or none) read
-    // whatever in-range bytes follow, or zeros past the buffer; they only feed accumulator
-    // columns the epilogue never stores.
-    const int64_t n = n0 + 8 * ng6;
+    // Columns at or past n_valid read whatever in-range bytes follow, or zeros past the
+    // buffer; they only feed accumulator columns the epilogue never stores.
+    const int64_t n = n0 + 32 * q6;
+    voB6 = (uint32_t)(kr6 * rowB6 + n / 2);               // piece q; piece q + 4 is 64 bytes on
+    voS6 = (uint32_t)(kr6 * rowS6 + n / 16);              // its two scale bytes; piece q + 4's at + 8
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      voB6[j] = (uint32_t)((8 * kg6 + j) * rowB6 + n / 2);
-      voS6[j] = (uint32_t)((8 * kg6 + j) * rowS6 + n / 16);
-    }
+    for (int c = 0; c < 4; ++c) wo6[c] = (uint32_t)(kr6 * BROW6 + 16 * (4 * (q6 ^ a6) + (c ^ a6)));
     t6 = p.tB[0];
   }
   // Two register buffers: the loads of tile t + 2 are in flight while tile t + 1's block is
-  // converted (row pair b in sub-block b of stage t) and written to its slot.
-  uint32_t bq6[2][NVT ? 8 : 1], bs6[2][NVT ? 8 : 1];
-  uint32_t out6[8][NVT ? 4 : 1];                          // converted block: [n][k pair]
-  // register loads of B tile t into buffer BUF (rows at or past k_end, and tiles past the
-  // end, read zeros)
+  // converted (16 values in sub-block b of stage t) and written to its slot.
+  uint32_t bq6[2][NVT ? 8 : 1], bs6[2][NVT ? 4 : 1];
+  uint32_t out6[NVT ? 32 : 1];                            // the converted block: chunk pairs of sub-blocks 0..3
+  // loads of B tile t into buffer BUF, in the order the sub-blocks use them (rows at or past
+  // k_end, and tiles past the end, read zeros)
   auto nvt_issue = [&](int t, auto BUF) {
     if constexpr (NVT) {
       constexpr int bf = decltype(BUF)::value;
+      typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
       const int k0 = kb_ + t * C::BK;
       const bool past = t >= nk_;
       const int so = (int)(past ? kOutOfRange : (uint32_t)(k0 * rowB6));
       const int ss = (int)(past ? kOutOfRange : (uint32_t)(k0 * rowS6));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bq6[bf][j] = __builtin_amdgcn_raw_buffer_load_b32(rsB6, (int)voB6[j], so, 0);
-        bs6[bf][j] = __builtin_amdgcn_raw_buffer_load_b8(rsS6, (int)voS6[j], ss, 0);
-      }
+      const v4u_t d0 = __builtin_amdgcn_raw_buffer_load_b128(rsB6, (int)voB6, so, 0);
+      bs6[bf][0] = __builtin_amdgcn_raw_buffer_load_b8(rsS6, (int)voS6, ss, 0);
+      bs6[bf][1] = __builtin_amdgcn_raw_buffer_load_b8(rsS6, (int)(voS6 + 1), ss, 0);
+      const v4u_t d1 = __builtin_amdgcn_raw_buffer_load_b128(rsB6, (int)(voB6 + 64), so, 0);
+      bs6[bf][2] = __builtin_amdgcn_raw_buffer_load_b8(rsS6, (int)(voS6 + 8), ss, 0);
+      bs6[bf][3] = __builtin_amdgcn_raw_buffer_load_b8(rsS6, (int)(voS6 + 9), ss, 0);
+      bq6[bf][0] = d0.x; bq6[bf][1] = d0.y; bq6[bf][2] = d0.z; bq6[bf][3] = d0.w;
+      bq6[bf][4] = d1.x; bq6[bf][5] = d1.y; bq6[bf][6] = d1.z; bq6[bf][7] = d1.w;
     }
   };
-  // row J of the block in buffer BUF -> v6[J % 2][n], the FP32 dequantized values
-  float v6[2][NVT ? 8 : 1];
-  auto nvt_row = [&](auto BUF, auto J) {
+  // half H (8 values) of sub-block b's 16 values of the block in buffer BUF -> out6[8 b + 4 H ..],
+  // BF16 pairs of adjacent n
+  auto nvt_conv = [&](auto BUF, auto SB, auto H) {
     if constexpr (NVT) {
-      constexpr int bf = decltype(BUF)::value, j = decltype(J)::value, r = j % 2;
-      const uint32_t w = bq6[bf][j];
-      const float Sb = __builtin_amdgcn_cvt_f32_fp8((int)bs6[bf][j], 0);   // exact E4M3 decode, no branch
+      constexpr int bf = decltype(BUF)::value, b = decltype(SB)::value, hh = decltype(H)::value;
+      const uint32_t w = bq6[bf][4 * (b / 2) + 2 * (b % 2) + hh];
+      const float Sb = __builtin_amdgcn_cvt_f32_fp8((int)bs6[bf][b], 0);   // exact E4M3 decode, no branch
       const v2f_t e0 = e2m1x2_to_f32<0>(w), e1 = e2m1x2_to_f32<1>(w);
       const v2f_t e2 = e2m1x2_to_f32<2>(w), e3 = e2m1x2_to_f32<3>(w);
-      v6[r][0] = (e0.x * Sb) * t6; v6[r][1] = (e0.y * Sb) * t6;        // q S exact, then * t
-      v6[r][2] = (e1.x * Sb) * t6; v6[r][3] = (e1.y * Sb) * t6;
-      v6[r][4] = (e2.x * Sb) * t6; v6[r][5] = (e2.y * Sb) * t6;
-      v6[r][6] = (e3.x * Sb) * t6; v6[r][7] = (e3.y * Sb) * t6;
+      out6[8 * b + 4 * hh + 0] = bf16x2_rne((e0.x * Sb) * t6, (e0.y * Sb) * t6);   // q S exact, then * t
+      out6[8 * b + 4 * hh + 1] = bf16x2_rne((e1.x * Sb) * t6, (e1.y * Sb) * t6);
+      out6[8 * b + 4 * hh + 2] = bf16x2_rne((e2.x * Sb) * t6, (e2.y * Sb) * t6);
+      out6[8 * b + 4 * hh + 3] = bf16x2_rne((e3.x * Sb) * t6, (e3.y * Sb) * t6);
     }
   };
-  // rows 2 jp, 2 jp + 1 (in v6) -> BF16 pairs out6[n][jp]
-  auto nvt_pack = [&](auto JP) {
+  // sub-block b's two chunks (piece q + 4 (b / 2), chunks 2 (b % 2) and 2 (b % 2) + 1) into
+  // the B area of slot S
+  auto nvt_write = [&](auto SLOT, auto SB) {
     if constexpr (NVT) {
-      constexpr int jp = decltype(JP)::value;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) out6[n][jp] = bf16x2_rne(v6[0][n], v6[1][n]);
-    }
-  };
-  auto nvt_convert = [&](auto BUF, auto JP) {
-    constexpr int jp = decltype(JP)::value;
-    nvt_row(BUF, ic<2 * jp>{});
-    nvt_row(BUF, ic<2 * jp + 1>{});
-    nvt_pack(JP);
-  };
-  // write the converted block into the B area of slot S
-  auto nvt_write = [&](auto SLOT) {
-    if constexpr (NVT) {
-      constexpr int S = decltype(SLOT)::value;
-      const uint32_t base = lbase[S] + C::A_BYTES;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int nl = 8 * ng6 + n;                       // B tile row
-        const uint32_t a = base + (uint32_t)(nl * RB + ((kg6 ^ swz<RB>(nl)) << 4));
-        const u32x4 v4 = {out6[n][0], out6[n][1], out6[n][2], out6[n][3]};
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)a = v4;
-      }
+      constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value;
+      const uint32_t base = lbase[S] + C::A_BYTES + (uint32_t)(256 * (b / 2));
+      const u32x4 v0 = {out6[8 * b + 0], out6[8 * b + 1], out6[8 * b + 2], out6[8 * b + 3]};
+      const u32x4 v1 = {out6[8 * b + 4], out6[8 * b + 5], out6[8 * b + 6], out6[8 * b + 7]};
+      *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + wo6[2 * (b % 2)]) = v0;
+      *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + wo6[2 * (b % 2) + 1]) = v1;
     }
   };
   auto nvt_store = [&](auto BUF, auto SLOT) {
-    static_for<0, 4>([&](auto JP) { nvt_convert(BUF, JP); });
-    nvt_write(SLOT);
+    static_for<0, 4>([&](auto SB) {
+      nvt_conv(BUF, SB, ic<0>{});
+      nvt_conv(BUF, SB, ic<1>{});
+      nvt_write(SLOT, SB);
+    });
   };
 
   const int kb = (int)p.k_begin, ke = (int)p.k_end;       // K <= 2^22
@@ -706,6 +706,27 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
 #pragma unroll
     for (int i = 0; i < TI; ++i) akm_lane[i] = rowoff + (uint32_t)((4 * ((wm * TI + i) ^ r) + xa) * 16);
   }
+  // LD 6 B fragments, read the same way from the K-major B rows (chunk group q = wn TJ + j
+  // of row k at group q ^ (k % 4), its chunk x at x ^ (k % 4)).
+  uint32_t bkm_lane[NVT ? TJ : 1] = {};
+  if constexpr (NVT) {
+    const int gq = lane >> 4, l16 = lane & 15, r = l16 >> 2;
+    const int xa = 2 * (gq & 1) + ((l16 & 3) >> 1);
+    const uint32_t rowoff = (uint32_t)(C::A_BYTES + (8 * (gq >> 1) + r) * BROW6 + (l16 & 1) * 8);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bkm_lane[j] = rowoff + (uint32_t)(16 * (4 * ((wn * TJ + j) ^ r) + (xa ^ r)));
+  }
+  // two transpose reads: rows k .. k + 3 of the lane's group at a, k + 4 .. k + 7 at a + 4 rows
+  auto tr_frag = [&](uint32_t a, uint32_t row_bytes) {
+    typedef short v4s16 __attribute__((ext_vector_type(4)));
+    const v4s16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16*)(uintptr_t)a);
+    const v4s16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s16*)(uintptr_t)(a + 4 * row_bytes));
+    uint32_t w[4];
+    __builtin_memcpy(&w[0], &r0, 8);
+    __builtin_memcpy(&w[2], &r1, 8);
+    return u32x4{w[0], w[1], w[2], w[3]};
+  };
   // TP = t % SPC, known at compile time in the unrolled rounds (R is a multiple of SPC)
   auto read_sub = [&](int t, auto SLOT, auto SB, auto TP, Frag& fr) {
     constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value, tp = decltype(TP)::value;
@@ -713,23 +734,19 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     const lds_cptr pb = as_lds(lbase[S] + wB + xo[b]);
     if constexpr (AKM) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const uint32_t a = lbase[S] + akm_lane[i] + (uint32_t)(16 * b * AROW);
-        typedef short v4s16 __attribute__((ext_vector_type(4)));
-        const v4s16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16*)(uintptr_t)a);
-        const v4s16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s16*)(uintptr_t)(a + 4 * AROW));
-        uint32_t w[4];
-        __builtin_memcpy(&w[0], &r0, 8);
-        __builtin_memcpy(&w[2], &r1, 8);
-        fr.raw[i] = u32x4{w[0], w[1], w[2], w[3]};
-      }
+      for (int i = 0; i < TI; ++i) fr.raw[i] = tr_frag(lbase[S] + akm_lane[i] + (uint32_t)(16 * b * AROW), AROW);
     } else {
 #pragma unroll
       for (int i = 0; i < TI; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
     }
+    if constexpr (NVT) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) fr.raw[TI + j] = lds_ld16(pb + j * 32 * RB);
+      for (int j = 0; j < TJ; ++j)
+        fr.raw[TI + j] = tr_frag(lbase[S] + bkm_lane[j] + (uint32_t)(16 * b * BROW6), BROW6);
+    } else {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) fr.raw[TI + j] = lds_ld16(pb + j * 32 * RB);
+    }
     if constexpr (LD == 5) {
       const lds_cptr pa2 = as_lds(lbase[S] + wA + xo2[b]);
       const lds_cptr pb2 = as_lds(lbase[S] + wB + xo2[b]);
@@ -940,7 +957,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // stages (issued ahead of their stage's data).
   auto allowed = [](auto RI) constexpr {
     constexpr int ri = decltype(RI)::value;
-    int n = (NS - 2) * OPS + (NVT ? 16 : 0);
+    int n = (NS - 2) * OPS + (NVT ? NB6 : 0);
     if constexpr (CH)
       for (int d = 0; d <= NS - 3; ++d)
         if (((ri - d) % R + R) % R % SPC == 0) n += XS;
@@ -971,31 +988,35 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           issue_chunk(kt / SPC + 1);                    // the next chunk, ahead of this stage's data loads
           __builtin_amdgcn_sched_barrier(0);
         }
-        // LD 6: the B block of tile kt + 1 was loaded during the previous stage (8 rows, two
-        // loads each; nothing older is in flight when the stage starts). Sub-block b converts
-        // row pair b, interleaved with the matrix work, after waiting for just those rows:
-        // loads return in order, so they have landed once no more than the later rows' loads
-        // (and, from sub-block 1 on, the 8 A loads and 16 B loads issued in sub-block 0) are
-        // outstanding; the compiler sees the waits and adds none at the uses. The last
+        // LD 6: the B block of tile kt + 1 was loaded during the previous stage (its six loads
+        // in use order; nothing older is in flight when the stage starts). Sub-block b converts
+        // its 16 values, interleaved with the matrix work, after waiting for just the loads it
+        // needs: loads return in order, so they have landed once no more than the later ones
+        // (and, from sub-block 1 on, the 8 A loads and 6 B loads issued in sub-block 0) are
+        // outstanding. (The compiler may still wait longer where the loads are carried over
+        // the loop's back edge.) A scheduling barrier keeps each sub-block's conversion below
+        // its wait (1% faster than letting it rise into the previous sub-block). The last
         // sub-block writes the block to tile kt + 1's slot before the barrier. Tile kt + 1's
         // A loads and the B register loads of tile kt + 2 go out during sub-block 0.
-        static_assert(!NVT || (C::IA == 8 && SBS == 4), "the wait counts assume 8 A loads per stage");
-        if constexpr (NVT && jj == 0) wait_vmcnt<b == 0 ? 12 : 8 + 16 + 4 * (3 - b)>();
+        if constexpr (NVT && jj == 0) {
+          constexpr int used = b == 0 ? 2 : b == 1 ? 3 : b == 2 ? 5 : 6;   // loads sub-blocks 0..b read
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<NB6 - used + (b > 0 ? C::IA + NB6 : 0)>();
+        }
         if constexpr (b == 0 && jj < PJ) {
           __builtin_amdgcn_sched_barrier(0);
           issue_range(tk, ic<SL>{}, ic<(UNITS * jj) / PJ>{}, ic<(UNITS * (jj + 1)) / PJ>{});
           if constexpr (NVT && jj == PJ - 1) nvt_issue(kt + 2, ic<ri & 1>{});
           __builtin_amdgcn_sched_barrier(0);
         }
-        // row 2b after fragment 0, row 2b + 1 and the packing after fragment 1 (no scheduling
-        // barrier: the scheduler interleaves them with the neighbouring MFMAs)
-        if constexpr (NVT && jj == 0) nvt_row(ic<(ri + 1) & 1>{}, ic<2 * b>{});
+        // the first 8 values after fragment 0, the other 8 after fragment 1 (no scheduling
+        // barrier: the scheduler interleaves them with the MFMAs)
+        if constexpr (NVT && jj == 0) nvt_conv(ic<(ri + 1) & 1>{}, ic<b>{}, ic<0>{});
         if constexpr (NVT && jj == 1) {
-          nvt_row(ic<(ri + 1) & 1>{}, ic<2 * b + 1>{});
-          nvt_pack(ic<b>{});
+          nvt_conv(ic<(ri + 1) & 1>{}, ic<b>{}, ic<1>{});
           if constexpr (b + 1 == SBS) {
             __builtin_amdgcn_sched_barrier(0);
-            nvt_write(ic<SL>{});
+            static_for<0, 4>([&](auto BB) { nvt_write(ic<SL>{}, BB); });
           }
         }
         if constexpr (b + 1 == SBS && jj == BJ) {
@@ -1022,7 +1043,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     nvt_issue(1, ic<1>{});                              // in flight into the first stage
     __builtin_amdgcn_s_waitcnt(0xC07F);
   }
-  wait_vmcnt<(NS - 2) * OPS + (NVT ? 16 : 0)>();
+  wait_vmcnt<(NS - 2) * OPS + (NVT ? NB6 : 0)>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_sub(0, ic<0>{}, ic<0>{}, ic<0>{}, F[0]);

@@ -688,6 +688,7 @@ def _nvfp4t_case(seed, G, K, N, rows, zero_group=None):
     (6, 512, 768, [0, 400, 513, 256, 390, 1000], None),     # 256-row tiles on both paths: bit-identical
     (4, 200, 400, [37, 0, 300, 129], 1),                     # K tail (200 % 64), N tail (400 % 256), zero expert
     (3, 1024, 2048, [700, 64, 900], 2),
+    (3, 328, 528, [700, 512, 400], None),                    # K tail 8, last column tile 16 wide (N % 32 = 16)
 ])
 def test_bf16_nvfp4t_dgrad_from_quantized_weights(G, K, N, rows, zg):
     """The BF16 x NVFP4-weights-transposed grouped GEMM (the weight dequantization done in

@@ -689,6 +689,7 @@ def _nvfp4t_case(seed, G, K, N, rows, zero_group=None):
     (4, 200, 400, [37, 0, 300, 129], 1),                     # K tail (200 % 64), N tail (400 % 256), zero expert
     (3, 1024, 2048, [700, 64, 900], 2),
     (3, 328, 528, [700, 512, 400], None),                    # K tail 8, last column tile 16 wide (N % 32 = 16)
+    (3, 24, 272, [1, 300, 0], None),                         # K below one stage, a one-row expert
 ])
 def test_bf16_nvfp4t_dgrad_from_quantized_weights(G, K, N, rows, zg):
     """The BF16 x NVFP4-weights-transposed grouped GEMM (the weight dequantization done in
@@ -851,6 +852,7 @@ def test_grouped_weight_gradient_with_more_than_4096_groups():
     (296, 260, [96, 0, 40, 416, 8]),                    # 128x128 tiles, ragged M and N, K tails of 8
     (2048, 2048, [520, 0, 64, 1000]),                   # 256x256 tiles (64 per group)
     (776, 1032, [0, 0, 136]),                           # empty leading groups, one group
+    (8, 136, [8, 24, 0]),                               # the narrowest A (one 16-byte chunk per row)
 ])
 def test_weight_gradient_from_k_major_a(M, N, sizes):
     """vary_k = 2 reads A as the (total, M) slot-major tensor through LDS transpose reads:

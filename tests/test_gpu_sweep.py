@@ -204,3 +204,64 @@ def test_grouped_weight_gradient_narrow_and_wide(fmt, wide):
             assert np.all(got[e] == 0.0), f"empty group {e}"
         else:
             assert_gemm_close(got[e][rows], og.gemm_tn_fp64(ah[rows, lo:hi], bh[:, lo:hi]), f"{fmt} group {e}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_k_major_weight_gradient(seed):
+    """BF16 weight gradients from the slot-major gradient (vary_k = 2) on random M
+    (multiples of 8), N and group sizes (multiples of 8, some empty): bit-identical to
+    vary_k = 1 on the transposed copy and within 2e-5 of the oracle per group."""
+    g = inputs.rng(181, seed)
+    M = 8 * int(g.integers(1, 140))
+    N = int(g.integers(1, 1100))
+    G = int(g.integers(1, 7))
+    sizes = 8 * g.integers(0, 40, G) * (g.random(G) > 0.25)
+    if sizes.sum() == 0:
+        sizes[-1] = 8 * int(g.integers(1, 40))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    total = int(off[-1])
+    a_km = _values(g, total, M)                                 # (slots, M): as the layer holds dY
+    b = inputs.normal_bf16(g, (N, total), 0.05)
+    got = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(a_km), dev_bf16(b), N=N, K=0, vary_k=2,
+                                             M=M, total=total))
+    two = host(mxq.grouped_gemm_block_scaled(mxq.BF16, dev(off), dev_bf16(np.ascontiguousarray(a_km.T)), dev_bf16(b),
+                                             N=N, K=0, vary_k=True, M=M, total=total))
+    assert np.array_equal(got.view(np.uint32), two.view(np.uint32)), f"M={M} N={N} sizes={list(sizes)}"
+    ah = F.bf16_bits_to_f32(a_km).astype(np.float64).T
+    bh = F.bf16_bits_to_f32(b).astype(np.float64)
+    rows = np.sort(g.choice(M, min(M, 96), replace=False))
+    for e in range(G):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            assert np.all(got[e] == 0.0), f"empty group {e}"
+        else:
+            assert_gemm_close(got[e][rows], og.gemm_tn_fp64(ah[rows, lo:hi], bh[:, lo:hi]), f"group {e}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_dgrad_from_nvfp4_weights(seed):
+    """The dequantized-backward dgrad straight from NVFP4 expert weights on random K
+    (multiples of 8), N (multiples of 16) and expert row counts (some empty, some one row):
+    within 2e-5 of the oracle's product with the BF16 dequantized weights, per expert."""
+    g = inputs.rng(182, seed)
+    G = int(g.integers(1, 6))
+    K = 8 * int(g.integers(1, 90))
+    N = 16 * int(g.integers(1, 70))
+    rows = g.integers(0, 700, G) * (g.random(G) > 0.2)
+    rows[g.random(G) < 0.15] = 1
+    if rows.sum() == 0:
+        rows[0] = int(g.integers(1, 700))
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    S = int(off[-1])
+    w = inputs.to_bf16_bits(g.standard_normal((G * K, N)) * 0.02 * np.exp2(g.integers(-3, 3, (G * K, 1))))
+    a = _values(g, S, K)
+    qw, sw, tw = mxq.quantize_nvfp4(dev_bf16(w), scope="group", group_rows=K)
+    wb = onv.dequantize_bf16_bits(host(qw), host(sw), np.repeat(host(tw), K))
+    b_hat = F.bf16_bits_to_f32(wb).astype(np.float64).reshape(G, K, N).transpose(0, 2, 1)
+    ref = omoe.grouped_gemm_ref(F.bf16_bits_to_f32(a).astype(np.float64), off, b_hat)
+    got = host(mxq.grouped_gemm_block_scaled(mxq.BF16_NVFP4T, dev(off), dev_bf16(a), qw, N=N, K=K, sB=sw, tB=tw,
+                                             tB_scope="group", total=S))
+    for e in range(G):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            assert_gemm_close(got[lo:hi], ref[lo:hi], f"K={K} N={N} expert {e}")

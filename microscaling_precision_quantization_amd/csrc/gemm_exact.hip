@@ -351,7 +351,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // last sub-block.
 // AKM: A is given K-major -- (k, m) row-major, p.lda = m per row -- as the slot-major
 // gradients of a weight-gradient GEMM are; BF16 with per-chunk K tails (SM 0) only.
-template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false, bool AKM = false>
+template <int LD, int BM, int BN, int SM, int OCC = 1, bool WIDE = false, bool AKM = false, bool PART = false>
 __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m0, int64_t n0, uint8_t* lds0,
                                                 uint8_t* lds1, uint8_t* lds2, uint8_t* lds3, uint8_t* ldsc) {
   using C = gx::Cfg<LD, BM, BN, SM, OCC, WIDE>;
@@ -728,16 +728,17 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     return u32x4{w[0], w[1], w[2], w[3]};
   };
   // TP = t % SPC, known at compile time in the unrolled rounds (R is a multiple of SPC)
-  auto read_sub = [&](int t, auto SLOT, auto SB, auto TP, Frag& fr) {
+  auto read_sub = [&](int t, auto SLOT, auto SB, auto TP, Frag& fr, auto TIAC) {
     constexpr int S = decltype(SLOT)::value, b = decltype(SB)::value, tp = decltype(TP)::value;
+    constexpr int TIA = decltype(TIAC)::value;           // A fragments this wave needs
     const lds_cptr pa = as_lds(lbase[S] + wA + xo[b]);
     const lds_cptr pb = as_lds(lbase[S] + wB + xo[b]);
     if constexpr (AKM) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i) fr.raw[i] = tr_frag(lbase[S] + akm_lane[i] + (uint32_t)(16 * b * AROW), AROW);
+      for (int i = 0; i < TIA; ++i) fr.raw[i] = tr_frag(lbase[S] + akm_lane[i] + (uint32_t)(16 * b * AROW), AROW);
     } else {
 #pragma unroll
-      for (int i = 0; i < TI; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
+      for (int i = 0; i < TIA; ++i) fr.raw[i] = lds_ld16(pa + i * 32 * RB);
     }
     if constexpr (NVT) {
 #pragma unroll
@@ -751,7 +752,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       const lds_cptr pa2 = as_lds(lbase[S] + wA + xo2[b]);
       const lds_cptr pb2 = as_lds(lbase[S] + wB + xo2[b]);
 #pragma unroll
-      for (int i = 0; i < TI; ++i) fr.raw2[i] = lds_ld16(pa2 + i * 32 * RB);
+      for (int i = 0; i < TIA; ++i) fr.raw2[i] = lds_ld16(pa2 + i * 32 * RB);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) fr.raw2[TI + j] = lds_ld16(pb2 + j * 32 * RB);
     }
@@ -850,24 +851,25 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   };
 
   // Convert + MFMA one sub-block; hook(jj) runs after the MFMAs of B fragment jj.
-  auto mma_sub = [&](const Frag& fr, auto&& hook) {
+  auto mma_sub = [&](const Frag& fr, auto TIAC, auto&& hook) {
+    constexpr int TIA = decltype(TIAC)::value;
     if constexpr (LD == 0 || LD == 6) {
       v8bf fa[TI];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) __builtin_memcpy(&fa[i], &fr.raw[i], 16);
+      for (int i = 0; i < TIA; ++i) __builtin_memcpy(&fa[i], &fr.raw[i], 16);
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
         v8bf fb;
         __builtin_memcpy(&fb, &fr.raw[TI + j], 16);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TIA; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb, acc[i][j], 0, 0, 0);
         hook(JJ);
       });
     } else if constexpr (LD == 1 || LD == 4) {
       // MXFP8: E4M3 * 2^(s-127); blockwise FP8: the E4M3 values themselves (scale 2^0)
       v8bf fa0[TI], fa1[TI];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
+      for (int i = 0; i < TIA; ++i) {
         const float s = LD == 4 ? 1.0f : mx_cvt_scale(fr.sc[i]);
         fa0[i] = mx_to_bf16(fr.raw[i].x, fr.raw[i].y, s);
         fa1[i] = mx_to_bf16(fr.raw[i].z, fr.raw[i].w, s);
@@ -878,9 +880,9 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
         const v8bf fb0 = mx_to_bf16(fr.raw[TI + j].x, fr.raw[TI + j].y, s);
         const v8bf fb1 = mx_to_bf16(fr.raw[TI + j].z, fr.raw[TI + j].w, s);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) dst(i, j) = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, dst(i, j), 0, 0, 0);
+        for (int i = 0; i < TIA; ++i) dst(i, j) = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0, dst(i, j), 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) dst(i, j) = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, dst(i, j), 0, 0, 0);
+        for (int i = 0; i < TIA; ++i) dst(i, j) = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1, dst(i, j), 0, 0, 0);
         hook(JJ);
       });
     } else if constexpr (LD == 5) {
@@ -888,12 +890,12 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       // [16h, 16h+16) of both 32-K blocks of the sub-block and the E8M0 byte of block h.
       v8i fa[TI];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) fa[i] = fp8_operand(fr.raw[i], fr.raw2[i]);
+      for (int i = 0; i < TIA; ++i) fa[i] = fp8_operand(fr.raw[i], fr.raw2[i]);
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
         const v8i fb = fp8_operand(fr.raw[TI + j], fr.raw2[TI + j]);
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TIA; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb, acc[i][j], 0, 0, 0, (int)fr.sc[i], 0,
                                                                      (int)fr.sc[TI + j]);
         hook(JJ);
@@ -904,12 +906,12 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       // sub-block reads already have).
       v8i fa[TI];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) fa[i] = fp4_operand(fr.raw[i]);
+      for (int i = 0; i < TIA; ++i) fa[i] = fp4_operand(fr.raw[i]);
       static_for<0, TJ>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
         const v8i fb = fp4_operand(fr.raw[TI + j]);
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TIA; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb, acc[i][j], 4, 4, 0, (int)fr.sc[i], 0,
                                                                      (int)fr.sc[TI + j]);
         hook(JJ);
@@ -917,7 +919,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     } else {
       v8h fa[2][2][TI];        // [half][dword pair][i]
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TIA; ++i)
       {
         float p0, p1;
         v2h mm;
@@ -938,9 +940,9 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           const v8h fb0 = nv_to_f16_h<hf>(hf ? fr.raw[TI + j].z : fr.raw[TI + j].x, p2, mb);
           const v8h fb1 = nv_to_f16_h<hf>(hf ? fr.raw[TI + j].w : fr.raw[TI + j].y, p2, mb);
 #pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][0][i], fb0, acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TIA; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][0][i], fb0, acc[i][j], 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][1][i], fb1, acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TIA; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[hf][1][i], fb1, acc[i][j], 0, 0, 0);
         });
         hook(JJ);
       });
@@ -965,7 +967,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   };
 
   // One stage: tile kt (round position RI) in slot RI % NS.
-  auto stage = [&](int kt, auto RI) {
+  auto stage = [&](int kt, auto RI, auto TIAC) {
     constexpr int ri = decltype(RI)::value;
     constexpr int S = ri % NS;
     constexpr int SN = (ri + 1) % NS;                    // slot of the next tile
@@ -978,10 +980,10 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
       constexpr int b = decltype(SB)::value;
       constexpr int cur = (ri * SBS + b) & 1;
       if constexpr (b + 1 < SBS) {
-        read_sub(kt, ic<S>{}, ic<b + 1>{}, ic<ri % SPC>{}, F[cur ^ 1]);
+        read_sub(kt, ic<S>{}, ic<b + 1>{}, ic<ri % SPC>{}, F[cur ^ 1], TIAC);
         __builtin_amdgcn_sched_barrier(0);              // keep the prefetch ahead of this sub-block's MFMAs
       }
-      mma_sub(F[cur], [&](auto JJ) {
+      mma_sub(F[cur], TIAC, [&](auto JJ) {
         constexpr int jj = decltype(JJ)::value;
         if constexpr (b == 0 && jj == 0 && CH && ri % SPC == 0) {
           __builtin_amdgcn_sched_barrier(0);
@@ -1025,7 +1027,7 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           wait_vmcnt<WAIT>();                           // tile kt + 1 has landed (this wave's loads)
           __builtin_amdgcn_s_barrier();                 // ... and every wave's; slot S fully read
           __builtin_amdgcn_sched_barrier(0);
-          read_sub(kt + 1, ic<SN>{}, ic<0>{}, ic<(ri + 1) % SPC>{}, F[cur ^ 1]);
+          read_sub(kt + 1, ic<SN>{}, ic<0>{}, ic<(ri + 1) % SPC>{}, F[cur ^ 1], TIAC);
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -1046,8 +1048,6 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   wait_vmcnt<(NS - 2) * OPS + (NVT ? NB6 : 0)>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_sub(0, ic<0>{}, ic<0>{}, ic<0>{}, F[0]);
-  __builtin_amdgcn_sched_barrier(0);
 
   // Whole rounds of R stages: stages past the end multiply zeros (their loads are
   // out of range), which adds nothing to the accumulators.
@@ -1056,12 +1056,32 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   // prologue or FP32 epilogue (DeepSeek expert wgrads 5% faster; no gain measured for the
   // NVFP4 and MXFP8 kernels, which keep equal priorities)
   constexpr bool PRIO = OCC > 1 && LD == 0;
-  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
-  for (int r = 0; r < rounds; ++r) {
-    const int kt = r * R;
-    static_for<0, R>([&](auto RI) { stage(kt + RI.value, RI); });
+  // main loop for a wave that needs its first TIA 32-row A fragments (the others cover
+  // only rows past m_valid: their MFMAs would multiply zeros into rows never stored)
+  auto main_loop = [&](auto TIAC) {
+    read_sub(0, ic<0>{}, ic<0>{}, ic<0>{}, F[0], TIAC);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+    for (int r = 0; r < rounds; ++r) {
+      const int kt = r * R;
+      static_for<0, R>([&](auto RI) { stage(kt + RI.value, RI, TIAC); });
+    }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  if constexpr (PART) {
+    // Row-grouped tiles end where their expert does: in an expert's last row tile a wave
+    // whose rows are all or mostly padding runs the loop with fewer A fragments (every
+    // wave still does its share of the loads, conversions and barriers).
+    const int64_t rows_left = p.m_valid - (m0 + wm * (BM / 2));
+    const int vg = rows_left <= 0 ? 0 : (int)min((rows_left + 31) / 32, (int64_t)TI);
+    if (vg >= TI) main_loop(ic<TI>{});
+    else if (vg == 0) main_loop(ic<0>{});
+    else if (vg == 1) main_loop(ic<1>{});
+    else if (vg == 2) main_loop(ic<(TI > 2 ? 2 : TI)>{});
+    else main_loop(ic<TI>{});
+  } else {
+    main_loop(ic<TI>{});
   }
-  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   wait_vmcnt<0>();                    // no direct load may still target this workgroup's LDS
   exact_drain();
 
@@ -1378,7 +1398,10 @@ exact_grouped_kernel(ExactProblem base, const int64_t* __restrict__ offsets, con
     p.k_end = offsets[g + 1];
     p.C = base.C + g * M * N;
   }
-  exact_gemm_tile<LD, BM, BN, SM, OCC, WIDE, AKM>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
+  // the expert-tail specialization pays on the converting forward formats (NVFP4 gate_up /
+  // down 3-6% faster); the BF16 kernels at one workgroup per CU measured no gain from it
+  constexpr bool PART = LD != 0 && LD != 6;
+  exact_gemm_tile<LD, BM, BN, SM, OCC, WIDE, AKM, PART>(p, tm * BM, tn * BN, lds0, lds1, lds2, lds3, ldsc);
 }
 
 // ---------------------------------------------------------------------------

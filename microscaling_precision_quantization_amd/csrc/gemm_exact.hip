@@ -365,7 +365,8 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   constexpr int SEB = LD == 4 ? 4 : 1;                    // bytes per scale entry
   constexpr int EPC = (LD == 0 || LD == 6) ? 8 : (LD == 1 || LD == 4 || LD == 5) ? 16 : 32;   // elements per 16-byte chunk
   constexpr int OPS = IA + IB + IS;                       // direct loads per stage and wave (chunks aside)
-  constexpr int R = CH ? lcm_int(SPC, NS) : NS;           // stages per unrolled round
+  // stages per unrolled round (LD 6: four, one per B register buffer)
+  constexpr int R = CH ? lcm_int(SPC, NS) : (LD == 6 ? 4 : NS);
   static_assert(R % NS == 0 && (!CH || R % SPC == 0), "round must cover whole slot and chunk cycles");
   static_assert((R * SBS) % 2 == 0, "fragment double buffer needs an even sub-block count per round");
   const int lane = threadIdx.x & 63;
@@ -524,9 +525,11 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
     for (int c = 0; c < 4; ++c) wo6[c] = (uint32_t)(kr6 * BROW6 + 16 * (4 * (q6 ^ a6) + (c ^ a6)));
     t6 = p.tB[0];
   }
-  // Two register buffers: the loads of tile t + 2 are in flight while tile t + 1's block is
-  // converted (16 values in sub-block b of stage t) and written to its slot.
-  uint32_t bq6[2][NVT ? 8 : 1], bs6[2][NVT ? 4 : 1];
+  // Four register buffers: the B loads of tile t + 4 go out during stage t, so each block has
+  // three stages to arrive before stage t + 3 converts it (16 values in each sub-block) and
+  // writes it to its slot (2-4% faster dgrads than two buffers, one stage ahead; rounds of
+  // four stages keep the buffer indices static).
+  uint32_t bq6[4][NVT ? 8 : 1], bs6[4][NVT ? 4 : 1];
   uint32_t out6[NVT ? 32 : 1];                            // the converted block: chunk pairs of sub-blocks 0..3
   // loads of B tile t into buffer BUF, in the order the sub-blocks use them (rows at or past
   // k_end, and tiles past the end, read zeros)
@@ -990,32 +993,25 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
           issue_chunk(kt / SPC + 1);                    // the next chunk, ahead of this stage's data loads
           __builtin_amdgcn_sched_barrier(0);
         }
-        // LD 6: the B block of tile kt + 1 was loaded during the previous stage (its six loads
-        // in use order; nothing older is in flight when the stage starts). Sub-block b converts
-        // its 16 values, interleaved with the matrix work, after waiting for just the loads it
-        // needs: loads return in order, so they have landed once no more than the later ones
-        // (and, from sub-block 1 on, the 8 A loads and 6 B loads issued in sub-block 0) are
-        // outstanding. (The compiler may still wait longer where the loads are carried over
-        // the loop's back edge.) A scheduling barrier keeps each sub-block's conversion below
-        // its wait (1% faster than letting it rise into the previous sub-block). The last
-        // sub-block writes the block to tile kt + 1's slot before the barrier. Tile kt + 1's
-        // A loads and the B register loads of tile kt + 2 go out during sub-block 0.
-        if constexpr (NVT && jj == 0) {
-          constexpr int used = b == 0 ? 2 : b == 1 ? 3 : b == 2 ? 5 : 6;   // loads sub-blocks 0..b read
-          __builtin_amdgcn_sched_barrier(0);
-          wait_vmcnt<NB6 - used + (b > 0 ? C::IA + NB6 : 0)>();
-        }
+        // LD 6: the B block of tile kt + 1 was loaded three stages ago, before the A loads that
+        // the last barrier waited for, so it has landed (loads return in order). Sub-block b
+        // converts its 16 values, interleaved with the matrix work (a scheduling barrier keeps
+        // each sub-block's conversion in its sub-block: 1% faster than letting it rise into
+        // the previous one). The last sub-block writes the block to tile kt + 1's slot before
+        // the barrier. Tile kt + 1's A loads and the B register loads of tile kt + 4 go out
+        // during sub-block 0.
+        if constexpr (NVT && jj == 0) __builtin_amdgcn_sched_barrier(0);
         if constexpr (b == 0 && jj < PJ) {
           __builtin_amdgcn_sched_barrier(0);
           issue_range(tk, ic<SL>{}, ic<(UNITS * jj) / PJ>{}, ic<(UNITS * (jj + 1)) / PJ>{});
-          if constexpr (NVT && jj == PJ - 1) nvt_issue(kt + 2, ic<ri & 1>{});
+          if constexpr (NVT && jj == PJ - 1) nvt_issue(kt + 4, ic<ri % 4>{});
           __builtin_amdgcn_sched_barrier(0);
         }
         // the first 8 values after fragment 0, the other 8 after fragment 1 (no scheduling
         // barrier: the scheduler interleaves them with the MFMAs)
-        if constexpr (NVT && jj == 0) nvt_conv(ic<(ri + 1) & 1>{}, ic<b>{}, ic<0>{});
+        if constexpr (NVT && jj == 0) nvt_conv(ic<(ri + 1) % 4>{}, ic<b>{}, ic<0>{});
         if constexpr (NVT && jj == 1) {
-          nvt_conv(ic<(ri + 1) & 1>{}, ic<b>{}, ic<1>{});
+          nvt_conv(ic<(ri + 1) % 4>{}, ic<b>{}, ic<1>{});
           if constexpr (b + 1 == SBS) {
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, 4>([&](auto BB) { nvt_write(ic<SL>{}, BB); });
@@ -1039,10 +1035,12 @@ __device__ __forceinline__ void exact_gemm_tile(const ExactProblem& p, int64_t m
   issue_chunk(0);
   static_for<0, NS - 1>([&](auto T) { issue_range(tile_k(T.value), T, ic<0>{}, ic<UNITS>{}); });
   if constexpr (NVT) {
-    static_assert(NS == 2, "the B register pipeline runs one stage ahead of two LDS slots");
+    static_assert(NS == 2 && R == 4, "the B register buffers rotate with rounds of four stages over two slots");
     nvt_issue(0, ic<0>{});
     nvt_store(ic<0>{}, ic<0>{});                        // tile 0 into slot 0 (waits for everything)
-    nvt_issue(1, ic<1>{});                              // in flight into the first stage
+    nvt_issue(1, ic<1>{});                              // in flight into the first stages
+    nvt_issue(2, ic<2>{});
+    nvt_issue(3, ic<3>{});
     __builtin_amdgcn_s_waitcnt(0xC07F);
   }
   wait_vmcnt<(NS - 2) * OPS + (NVT ? NB6 : 0)>();
